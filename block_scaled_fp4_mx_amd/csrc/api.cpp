@@ -1,0 +1,251 @@
+// C ABI of libfp4: argument validation and dispatch to the gfx950 kernels.
+// Every check runs before the first HIP call, so a rejected call enqueues
+// nothing; the library holds no state besides the per-thread error message.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "fp4_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int ok() {
+    g_last_error[0] = '\0';
+    return FP4_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int hip_status(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(FP4_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+#define FP4_REQUIRE(cond, status, ...) \
+    do {                               \
+        if (!(cond)) return fail(status, __VA_ARGS__); \
+    } while (0)
+
+#define FP4_PTR(p) FP4_REQUIRE((p) != nullptr, FP4_ERR_INVALID, "%s is NULL", #p); \
+    FP4_REQUIRE(aligned16(p), FP4_ERR_ALIGN, "%s is not 16-byte aligned", #p)
+
+// Scalars the kernels read (tensor scales, counters) need only natural alignment.
+#define FP4_SCALAR_PTR(p) FP4_REQUIRE((p) != nullptr, FP4_ERR_INVALID, "%s is NULL", #p); \
+    FP4_REQUIRE((reinterpret_cast<uintptr_t>(p) & 3u) == 0, FP4_ERR_ALIGN, "%s is not 4-byte aligned", #p)
+
+int check_ld(int64_t ld, int64_t width, const char* name) {
+    FP4_REQUIRE(ld >= width, FP4_ERR_INVALID, "%s (%lld) is smaller than the row width (%lld)", name,
+                (long long)ld, (long long)width);
+    FP4_REQUIRE(ld % 8 == 0, FP4_ERR_ALIGN, "%s (%lld) is not a multiple of 8", name, (long long)ld);
+    return FP4_OK;
+}
+
+size_t nv_ws_bytes() { return 256; }
+
+}  // namespace
+
+extern "C" {
+
+int fp4_abi_version(void) { return 1; }
+
+const char* fp4_status_string(int status) {
+    switch (status) {
+        case FP4_OK: return "ok";
+        case FP4_ERR_INVALID: return "invalid argument";
+        case FP4_ERR_SHAPE: return "unsupported shape";
+        case FP4_ERR_ALIGN: return "misaligned pointer or leading dimension";
+        case FP4_ERR_UNSUPPORTED: return "unsupported combination";
+        case FP4_ERR_WORKSPACE: return "workspace missing or too small";
+        case FP4_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char* fp4_last_error(void) { return g_last_error; }
+
+int fp4_quantize_mx(const void* x_bf16, int64_t rows, int64_t k, int64_t ld_x,
+                    uint8_t* codes, uint8_t* scales, void* stream) {
+    FP4_REQUIRE(rows >= 0 && k >= 0, FP4_ERR_INVALID, "negative size rows=%lld k=%lld", (long long)rows, (long long)k);
+    FP4_REQUIRE(k % 32 == 0, FP4_ERR_SHAPE, "k=%lld is not a multiple of 32", (long long)k);
+    if (rows == 0 || k == 0) return ok();
+    FP4_PTR(x_bf16);
+    FP4_PTR(codes);
+    FP4_PTR(scales);
+    if (int e = check_ld(ld_x, k, "ld_x")) return e;
+    return hip_status(fp4::launch_quantize_mx(static_cast<const uint16_t*>(x_bf16), rows, k, ld_x, codes,
+                                              scales, static_cast<hipStream_t>(stream)),
+                      "fp4_quantize_mx launch");
+}
+
+size_t fp4_quantize_nv_workspace_bytes(int64_t rows, int64_t k) {
+    (void)rows;
+    (void)k;
+    return nv_ws_bytes();
+}
+
+int fp4_quantize_nv(const void* x_bf16, int64_t rows, int64_t k, int64_t ld_x, uint8_t* codes,
+                    uint8_t* scales, float* tensor_scale, int tensor_scale_is_input, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+    FP4_REQUIRE(rows >= 0 && k >= 0, FP4_ERR_INVALID, "negative size rows=%lld k=%lld", (long long)rows, (long long)k);
+    FP4_REQUIRE(k % 16 == 0, FP4_ERR_SHAPE, "k=%lld is not a multiple of 16", (long long)k);
+    if (rows == 0 || k == 0) return ok();
+    FP4_PTR(x_bf16);
+    FP4_PTR(codes);
+    FP4_PTR(scales);
+    FP4_SCALAR_PTR(tensor_scale);
+    if (int e = check_ld(ld_x, k, "ld_x")) return e;
+    if (!tensor_scale_is_input) {
+        FP4_REQUIRE(workspace != nullptr && workspace_bytes >= nv_ws_bytes(), FP4_ERR_WORKSPACE,
+                    "workspace needs %zu bytes, got %zu", nv_ws_bytes(), workspace ? workspace_bytes : (size_t)0);
+        FP4_REQUIRE(aligned16(workspace), FP4_ERR_ALIGN, "workspace is not 16-byte aligned");
+    }
+    return hip_status(fp4::launch_quantize_nv(static_cast<const uint16_t*>(x_bf16), rows, k, ld_x, codes, scales,
+                                              tensor_scale, tensor_scale_is_input != 0,
+                                              static_cast<uint32_t*>(workspace), static_cast<hipStream_t>(stream)),
+                      "fp4_quantize_nv launch");
+}
+
+int fp4_remap_mx_to_nv(const uint8_t* codes, const uint8_t* scales_e8m0, int64_t rows, int64_t k,
+                       uint8_t* scales_e4m3, float* tensor_scale, int32_t* n_inexact_blocks, void* stream) {
+    FP4_REQUIRE(rows >= 0 && k >= 0, FP4_ERR_INVALID, "negative size rows=%lld k=%lld", (long long)rows, (long long)k);
+    FP4_REQUIRE(k % 32 == 0, FP4_ERR_SHAPE, "k=%lld is not a multiple of 32", (long long)k);
+    if (rows == 0 || k == 0) return ok();
+    FP4_PTR(codes);
+    FP4_PTR(scales_e8m0);
+    FP4_PTR(scales_e4m3);
+    FP4_SCALAR_PTR(tensor_scale);
+    FP4_SCALAR_PTR(n_inexact_blocks);
+    return hip_status(fp4::launch_remap(codes, scales_e8m0, rows, k, scales_e4m3, tensor_scale, n_inexact_blocks,
+                                        static_cast<hipStream_t>(stream)),
+                      "fp4_remap_mx_to_nv launch");
+}
+
+int fp4_dequant(fp4_format fmt, const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
+                int64_t rows, int64_t k, void* out, fp4_dtype out_dtype, int64_t ld_out, void* stream) {
+    FP4_REQUIRE(fmt == FP4_FMT_MX || fmt == FP4_FMT_NV, FP4_ERR_INVALID, "bad format %d", (int)fmt);
+    FP4_REQUIRE(out_dtype == FP4_DT_BF16 || out_dtype == FP4_DT_F32, FP4_ERR_INVALID, "bad dtype %d", (int)out_dtype);
+    FP4_REQUIRE(rows >= 0 && k >= 0, FP4_ERR_INVALID, "negative size rows=%lld k=%lld", (long long)rows, (long long)k);
+    const int blk = fmt == FP4_FMT_MX ? 32 : 16;
+    FP4_REQUIRE(k % blk == 0, FP4_ERR_SHAPE, "k=%lld is not a multiple of %d", (long long)k, blk);
+    if (rows == 0 || k == 0) return ok();
+    FP4_PTR(codes);
+    FP4_PTR(scales);
+    FP4_PTR(out);
+    if (fmt == FP4_FMT_NV) { FP4_SCALAR_PTR(tensor_scale); }
+    if (int e = check_ld(ld_out, k, "ld_out")) return e;
+    return hip_status(fp4::launch_dequant(fmt, codes, scales, tensor_scale, rows, k, out, out_dtype == FP4_DT_F32,
+                                          ld_out, static_cast<hipStream_t>(stream)),
+                      "fp4_dequant launch");
+}
+
+int fp4_gemm(fp4_format fmt, const uint8_t* a_codes, const uint8_t* a_scales, const float* a_tensor_scale,
+             const uint8_t* b_codes, const uint8_t* b_scales, const float* b_tensor_scale, int64_t m, int64_t n,
+             int64_t k, void* c, fp4_dtype c_dtype, int64_t ldc, void* stream) {
+    FP4_REQUIRE(fmt == FP4_FMT_MX || fmt == FP4_FMT_NV, FP4_ERR_INVALID, "bad format %d", (int)fmt);
+    FP4_REQUIRE(c_dtype == FP4_DT_BF16 || c_dtype == FP4_DT_F32, FP4_ERR_INVALID, "bad dtype %d", (int)c_dtype);
+    FP4_REQUIRE(m >= 0 && n >= 0 && k >= 0, FP4_ERR_INVALID, "negative size m=%lld n=%lld k=%lld", (long long)m,
+                (long long)n, (long long)k);
+    const int blk = fmt == FP4_FMT_MX ? 32 : 16;
+    FP4_REQUIRE(k % blk == 0, FP4_ERR_SHAPE, "k=%lld is not a multiple of %d", (long long)k, blk);
+    FP4_REQUIRE(m < (int64_t)65535 * 128, FP4_ERR_SHAPE, "m=%lld too large", (long long)m);
+    if (m == 0 || n == 0) return ok();
+    FP4_PTR(c);
+    FP4_REQUIRE(ldc >= n, FP4_ERR_INVALID, "ldc (%lld) < n (%lld)", (long long)ldc, (long long)n);
+    if (k > 0) {
+        FP4_PTR(a_codes);
+        FP4_PTR(a_scales);
+        FP4_PTR(b_codes);
+        FP4_PTR(b_scales);
+    }
+    if (fmt == FP4_FMT_NV) {
+        FP4_SCALAR_PTR(a_tensor_scale);
+        FP4_SCALAR_PTR(b_tensor_scale);
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = fmt == FP4_FMT_MX
+                       ? fp4::launch_gemm_mx(a_codes, a_scales, b_codes, b_scales, m, n, k, c, c_dtype == FP4_DT_F32, ldc, s)
+                       : fp4::launch_gemm_nv(a_codes, a_scales, a_tensor_scale, b_codes, b_scales, b_tensor_scale, m, n,
+                                             k, c, c_dtype == FP4_DT_F32, ldc, s);
+    return hip_status(e, "fp4_gemm launch");
+}
+
+size_t fp4_moe_workspace_bytes(fp4_format fmt, int64_t tokens, int64_t hidden, int topk, int num_experts,
+                               int64_t inter) {
+    if (tokens < 0 || hidden <= 0 || topk < 1 || num_experts < 1 || inter <= 0) return 0;
+    return fp4::moe_workspace_bytes(fmt, tokens, hidden, topk, num_experts, inter);
+}
+
+int fp4_moe_grouped_gemm(fp4_format fmt, const void* x_bf16, int64_t tokens, int64_t hidden,
+                         const int32_t* topk_ids, const float* topk_weights, int topk, int num_experts,
+                         int64_t inter, const uint8_t* w13_codes, const uint8_t* w13_scales,
+                         const float* w13_tensor_scales, const uint8_t* w2_codes, const uint8_t* w2_scales,
+                         const float* w2_tensor_scales, const float* act_tensor_scales, void* out_bf16,
+                         void* workspace, size_t workspace_bytes, const fp4_moe_debug* dbg, void* stream) {
+    FP4_REQUIRE(fmt == FP4_FMT_MX || fmt == FP4_FMT_NV, FP4_ERR_INVALID, "bad format %d", (int)fmt);
+    FP4_REQUIRE(tokens >= 0, FP4_ERR_INVALID, "negative tokens");
+    FP4_REQUIRE(topk >= 1 && topk <= 16, FP4_ERR_INVALID, "topk=%d outside [1, 16]", topk);
+    FP4_REQUIRE(num_experts >= 1 && num_experts <= 4096, FP4_ERR_INVALID, "num_experts=%d outside [1, 4096]", num_experts);
+    FP4_REQUIRE(hidden > 0 && inter > 0, FP4_ERR_INVALID, "hidden and inter must be positive");
+    FP4_REQUIRE(hidden % 128 == 0 && inter % 128 == 0, FP4_ERR_SHAPE, "hidden=%lld and inter=%lld must be multiples of 128",
+                (long long)hidden, (long long)inter);
+    FP4_REQUIRE(tokens * topk < (int64_t)1 << 30, FP4_ERR_SHAPE, "tokens*topk too large");
+    if (tokens == 0) return ok();
+    FP4_PTR(x_bf16);
+    FP4_SCALAR_PTR(topk_ids);
+    FP4_SCALAR_PTR(topk_weights);
+    FP4_PTR(w13_codes);
+    FP4_PTR(w13_scales);
+    FP4_PTR(w2_codes);
+    FP4_PTR(w2_scales);
+    FP4_PTR(out_bf16);
+    if (fmt == FP4_FMT_NV) {
+        FP4_SCALAR_PTR(w13_tensor_scales);
+        FP4_SCALAR_PTR(w2_tensor_scales);
+        FP4_SCALAR_PTR(act_tensor_scales);
+    }
+    const size_t need = fp4::moe_workspace_bytes(fmt, tokens, hidden, topk, num_experts, inter);
+    FP4_REQUIRE(workspace != nullptr && workspace_bytes >= need, FP4_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu",
+                need, workspace ? workspace_bytes : (size_t)0);
+    FP4_REQUIRE(aligned16(workspace), FP4_ERR_ALIGN, "workspace is not 16-byte aligned");
+    fp4::MoeArgs a{};
+    a.fmt = fmt;
+    a.x = static_cast<const uint16_t*>(x_bf16);
+    a.tokens = tokens;
+    a.hidden = hidden;
+    a.inter = inter;
+    a.ids = topk_ids;
+    a.weights = topk_weights;
+    a.topk = topk;
+    a.num_experts = num_experts;
+    a.w13c = w13_codes;
+    a.w13s = w13_scales;
+    a.w2c = w2_codes;
+    a.w2s = w2_scales;
+    a.w13ts = w13_tensor_scales;
+    a.w2ts = w2_tensor_scales;
+    a.act_ts = act_tensor_scales;
+    a.out = static_cast<uint16_t*>(out_bf16);
+    a.ws = workspace;
+    a.ws_bytes = workspace_bytes;
+    if (dbg) {
+        a.dbg = *dbg;
+        FP4_REQUIRE(aligned16(a.dbg.gate_up) && aligned16(a.dbg.h_bf16) && aligned16(a.dbg.h_codes) &&
+                        aligned16(a.dbg.h_scales) && aligned16(a.dbg.y),
+                    FP4_ERR_ALIGN, "debug buffers must be 16-byte aligned");
+    }
+    return hip_status(fp4::launch_moe(a, static_cast<hipStream_t>(stream)), "fp4_moe_grouped_gemm launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,213 @@
+/*
+ * fp4.h -- C ABI of the MI355X (gfx950) block-scaled FP4 library (libfp4.so).
+ *
+ * Formats.  An FP4 element is E2M1: one sign bit, two exponent bits and one
+ * mantissa bit, whose non-negative values are exactly {0, 0.5, 1, 1.5, 2, 3, 4, 6}
+ * ("DeepSeek-V4.1-Flash-NVFP4" explainer, section 2, NVFP4 format breakdown).
+ *   MXFP4: blocks of 32 consecutive elements along K share one UE8M0 scale byte
+ *          b meaning 2^(b-127) (same explainer, section 3, and the "DeepSeek-V4"
+ *          architecture article, section 6.3, 1x32 tiles).
+ *   NVFP4: groups of 16 consecutive elements along K share one E4M3 (OCP FP8
+ *          E4M3FN) scale byte, and the whole tensor shares one fp32 scale s_t
+ *          (explainer section 2: group_size 16 plus a tensor-level scale).
+ *
+ * Memory layout (all tensors row-major, K contiguous, no padding):
+ *   codes   uint8 [rows, k/2]: byte j holds element 2j in bits 3:0 and element
+ *           2j+1 in bits 7:4; a code is sign*8 + index into the value table.
+ *   MX      scales uint8 [rows, k/32] (UE8M0).
+ *   NV      scales uint8 [rows, k/16] (E4M3FN), plus one fp32 tensor scale in
+ *           device memory.
+ *   bf16 inputs/outputs are IEEE bfloat16 bit patterns with a leading dimension
+ *   in elements (ld_x, ldc, ld_out >= k or n).
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers are device pointers owned by the caller; the library never
+ *     allocates, frees or keeps them.  Every pointer must be 16-byte aligned and
+ *     every leading dimension a multiple of 8 elements, else FP4_ERR_ALIGN.
+ *   - All work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *     stream) and is asynchronous: the return value reports argument and
+ *     launch errors only.  Data-dependent results (the remap's inexact count,
+ *     computed tensor scales) are written to device memory.
+ *   - Arguments are validated before any HIP call; a failing call enqueues
+ *     nothing and returns a negative fp4_status.  fp4_last_error() gives the
+ *     message of the last failure on the calling thread.
+ *   - Zero-sized problems return FP4_OK and enqueue nothing.
+ *   - Calls that overlap in time may not share output or workspace buffers.
+ */
+#ifndef FP4_H
+#define FP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FP4_OK = 0,
+    FP4_ERR_INVALID = -1,      /* null pointer, bad enum, negative size        */
+    FP4_ERR_SHAPE = -2,        /* k not a multiple of the block/group size ... */
+    FP4_ERR_ALIGN = -3,        /* pointer not 16-B aligned, ld not multiple of 8 */
+    FP4_ERR_UNSUPPORTED = -4,  /* no kernel for this combination               */
+    FP4_ERR_WORKSPACE = -5,    /* workspace null or smaller than required      */
+    FP4_ERR_HIP = -6           /* a HIP runtime call failed                    */
+} fp4_status;
+
+typedef enum { FP4_FMT_MX = 0, FP4_FMT_NV = 1 } fp4_format;
+typedef enum { FP4_DT_BF16 = 0, FP4_DT_F32 = 1 } fp4_dtype;
+
+/* Version of this ABI (incremented on any incompatible change). */
+int fp4_abi_version(void);
+
+/* Static text for a status code. */
+const char* fp4_status_string(int status);
+
+/* Message of the last failed call on the calling thread ("" if none). */
+const char* fp4_last_error(void);
+
+/*
+ * MXFP4 quantization ("DeepSeek-V4.1-Flash-NVFP4" explainer, section 3: one
+ * UE8M0 scale per 32 elements; "DeepSeek-V4" article, section 6.3).
+ * For each row and each block of 32 elements along k:
+ *   amax = max|x|; E = floor(log2 amax) - 2 (E = -127 when amax = 0), clamped to
+ *   [-127, 127]; scales = E + 127; code = round-to-nearest-even of x * 2^-E onto
+ *   the E2M1 values, saturating at 6, keeping the sign bit of x (so -0.0 gives 0x8).
+ * x_bf16: [rows, ld_x] bf16; codes: [rows, k/2]; scales: [rows, k/32].
+ * Errors: k % 32 != 0 -> FP4_ERR_SHAPE.  Inputs must be finite.
+ */
+int fp4_quantize_mx(const void* x_bf16, int64_t rows, int64_t k, int64_t ld_x,
+                    uint8_t* codes, uint8_t* scales, void* stream);
+
+/*
+ * NVFP4 quantization (explainer, section 2: groups of 16 with a per-group scale
+ * bringing the group into [-6, 6] and a tensor-level scale; section 4: activation
+ * scales are calibrated).
+ *   s_t = fp32(amax_tensor / (6 * 448)) unless tensor_scale_is_input != 0, in
+ *   which case *tensor_scale (device fp32) is read as the calibrated s_t;
+ *   per group: s_g = E4M3 round-to-nearest-even of amax_g / (6 s_t), saturating
+ *   at 448; code = E2M1 round-to-nearest-even of x / (s_g s_t), saturating at 6.
+ *   Each step is a single correct rounding of the exact real quotient.  When
+ *   s_t = 0 or s_g = 0 the group's codes are signed zeros and s_g = 0.
+ * codes: [rows, k/2]; scales: [rows, k/16]; tensor_scale: one device float,
+ * written when computed.  workspace: device memory of at least
+ * fp4_quantize_nv_workspace_bytes() bytes (used for the tensor amax).
+ * Errors: k % 16 != 0 -> FP4_ERR_SHAPE; workspace too small -> FP4_ERR_WORKSPACE.
+ */
+int fp4_quantize_nv(const void* x_bf16, int64_t rows, int64_t k, int64_t ld_x,
+                    uint8_t* codes, uint8_t* scales, float* tensor_scale,
+                    int tensor_scale_is_input,
+                    void* workspace, size_t workspace_bytes, void* stream);
+size_t fp4_quantize_nv_workspace_bytes(int64_t rows, int64_t k);
+
+/*
+ * Lossless MXFP4 -> NVFP4 scale remap (explainer, section 1: NVFP4's finer
+ * 16-element scale layout can re-express MXFP4 weights block by block without
+ * loss; section 6: the conversion script's E2M1 -> E4M3 remap).
+ * Codes are reused unchanged (the NVFP4 tensor is (codes, scales_e4m3, s_t)).
+ *   E_max = max over blocks of (scale byte - 127); k = E_max - 8;
+ *   *tensor_scale = 2^k; both 16-groups of a block with exponent E_b get the
+ *   E4M3 value nearest 2^(E_b - k) (exact for E_b - k in [-9, 8]).
+ *   *n_inexact_blocks = number of blocks with a nonzero code whose 2^(E_b - k)
+ *   is below 2^-9 (those lose precision); 0 means the remap is lossless.
+ * codes: [rows, k/2]; scales_e8m0: [rows, k/32]; scales_e4m3: [rows, k/16];
+ * tensor_scale: 1 device float; n_inexact_blocks: 1 device int32.
+ * Errors: k % 32 != 0 -> FP4_ERR_SHAPE.
+ */
+int fp4_remap_mx_to_nv(const uint8_t* codes, const uint8_t* scales_e8m0,
+                       int64_t rows, int64_t k, uint8_t* scales_e4m3,
+                       float* tensor_scale, int32_t* n_inexact_blocks, void* stream);
+
+/*
+ * Dequantization (explainer, section 2: the block scales multiply back in;
+ * "DeepSeek-V4 FP4 QAT" article, section 4.2: FP4 data times the scale).
+ *   MX: value = (-1)^s * MAG[i] * 2^(b-127), exact in fp32 and bf16.
+ *   NV: fp32 value = round-to-nearest-even(MAG[i] * s_g * s_t); bf16 output is
+ *       the bf16 rounding of that fp32 value.
+ * out: [rows, ld_out] of out_dtype.  tensor_scale: device float (NV only).
+ * Errors: k % 32 (MX) or k % 16 (NV) != 0 -> FP4_ERR_SHAPE.
+ */
+int fp4_dequant(fp4_format fmt, const uint8_t* codes, const uint8_t* scales,
+                const float* tensor_scale, int64_t rows, int64_t k,
+                void* out, fp4_dtype out_dtype, int64_t ld_out, void* stream);
+
+/*
+ * W4A4 GEMM: C[m, n] = sum_k A_hat[m, k] * B_hat[n, k] with fp32 accumulation
+ * (explainer, section 2: activations and weights both 4-bit block-scaled, the
+ * accumulator rescaled per block).  A_hat, B_hat are the exact dequantized
+ * operands; B is given [n, k] (the nn.Linear weight layout), so C = A . B^T.
+ *   MX: scaled MFMA with the UE8M0 block scales applied by the matrix core.
+ *   NV: operands expanded exactly to bf16 (code * s_g) and multiplied with bf16
+ *       MFMA; the product is scaled by (*a_tensor_scale) * (*b_tensor_scale).
+ * c: [m, ldc] of c_dtype.  Tensor scales are device floats (NV only, else NULL).
+ * Errors: k % 32 (MX) or k % 16 (NV) != 0 -> FP4_ERR_SHAPE.
+ */
+int fp4_gemm(fp4_format fmt,
+             const uint8_t* a_codes, const uint8_t* a_scales, const float* a_tensor_scale,
+             const uint8_t* b_codes, const uint8_t* b_scales, const float* b_tensor_scale,
+             int64_t m, int64_t n, int64_t k,
+             void* c, fp4_dtype c_dtype, int64_t ldc, void* stream);
+
+/*
+ * Optional intermediate outputs of fp4_moe_grouped_gemm, for staged testing.
+ * Every member may be NULL.  Slot s = t * topk + j (token t, choice j).
+ *   counts    int32 [num_experts]    slots routed to each expert
+ *   offsets   int32 [num_experts+1]  exclusive prefix sum of counts
+ *   perm      int32 [tokens*topk]    slots grouped by expert, stable
+ *   gate_up   fp32  [tokens*topk, 2*inter]  g (first inter) then u, per slot
+ *   h_bf16    bf16  [tokens*topk, inter]    SiLU(g)*u rounded to bf16
+ *   h_codes   uint8 [tokens*topk, inter/2], h_scales [tokens*topk, inter/32|16]
+ *   y         fp32  [tokens*topk, hidden]   down-projection output per slot
+ */
+typedef struct fp4_moe_debug {
+    int32_t* counts;
+    int32_t* offsets;
+    int32_t* perm;
+    float* gate_up;
+    void* h_bf16;
+    uint8_t* h_codes;
+    uint8_t* h_scales;
+    float* y;
+} fp4_moe_debug;
+
+/*
+ * Routed-expert MoE layer on block-scaled FP4 weights and activations
+ * (explainer, section 3: the routed experts' w1/w2/w3 are the quantized
+ * layers; "DeepSeek-V4" article, section 2: 384 routed experts, 6 active;
+ * section 6.1: dispatch to experts and combine back).  For each token t and
+ * choice j with e = topk_ids[t, j]:
+ *   x_hat = dequant(quant(x[t]))  (MX; or NV with s_t = act_tensor_scales[0])
+ *   g = x_hat . w1[e]^T, u = x_hat . w3[e]^T   (w13[e] rows 0..inter-1 are w1,
+ *                                               rows inter..2*inter-1 are w3)
+ *   h = bf16(SiLU(g) * u); h_hat = dequant(quant(h)) (NV: s_t = act_tensor_scales[1])
+ *   y = h_hat . w2[e]^T;  out[t] = bf16(sum_j topk_weights[t, j] * y)
+ * x_bf16 [tokens, hidden]; topk_ids int32 [tokens, topk] in [0, num_experts);
+ * topk_weights fp32 [tokens, topk];
+ * w13_codes [E, 2*inter, hidden/2], w13_scales [E, 2*inter, hidden/32|16];
+ * w2_codes [E, hidden, inter/2], w2_scales [E, hidden, inter/32|16];
+ * NV: w13_tensor_scales, w2_tensor_scales fp32 [E] and act_tensor_scales fp32 [2]
+ * (device); MX: all three NULL.  out_bf16 [tokens, hidden].
+ * workspace: at least fp4_moe_workspace_bytes(...) bytes of device memory.
+ * Errors: hidden or inter not a multiple of 128 -> FP4_ERR_SHAPE; topk < 1 or
+ * topk > 16 -> FP4_ERR_INVALID; workspace too small -> FP4_ERR_WORKSPACE.
+ * Expert ids outside [0, num_experts) are not checked on the device and are
+ * undefined behaviour.
+ */
+int fp4_moe_grouped_gemm(fp4_format fmt, const void* x_bf16, int64_t tokens, int64_t hidden,
+                         const int32_t* topk_ids, const float* topk_weights, int topk,
+                         int num_experts, int64_t inter,
+                         const uint8_t* w13_codes, const uint8_t* w13_scales,
+                         const float* w13_tensor_scales,
+                         const uint8_t* w2_codes, const uint8_t* w2_scales,
+                         const float* w2_tensor_scales,
+                         const float* act_tensor_scales,
+                         void* out_bf16, void* workspace, size_t workspace_bytes,
+                         const fp4_moe_debug* dbg, void* stream);
+size_t fp4_moe_workspace_bytes(fp4_format fmt, int64_t tokens, int64_t hidden, int topk,
+                               int num_experts, int64_t inter);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP4_H */

@@ -1,0 +1,106 @@
+"""GPU parity of the W4A4 GEMM against the oracle: every output element within
+|C - C_ref| <= 1e-5 * sum_k |a b| (bf16 output: inside the rounded bracket)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_fp4_mx_amd as F
+import workloads as W
+from oracle import gemm as G
+from oracle import quant as Q
+from gpu_util import DEV, chunked, dev_bf16, quantize_mx, quantize_nv
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-5
+
+
+def _run_gemm(fmt, a, b, dtype, st=(None, None)):
+    m, n = a[0].shape[0], b[0].shape[0]
+    c = torch.empty((m, n), dtype=dtype, device=DEV)
+    F.fp4_gemm(F.FMT_MX if fmt == "mx" else F.FMT_NV, a[0], a[1], b[0], b[1], c, st[0], st[1])
+    torch.cuda.synchronize()
+    return c
+
+
+def _assert_within(c, Cref, S, rows=None, cols=None):
+    got = c if rows is None else c[rows][:, cols]
+    if got.dtype == torch.float32:
+        ok = G.within_tol_f32(got.cpu().numpy(), Cref, S, TOL)
+    else:
+        ok = G.within_tol_bf16(W.bf16_bits(got), Cref, S, TOL)
+    if not ok.all():
+        bad = np.argwhere(~ok)[:8]
+        g = got.float().cpu().numpy()
+        msg = "\n".join(f"  {tuple(i)}: got {g[tuple(i)]!r} ref {Cref[tuple(i)]!r} S {S[tuple(i)]!r}" for i in bad)
+        raise AssertionError(f"{(~ok).sum()} of {ok.size} outside tolerance\n{msg}")
+
+
+def _mx_case(wl, dtype):
+    ab, wb = W.bf16_bits(wl.A), W.bf16_bits(wl.W)
+    a = quantize_mx(dev_bf16(ab))
+    b = quantize_mx(dev_bf16(wb))
+    c = _run_gemm("mx", a, b, dtype)
+    ea, eb = Q.mx_quantize(ab), Q.mx_quantize(wb)
+    Cref, S = G.gemm_ref("mx", *ea, *eb)
+    _assert_within(c, Cref, S)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_gemm_mx_workload1(dtype):
+    _mx_case(W.workload1(), dtype)
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 1, 32), (37, 75, 96), (130, 260, 160), (16, 512, 4096), (300, 200, 544)])
+def test_gemm_mx_ragged(m, n, k):
+    _mx_case(W.random_linear(m * 1000 + n + k, m, n, k, outlier_p=0.01), torch.float32)
+
+
+def test_gemm_mx_workload3_full_sampled():
+    """Workload 3 (4096^3) at full size, in the launch the bench times; every
+    output of 48 sampled rows and 48 sampled columns is checked."""
+    wl = W.workload3()
+    ab, wb = W.bf16_bits(wl.A), W.bf16_bits(wl.W)
+    a = quantize_mx(dev_bf16(ab))
+    b = quantize_mx(dev_bf16(wb))
+    c = _run_gemm("mx", a, b, torch.bfloat16)
+    rng = np.random.default_rng(3)
+    rows = np.sort(rng.choice(4096, 48, replace=False))
+    cols = np.sort(rng.choice(4096, 48, replace=False))
+    ea = Q.mx_quantize(ab[rows])
+    eb = chunked(Q.mx_quantize, wb)
+    Cref, S = G.gemm_ref("mx", *ea, *eb)
+    _assert_within(c[rows], Cref, S)
+    Cref2, S2 = G.gemm_ref("mx", *chunked(Q.mx_quantize, ab), eb[0][cols], eb[1][cols])
+    _assert_within(c[:, cols], Cref2, S2)
+
+
+def test_gemm_mx_deterministic():
+    wl = W.random_linear(77, 256, 384, 1024)
+    a = quantize_mx(dev_bf16(W.bf16_bits(wl.A)))
+    b = quantize_mx(dev_bf16(W.bf16_bits(wl.W)))
+    c1 = _run_gemm("mx", a, b, torch.float32)
+    c2 = _run_gemm("mx", a, b, torch.float32)
+    assert torch.equal(c1, c2)
+
+
+def _nv_case(wl, dtype):
+    ab, wb = W.bf16_bits(wl.A), W.bf16_bits(wl.W)
+    ac, as_, ats = quantize_nv(dev_bf16(ab))
+    bc, bs, bts = quantize_nv(dev_bf16(wb))
+    c = _run_gemm("nv", (ac, as_), (bc, bs), dtype, (ats, bts))
+    ea, eb = Q.nv_quantize(ab), Q.nv_quantize(wb)
+    Cref, S = G.gemm_ref("nv", ea[0], ea[1], eb[0], eb[1], ea[2], eb[2])
+    _assert_within(c, Cref, S)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_gemm_nv_small(dtype):
+    _nv_case(W.random_linear(91, 64, 96, 512, outlier_p=0.01), dtype)
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 3, 16), (37, 75, 112), (130, 260, 4096)])
+def test_gemm_nv_ragged(m, n, k):
+    _nv_case(W.random_linear(m * 7 + n + k, m, n, k), torch.float32)

@@ -1,0 +1,244 @@
+"""GPU parity of quantize / dequantize / remap against the CPU oracle:
+codes and scales bit-exact at the workloads' full sizes and on edge cases."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_fp4_mx_amd as F
+import workloads as W
+from oracle import formats as OF
+from oracle import quant as Q
+from gpu_util import (DEV, chunked, describe_mismatch, dev_bf16, empty_u8, host_u8, quantize_mx,
+                      quantize_nv)
+
+pytestmark = pytest.mark.gpu
+
+
+def _crafted(K, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = []
+    ties = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, 7.0, 4.0, 0.5, 3.0])
+    for scale in (1.0, 2.0 ** -20, 2.0 ** 30, 2.0 ** -126, 2.0 ** -128, 2.0 ** -133, 2.0 ** 100):
+        rows.append(rng.choice(ties, K) * scale * rng.choice([-1, 1], K))
+    rows.append(np.zeros(K))
+    rows.append(np.where(np.arange(K) % 2 == 1, -0.0, 0.0))
+    rows.append(rng.standard_normal(K) * 2.0 ** -130)
+    rows.append(rng.standard_normal(K) * 1e35)
+    rows.append(rng.standard_t(3, K) * 0.02)
+    rows.append(rng.standard_normal(K) * np.where(rng.random(K) < 0.05, 1000.0, 1.0))
+    return W.bf16_bits(W.to_bf16(np.array(rows)))
+
+
+def _check_mx(bits):
+    x = dev_bf16(bits)
+    c, s = quantize_mx(x)
+    torch.cuda.synchronize()
+    ec, es = chunked(Q.mx_quantize, bits)
+    gs, gc = host_u8(s), host_u8(c)
+    assert np.array_equal(gs, es), describe_mismatch("mx scales", gs, es)
+    assert np.array_equal(gc, ec), describe_mismatch("mx codes", gc, ec)
+
+
+def _check_nv(bits, s_t=None):
+    x = dev_bf16(bits)
+    c, s, ts = quantize_nv(x, s_t)
+    torch.cuda.synchronize()
+    ec, es, est = chunked(Q.nv_quantize, bits, s_t=(Q.nv_tensor_scale(bits) if s_t is None else s_t))
+    assert ts.item() == float(est), (ts.item(), float(est))
+    gs, gc = host_u8(s), host_u8(c)
+    assert np.array_equal(gs, es), describe_mismatch("nv scales", gs, es)
+    assert np.array_equal(gc, ec), describe_mismatch("nv codes", gc, ec)
+
+
+@pytest.mark.parametrize("which", ["A", "W"])
+def test_mx_quantize_workload1(which):
+    wl = W.workload1()
+    _check_mx(W.bf16_bits(getattr(wl, which)))
+
+
+@pytest.mark.parametrize("which", ["A", "W"])
+def test_mx_quantize_workload2_full(which):
+    wl = W.workload2()
+    _check_mx(W.bf16_bits(getattr(wl, which)))
+
+
+def test_mx_quantize_crafted_edges():
+    _check_mx(_crafted(256))
+
+
+@pytest.mark.parametrize("rows,k", [(1, 32), (3, 96), (37, 160), (130, 4096)])
+def test_mx_quantize_ragged(rows, k):
+    rng = np.random.default_rng(rows * 7 + k)
+    _check_mx(W.bf16_bits(W.to_bf16(rng.standard_normal((rows, k)))))
+
+
+def test_mx_quantize_strided_rows():
+    rng = np.random.default_rng(3)
+    full = W.to_bf16(rng.standard_normal((40, 200)))
+    bits = W.bf16_bits(full)[:, :160]
+    x = W.from_bits(W.bf16_bits(full)).to(DEV)[:, :160]
+    assert x.stride(0) == 200
+    c, s = quantize_mx(x)
+    torch.cuda.synchronize()
+    ec, es = Q.mx_quantize(bits)
+    assert np.array_equal(host_u8(s), es) and np.array_equal(host_u8(c), ec)
+
+
+def test_mx_quantize_exhaustive_bf16_patterns():
+    """Every finite bf16 pattern, placed in blocks whose amax fixes a range of
+    block exponents (each block: one anchor value and 31 patterns)."""
+    pats = np.arange(1 << 16, dtype=np.uint32)
+    pats = pats[((pats >> 7) & 0xFF) != 0xFF].astype(np.uint16)
+    mags = OF.bf16_bits_to_f64(pats & 0x7FFF)
+    rows = []
+    rows.append(np.zeros((1, 32), np.uint16))
+    for anchor_exp in range(-133, 128, 3):
+        anchor = 1.5 * 2.0 ** anchor_exp
+        sel = pats[mags <= anchor]
+        if len(sel) == 0:
+            continue
+        sel = sel[:: max(1, len(sel) // (31 * 64))][: 31 * 64]
+        n = len(sel) // 31
+        if n == 0:
+            continue
+        blk = sel[: n * 31].reshape(n, 31)
+        a = W.bf16_bits(W.to_bf16(np.full((n, 1), anchor)))
+        rows.append(np.concatenate([a, blk], axis=1))
+    bits = np.concatenate(rows).reshape(-1, 32)
+    pad = (-bits.shape[0]) % 4
+    bits = np.concatenate([bits, np.zeros((pad, 32), np.uint16)]).reshape(-1, 128)
+    _check_mx(bits)
+
+
+@pytest.mark.parametrize("which", ["A", "W"])
+def test_nv_quantize_workload2_full(which):
+    wl = W.workload2()
+    _check_nv(W.bf16_bits(getattr(wl, which)))
+
+
+@pytest.mark.parametrize("s_t", [1.0 / 64, 0.0123, 2.0 ** -20, 3.0e-30])
+def test_nv_quantize_supplied_scale_crafted(s_t):
+    _check_nv(_crafted(256, seed=5), s_t=s_t)
+
+
+def test_nv_quantize_dynamic_scale_crafted():
+    _check_nv(_crafted(128, seed=6))
+
+
+@pytest.mark.parametrize("rows,k", [(1, 16), (5, 48), (33, 272)])
+def test_nv_quantize_ragged(rows, k):
+    rng = np.random.default_rng(rows + k)
+    _check_nv(W.bf16_bits(W.to_bf16(rng.standard_t(3, (rows, k)) * 0.02)))
+
+
+def test_nv_quantize_power_of_two_scale_ties():
+    """A power-of-two s_t makes exact E2M1 midpoints common: the exact tie path."""
+    rng = np.random.default_rng(9)
+    bits = W.bf16_bits(W.to_bf16(rng.choice([0.25, 0.75, 1.25, 2.5, 3.5, 5.0], (64, 256)) * rng.choice([1, 2, 4, 8], (64, 256))))
+    _check_nv(bits, s_t=2.0 ** -3)
+
+
+@pytest.mark.parametrize("fmt", ["mx", "nv"])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_dequant_bit_exact(fmt, dtype):
+    wl = W.random_linear(50, 96, 8, 512, outlier_p=0.01)
+    bits = W.bf16_bits(wl.A)
+    x = dev_bf16(bits)
+    if fmt == "mx":
+        c, s = quantize_mx(x)
+        ts = None
+        ec, es = Q.mx_quantize(bits)
+        est = None
+    else:
+        c, s, ts = quantize_nv(x)
+        ec, es, est = Q.nv_quantize(bits)
+    out = torch.empty((96, 520), dtype=dtype, device=DEV)[:, :512]
+    F.fp4_dequant(F.FMT_MX if fmt == "mx" else F.FMT_NV, c, s, ts, out)
+    torch.cuda.synchronize()
+    if dtype == torch.float32:
+        exp = Q.dequant_fp32(fmt, ec, es, est)
+        got = out.cpu().numpy()
+        assert np.array_equal(got.view(np.uint32), exp.view(np.uint32)), describe_mismatch("deq f32", got, exp)
+    else:
+        exp = Q.dequant_bf16_bits(fmt, ec, es, est)
+        got = W.bf16_bits(out)
+        assert np.array_equal(got, exp), describe_mismatch("deq bf16", got, exp)
+
+
+def test_dequant_mx_extreme_scales():
+    codes = np.tile(np.arange(16, dtype=np.uint8), (4, 8))
+    packed = Q.pack_nibbles(codes)
+    scales = np.array([[0, 1, 127, 252]] * 4, np.uint8)
+    c = torch.from_numpy(packed).to(DEV)
+    s = torch.from_numpy(np.ascontiguousarray(scales)).to(DEV)
+    out = torch.empty((4, 128), dtype=torch.float32, device=DEV)
+    F.fp4_dequant(F.FMT_MX, c, s, None, out)
+    torch.cuda.synchronize()
+    exp = Q.dequant_fp32("mx", packed, scales)
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), exp.view(np.uint32))
+
+
+@pytest.mark.parametrize("which", ["A", "W"])
+def test_remap_workload2_lossless(which):
+    wl = W.workload2()
+    bits = W.bf16_bits(getattr(wl, which))
+    x = dev_bf16(bits)
+    c, s = quantize_mx(x)
+    snv = empty_u8(bits.shape[0], bits.shape[1] // 16)
+    ts = torch.zeros(1, dtype=torch.float32, device=DEV)
+    n = torch.full((1,), -7, dtype=torch.int32, device=DEV)
+    F.fp4_remap_mx_to_nv(c, s, snv, ts, n)
+    torch.cuda.synchronize()
+    ec, es = chunked(Q.mx_quantize, bits)
+    esnv, est, en = Q.remap_mx_to_nv(ec, es)
+    assert n.item() == en == 0
+    assert ts.item() == float(est)
+    assert np.array_equal(host_u8(snv), esnv)
+    # lossless: the NV reading of the same codes dequantizes to identical fp32 values
+    o1 = torch.empty(x.shape, dtype=torch.float32, device=DEV)
+    o2 = torch.empty(x.shape, dtype=torch.float32, device=DEV)
+    F.fp4_dequant(F.FMT_MX, c, s, None, o1)
+    F.fp4_dequant(F.FMT_NV, c, snv, ts, o2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int32), o2.view(torch.int32))
+
+
+def test_remap_inexact_blocks_counted():
+    rng = np.random.default_rng(26)
+    bits = W.bf16_bits(W.to_bf16(rng.standard_normal((4, 256))))
+    ec, es = Q.mx_quantize(bits)
+    es = es.copy()
+    es[0, 0] = 137; es[1, 1] = 120; es[1, 2] = 119; es[2, 3] = 107; es[3, 4] = 0
+    c4 = Q.unpack_nibbles(ec); c4[3, 128:160] &= 8; ec = Q.pack_nibbles(c4)
+    c = torch.from_numpy(ec).to(DEV)
+    s = torch.from_numpy(es).to(DEV)
+    snv = empty_u8(4, 16)
+    ts = torch.zeros(1, dtype=torch.float32, device=DEV)
+    n = torch.zeros(1, dtype=torch.int32, device=DEV)
+    F.fp4_remap_mx_to_nv(c, s, snv, ts, n)
+    torch.cuda.synchronize()
+    esnv, est, en = Q.remap_mx_to_nv(ec, es)
+    assert en == 2 and n.item() == 2
+    assert ts.item() == float(est)
+    assert np.array_equal(host_u8(snv), esnv)
+
+
+def test_quantize_deterministic_run_to_run():
+    wl = W.workload2()
+    x = dev_bf16(W.bf16_bits(wl.A))
+    c1, s1 = quantize_mx(x)
+    c2, s2 = quantize_mx(x)
+    n1, ns1, t1 = quantize_nv(x)
+    n2, ns2, t2 = quantize_nv(x)
+    torch.cuda.synchronize()
+    assert torch.equal(c1, c2) and torch.equal(s1, s2)
+    assert torch.equal(n1, n2) and torch.equal(ns1, ns2) and torch.equal(t1, t2)
+
+
+def test_zero_size_calls_are_noops():
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device=DEV)
+    c = empty_u8(0, 32); s = empty_u8(0, 2)
+    F.fp4_quantize_mx(x, c, s)
+    torch.cuda.synchronize()
