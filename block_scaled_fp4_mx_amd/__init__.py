@@ -29,8 +29,9 @@ _vp, _i64, _i32, _sz = _c.c_void_p, _c.c_int64, _c.c_int, _c.c_size_t
 
 class MoeDebug(_c.Structure):
     """Mirror of struct fp4_moe_debug (all members nullable device pointers)."""
-    _fields_ = [("counts", _vp), ("offsets", _vp), ("perm", _vp), ("gate_up", _vp),
-                ("h_bf16", _vp), ("h_codes", _vp), ("h_scales", _vp), ("y", _vp)]
+    _fields_ = [("x_codes", _vp), ("x_scales", _vp), ("counts", _vp), ("offsets", _vp), ("perm", _vp), ("gate_up", _vp),
+                ("h_bf16", _vp), ("h_codes", _vp), ("h_scales", _vp), ("y", _vp),
+                ("gate_up_in", _vp), ("h_codes_in", _vp), ("h_scales_in", _vp)]
 
 
 _SIGS = {

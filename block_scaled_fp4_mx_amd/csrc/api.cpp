@@ -196,11 +196,12 @@ int fp4_moe_grouped_gemm(fp4_format fmt, const void* x_bf16, int64_t tokens, int
     FP4_REQUIRE(fmt == FP4_FMT_MX || fmt == FP4_FMT_NV, FP4_ERR_INVALID, "bad format %d", (int)fmt);
     FP4_REQUIRE(tokens >= 0, FP4_ERR_INVALID, "negative tokens");
     FP4_REQUIRE(topk >= 1 && topk <= 16, FP4_ERR_INVALID, "topk=%d outside [1, 16]", topk);
-    FP4_REQUIRE(num_experts >= 1 && num_experts <= 4096, FP4_ERR_INVALID, "num_experts=%d outside [1, 4096]", num_experts);
+    FP4_REQUIRE(num_experts >= 1 && num_experts <= 1024, FP4_ERR_INVALID, "num_experts=%d outside [1, 1024]", num_experts);
     FP4_REQUIRE(hidden > 0 && inter > 0, FP4_ERR_INVALID, "hidden and inter must be positive");
     FP4_REQUIRE(hidden % 128 == 0 && inter % 128 == 0, FP4_ERR_SHAPE, "hidden=%lld and inter=%lld must be multiples of 128",
                 (long long)hidden, (long long)inter);
-    FP4_REQUIRE(tokens * topk < (int64_t)1 << 30, FP4_ERR_SHAPE, "tokens*topk too large");
+    FP4_REQUIRE(tokens * topk < (int64_t)1 << 30 && fp4::moe_max_tiles(tokens, topk, num_experts) <= 65535,
+                FP4_ERR_SHAPE, "tokens*topk=%lld too large", (long long)(tokens * topk));
     if (tokens == 0) return ok();
     FP4_PTR(x_bf16);
     FP4_SCALAR_PTR(topk_ids);
@@ -242,8 +243,11 @@ int fp4_moe_grouped_gemm(fp4_format fmt, const void* x_bf16, int64_t tokens, int
     if (dbg) {
         a.dbg = *dbg;
         FP4_REQUIRE(aligned16(a.dbg.gate_up) && aligned16(a.dbg.h_bf16) && aligned16(a.dbg.h_codes) &&
-                        aligned16(a.dbg.h_scales) && aligned16(a.dbg.y),
+                        aligned16(a.dbg.h_scales) && aligned16(a.dbg.y) && aligned16(a.dbg.gate_up_in) &&
+                        aligned16(a.dbg.h_codes_in) && aligned16(a.dbg.h_scales_in),
                     FP4_ERR_ALIGN, "debug buffers must be 16-byte aligned");
+        FP4_REQUIRE((a.dbg.h_codes_in == nullptr) == (a.dbg.h_scales_in == nullptr), FP4_ERR_INVALID,
+                    "h_codes_in and h_scales_in must be given together");
     }
     return hip_status(fp4::launch_moe(a, static_cast<hipStream_t>(stream)), "fp4_moe_grouped_gemm launch");
 }

@@ -106,6 +106,7 @@ struct MoeArgs {
     size_t ws_bytes;
     fp4_moe_debug dbg;
 };
+int64_t moe_max_tiles(int64_t tokens, int topk, int num_experts);
 size_t moe_workspace_bytes(int fmt, int64_t tokens, int64_t hidden, int topk, int num_experts,
                            int64_t inter);
 hipError_t launch_moe(const MoeArgs& a, hipStream_t s);

@@ -1,10 +1,500 @@
-// Routed-expert MoE path (placeholder until the grouped kernels land).
-#include "fp4_internal.h"
+// Routed-expert MoE layer on block-scaled FP4 for gfx950.
+//
+// Pipeline (all on one stream, no host synchronization):
+//   1. quantize X per token row (MX, or NV with the calibrated activation s_t);
+//   2. routing metadata on the device: per-block expert histograms, one scan
+//      block (offsets, per-block bases, row-tile list) and a stable placement
+//      of every slot s = t*topk + j into its expert's segment (perm / slot_pos);
+//   3. grouped gate/up GEMM over row tiles of each expert's segment, gathering
+//      the quantized X rows through perm; each wave holds g and u for the same
+//      (row, column) positions, so the epilogue forms h = SiLU(g) * u in
+//      registers, rounds it to bf16 and quantizes it (MX or NV) straight from LDS;
+//   4. grouped down GEMM on the quantized h rows, whose epilogue multiplies by
+//      the routing weight and adds into an fp32 [tokens, hidden] buffer;
+//   5. cast of that buffer to bf16.
+// The steps follow the expert path of the routed experts' w1/w3/w2 projections
+// ("DeepSeek-V4.1-Flash-NVFP4" explainer, section 3) and the dispatch /
+// combine of tokens to experts ("DeepSeek-V4" article, section 6.1).
+#include "mma_core.h"
+#include "quant_device.h"
 
 namespace fp4 {
+namespace {
 
-size_t moe_workspace_bytes(int, int64_t, int64_t, int, int, int64_t) { return 256; }
+constexpr int kRouteSlots = 512;    // slots per routing block (bit masks of 16 words per expert)
+constexpr int kMaxExperts = 1024;
+constexpr int kBM = 128;            // routed rows per grouped-GEMM tile
+constexpr int kGuCols = 64;         // intermediate columns (of g and of u) per gate/up tile
+constexpr int kDnCols = 128;        // hidden columns per down tile
+constexpr int kThreads = 256;
 
-hipError_t launch_moe(const MoeArgs&, hipStream_t) { return hipErrorNotSupported; }
+inline size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Layout {
+    size_t xc, xs, counts, offsets, blockbase, perm, slot_pos, tile_e, tile_r, ntiles, hc, hs, out32, total;
+    int64_t nblk, max_tiles;
+};
+
+Layout layout(int fmt, int64_t T, int64_t H, int topk, int E, int64_t I) {
+    Layout L{};
+    const int64_t S = T * topk;
+    const int blk = fmt == FP4_FMT_MX ? 32 : 16;
+    L.nblk = (S + kRouteSlots - 1) / kRouteSlots;
+    L.max_tiles = (S + kBM - 1) / kBM + (E < S ? E : S);
+    size_t o = 0;
+    auto take = [&](size_t bytes) { size_t at = o; o += a256(bytes); return at; };
+    L.xc = take((size_t)T * H / 2);
+    L.xs = take((size_t)T * H / blk);
+    L.counts = take((size_t)E * 4);
+    L.offsets = take((size_t)(E + 1) * 4);
+    L.blockbase = take((size_t)L.nblk * E * 4);
+    L.perm = take((size_t)S * 4);
+    L.slot_pos = take((size_t)S * 4);
+    L.tile_e = take((size_t)L.max_tiles * 4);
+    L.tile_r = take((size_t)L.max_tiles * 4);
+    L.ntiles = take(4);
+    L.hc = take((size_t)S * I / 2);
+    L.hs = take((size_t)S * I / blk);
+    L.out32 = take((size_t)T * H * 4);
+    L.total = o;
+    return L;
+}
+
+// ------------------------------------------------------------------ routing
+// Per block of kRouteSlots slots: expert histogram in LDS -> blockcount[b][e].
+__global__ __launch_bounds__(kRouteSlots) void route_count_kernel(const int32_t* __restrict__ ids, int64_t S, int E,
+                                                                  int32_t* __restrict__ blockcount) {
+    __shared__ int32_t cnt[kMaxExperts];
+    for (int e = threadIdx.x; e < E; e += kRouteSlots) cnt[e] = 0;
+    __syncthreads();
+    const int64_t s = (int64_t)blockIdx.x * kRouteSlots + threadIdx.x;
+    if (s < S) {
+        const int e = ids[s];
+        if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[e], 1);   // other ids route nowhere
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += kRouteSlots) blockcount[(int64_t)blockIdx.x * E + e] = cnt[e];
+}
+
+// Exclusive scan of a pair of ints over a 1024-thread block.
+__device__ void block_scan2(int& a, int& b, int* sh) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int ia = a, ib = b;
+    for (int off = 1; off < 64; off <<= 1) {
+        const int ta = __shfl_up(ia, off), tb = __shfl_up(ib, off);
+        if (lane >= off) { ia += ta; ib += tb; }
+    }
+    if (lane == 63) { sh[wave] = ia; sh[16 + wave] = ib; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int ra = 0, rb = 0;
+        for (int w = 0; w < 16; ++w) {
+            const int xa = sh[w], xb = sh[16 + w];
+            sh[w] = ra; sh[16 + w] = rb;
+            ra += xa; rb += xb;
+        }
+        sh[32] = ra; sh[33] = rb;
+    }
+    __syncthreads();
+    a = ia - a + sh[wave];
+    b = ib - b + sh[16 + wave];
+}
+
+// One block: totals per expert, exclusive offsets, per-block bases (in place of
+// the block counts) and the list of row tiles (expert, first row).
+__global__ __launch_bounds__(1024) void route_scan_kernel(int32_t* __restrict__ blockcount, int64_t nblk, int E,
+                                                          int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                          int32_t* __restrict__ tile_e, int32_t* __restrict__ tile_r,
+                                                          int32_t* __restrict__ ntiles) {
+    __shared__ int sh[40];
+    constexpr int EPT = kMaxExperts / 1024;       // experts per thread (1)
+    int tot[EPT];
+    int rows = 0, tiles = 0;
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) {
+        const int e = threadIdx.x * EPT + q;
+        int t = 0;
+        if (e < E)
+            for (int64_t b = 0; b < nblk; ++b) t += blockcount[b * E + e];
+        tot[q] = t;
+        rows += t;
+        tiles += (t + kBM - 1) / kBM;
+        if (e < E) counts[e] = t;
+    }
+    int prow = rows, ptile = tiles;
+    block_scan2(prow, ptile, sh);
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) {
+        const int e = threadIdx.x * EPT + q;
+        if (e >= E) break;
+        offsets[e] = prow;
+        int base = prow;
+        for (int64_t b = 0; b < nblk; ++b) {
+            const int c = blockcount[b * E + e];
+            blockcount[b * E + e] = base;
+            base += c;
+        }
+        const int nt = (tot[q] + kBM - 1) / kBM;
+        for (int i = 0; i < nt; ++i) {
+            tile_e[ptile + i] = e;
+            tile_r[ptile + i] = prow + i * kBM;
+        }
+        ptile += nt;
+        prow += tot[q];
+    }
+    if (threadIdx.x == 0) {
+        offsets[E] = sh[32];
+        *ntiles = sh[33];
+    }
+}
+
+// Stable placement: the rank of slot s among the earlier slots of its block with
+// the same expert comes from a per-expert bit mask of the block's slots.
+__global__ __launch_bounds__(kRouteSlots) void route_place_kernel(const int32_t* __restrict__ ids, int64_t S, int E,
+                                                                  const int32_t* __restrict__ blockbase,
+                                                                  int32_t* __restrict__ perm,
+                                                                  int32_t* __restrict__ slot_pos) {
+    constexpr int kWords = kRouteSlots / 32;
+    extern __shared__ uint32_t mask[];               // [E][kWords]
+    for (int i = threadIdx.x; i < E * kWords; i += kRouteSlots) mask[i] = 0u;
+    __syncthreads();
+    const int64_t s = (int64_t)blockIdx.x * kRouteSlots + threadIdx.x;
+    const int w = threadIdx.x >> 5, bit = threadIdx.x & 31;
+    int e = -1;
+    if (s < S) {
+        e = ids[s];
+        if ((unsigned)e < (unsigned)E) atomicOr(&mask[e * kWords + w], 1u << bit);
+        else e = -1;
+    }
+    __syncthreads();
+    if (e >= 0) {
+        int rank = __popc(mask[e * kWords + w] & ((1u << bit) - 1u));
+        for (int ww = 0; ww < w; ++ww) rank += __popc(mask[e * kWords + ww]);
+        const int pos = blockbase[(int64_t)blockIdx.x * E + e] + rank;
+        perm[pos] = (int32_t)s;
+        slot_pos[s] = pos;
+    }
+}
+
+// ------------------------------------------------------------------ grouped GEMMs
+struct GemmParams {
+    int fmt;
+    int64_t H, I;
+    int topk;
+    const uint8_t *xc, *xs;            // quantized X [T, H/2], [T, H/blk]
+    const uint8_t *w13c, *w13s, *w2c, *w2s;
+    const float *w13ts, *w2ts, *act_ts;
+    const int32_t *perm, *offsets, *tile_e, *tile_r, *ntiles;
+    const float* weights;              // [S]
+    uint8_t *hc, *hs;                  // quantized h [S, I/2], [S, I/blk] in routed order
+    float* out32;                      // [T, H]
+    fp4_moe_debug dbg;
+};
+
+__device__ __forceinline__ float silu_mul(float g, float u) {
+    return (g / (1.0f + expf(-g))) * u;
+}
+
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void moe_gate_up_kernel(GemmParams p) {
+    const int tile = blockIdx.y;
+    if (tile >= *p.ntiles) return;
+    const int e = p.tile_e[tile];
+    const int64_t r0 = p.tile_r[tile];
+    const int64_t rend = p.offsets[e + 1];
+    const int64_t c0 = (int64_t)blockIdx.x * kGuCols;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int lr = lane & 15, lk = lane >> 4;
+    const int blk = FMT == FP4_FMT_MX ? 32 : 16;
+    const int64_t H = p.H, I = p.I;
+
+    const uint8_t* a_rows[4];
+    const uint8_t* a_srow[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t pos = r0 + wm * 64 + i * 16 + lr;
+        if (pos < rend) {
+            const int64_t t = p.perm[pos] / p.topk;
+            a_rows[i] = p.xc + t * (H / 2);
+            a_srow[i] = p.xs + t * (H / blk);
+        } else {
+            a_rows[i] = nullptr;
+            a_srow[i] = nullptr;
+        }
+    }
+    const uint8_t* wc = p.w13c + (int64_t)e * (2 * I) * (H / 2);
+    const uint8_t* ws = p.w13s + (int64_t)e * (2 * I) * (H / blk);
+    const uint8_t* b_rows[4];
+    const uint8_t* b_srow[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int64_t col = c0 + wn * 32 + (j & 1) * 16 + lr;          // j 0,1: gate; 2,3: up
+        const int64_t brow = (j < 2 ? 0 : I) + col;
+        b_rows[j] = wc + brow * (H / 2);
+        b_srow[j] = ws + brow * (H / blk);
+    }
+    v4f acc[4][4];
+    zero_acc(acc);
+    const bool injected = p.dbg.gate_up_in != nullptr;
+    if (injected) {
+        // g|u given per slot (already scaled): place them in the accumulator layout
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t pos = r0 + wm * 64 + i * 16 + lk * 4 + r;
+                if (pos >= rend) continue;
+                const float* src = p.dbg.gate_up_in + (int64_t)p.perm[pos] * 2 * I;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int64_t col = c0 + wn * 32 + (j & 1) * 16 + lr;
+                    acc[i][j][r] = src[(j < 2 ? 0 : I) + col];
+                }
+            }
+    } else if (FMT == FP4_FMT_MX) {
+        mma_mx_64x64(acc, a_rows, a_srow, b_rows, b_srow, H, lane);
+    } else {
+        mma_nv_64x64(acc, a_rows, a_srow, b_rows, b_srow, H, lane);
+    }
+
+    const float gscale = (FMT == FP4_FMT_NV && !injected) ? __fmul_rn(p.act_ts[0], p.w13ts[e]) : 1.0f;
+    __shared__ __align__(16) uint16_t hs[kBM * kGuCols];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int rl = wm * 64 + i * 16 + lk * 4 + r;
+                const int cl = wn * 32 + j * 16 + lr;
+                float g = acc[i][j][r], u = acc[i][j + 2][r];
+                if (FMT == FP4_FMT_NV && !injected) {
+                    g = __fmul_rn(g, gscale);
+                    u = __fmul_rn(u, gscale);
+                }
+                const uint32_t hb = f32_to_bf16_rne(silu_mul(g, u));
+                hs[rl * kGuCols + cl] = (uint16_t)hb;
+                const int64_t pos = r0 + rl;
+                if (pos < rend && (p.dbg.gate_up || p.dbg.h_bf16)) {
+                    const int64_t slot = p.perm[pos];
+                    if (p.dbg.gate_up) {
+                        p.dbg.gate_up[slot * 2 * I + c0 + cl] = g;
+                        p.dbg.gate_up[slot * 2 * I + I + c0 + cl] = u;
+                    }
+                    if (p.dbg.h_bf16) static_cast<uint16_t*>(p.dbg.h_bf16)[slot * I + c0 + cl] = (uint16_t)hb;
+                }
+            }
+    __syncthreads();
+    // quantize the 128 x 64 bf16 tile: unit = 8 consecutive columns of one row
+    const double st_h = FMT == FP4_FMT_NV ? (double)p.act_ts[1] : 0.0;
+#pragma unroll
+    for (int q = 0; q < (kBM * kGuCols / 8) / kThreads; ++q) {
+        const int unit = threadIdx.x + q * kThreads;
+        const int rl = unit / (kGuCols / 8), cu = unit % (kGuCols / 8);
+        const uint4 v = *reinterpret_cast<const uint4*>(&hs[rl * kGuCols + cu * 8]);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        uint32_t sb;
+        const uint32_t packed = FMT == FP4_FMT_MX ? mx_quant8(w, sb) : nv_quant8(w, st_h, sb);
+        const int64_t pos = r0 + rl;
+        if (pos < rend) {
+            const int64_t col = c0 + cu * 8;
+            reinterpret_cast<uint32_t*>(p.hc + pos * (I / 2) + col / 2)[0] = packed;
+            const bool lead = (cu % (blk / 8)) == 0;
+            if (lead) p.hs[pos * (I / blk) + col / blk] = (uint8_t)sb;
+            if (p.dbg.h_codes || p.dbg.h_scales) {
+                const int64_t slot = p.perm[pos];
+                if (p.dbg.h_codes) reinterpret_cast<uint32_t*>(p.dbg.h_codes + slot * (I / 2) + col / 2)[0] = packed;
+                if (p.dbg.h_scales && lead) p.dbg.h_scales[slot * (I / blk) + col / blk] = (uint8_t)sb;
+            }
+        }
+    }
+}
+
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void moe_down_kernel(GemmParams p) {
+    const int tile = blockIdx.y;
+    if (tile >= *p.ntiles) return;
+    const int e = p.tile_e[tile];
+    const int64_t r0 = p.tile_r[tile];
+    const int64_t rend = p.offsets[e + 1];
+    const int64_t n0 = (int64_t)blockIdx.x * kDnCols;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int lr = lane & 15, lk = lane >> 4;
+    const int blk = FMT == FP4_FMT_MX ? 32 : 16;
+    const int64_t H = p.H, I = p.I;
+
+    const uint8_t* a_rows[4];
+    const uint8_t* a_srow[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t pos = r0 + wm * 64 + i * 16 + lr;
+        const bool ok = pos < rend;
+        if (ok && p.dbg.h_codes_in) {            // quantized h given per slot
+            const int64_t slot = p.perm[pos];
+            a_rows[i] = p.dbg.h_codes_in + slot * (I / 2);
+            a_srow[i] = p.dbg.h_scales_in + slot * (I / blk);
+        } else {
+            a_rows[i] = ok ? p.hc + pos * (I / 2) : nullptr;
+            a_srow[i] = ok ? p.hs + pos * (I / blk) : nullptr;
+        }
+    }
+    const uint8_t* wc = p.w2c + (int64_t)e * H * (I / 2);
+    const uint8_t* ws = p.w2s + (int64_t)e * H * (I / blk);
+    const uint8_t* b_rows[4];
+    const uint8_t* b_srow[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int64_t brow = n0 + wn * 64 + j * 16 + lr;
+        b_rows[j] = wc + brow * (I / 2);
+        b_srow[j] = ws + brow * (I / blk);
+    }
+    v4f acc[4][4];
+    zero_acc(acc);
+    if (FMT == FP4_FMT_MX)
+        mma_mx_64x64(acc, a_rows, a_srow, b_rows, b_srow, I, lane);
+    else
+        mma_nv_64x64(acc, a_rows, a_srow, b_rows, b_srow, I, lane);
+
+    const float yscale = FMT == FP4_FMT_NV ? __fmul_rn(p.act_ts[1], p.w2ts[e]) : 1.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t pos = r0 + wm * 64 + i * 16 + lk * 4 + r;
+            if (pos >= rend) continue;
+            const int64_t slot = p.perm[pos];
+            const int64_t t = slot / p.topk;
+            const float wgt = p.weights[slot];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t col = n0 + wn * 64 + j * 16 + lr;
+                float y = acc[i][j][r];
+                if (FMT == FP4_FMT_NV) y = __fmul_rn(y, yscale);
+                if (p.dbg.y) p.dbg.y[slot * H + col] = y;
+                unsafeAtomicAdd(&p.out32[t * H + col], __fmul_rn(wgt, y));
+            }
+        }
+}
+
+__global__ __launch_bounds__(kThreads) void zero_f32_kernel(float4* __restrict__ p, int64_t n4) {
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n4; i += stride) p[i] = make_float4(0, 0, 0, 0);
+}
+
+__global__ __launch_bounds__(kThreads) void cast_bf16_kernel(const float4* __restrict__ in, uint2* __restrict__ out,
+                                                             int64_t n4) {
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n4; i += stride) {
+        const float4 v = in[i];
+        out[i] = make_uint2(f32_to_bf16_rne(v.x) | (f32_to_bf16_rne(v.y) << 16),
+                            f32_to_bf16_rne(v.z) | (f32_to_bf16_rne(v.w) << 16));
+    }
+}
+
+inline unsigned stream_grid(int64_t n) {
+    int64_t b = (n + kThreads - 1) / kThreads;
+    if (b > 8192) b = 8192;
+    return (unsigned)(b < 1 ? 1 : b);
+}
+
+}  // namespace
+
+int64_t moe_max_tiles(int64_t tokens, int topk, int num_experts) {
+    return layout(FP4_FMT_MX, tokens, 128, topk, num_experts, 128).max_tiles;
+}
+
+size_t moe_workspace_bytes(int fmt, int64_t tokens, int64_t hidden, int topk, int num_experts, int64_t inter) {
+    return layout(fmt, tokens, hidden, topk, num_experts, inter).total;
+}
+
+hipError_t launch_moe(const MoeArgs& a, hipStream_t s) {
+    if (a.num_experts > kMaxExperts) return hipErrorInvalidValue;
+    const Layout L = layout(a.fmt, a.tokens, a.hidden, a.topk, a.num_experts, a.inter);
+    uint8_t* base = static_cast<uint8_t*>(a.ws);
+    uint8_t* xc = base + L.xc;
+    uint8_t* xs = base + L.xs;
+    int32_t* counts = reinterpret_cast<int32_t*>(base + L.counts);
+    int32_t* offsets = reinterpret_cast<int32_t*>(base + L.offsets);
+    int32_t* blockbase = reinterpret_cast<int32_t*>(base + L.blockbase);
+    int32_t* perm = reinterpret_cast<int32_t*>(base + L.perm);
+    int32_t* slot_pos = reinterpret_cast<int32_t*>(base + L.slot_pos);
+    int32_t* tile_e = reinterpret_cast<int32_t*>(base + L.tile_e);
+    int32_t* tile_r = reinterpret_cast<int32_t*>(base + L.tile_r);
+    int32_t* ntiles = reinterpret_cast<int32_t*>(base + L.ntiles);
+    uint8_t* hc = base + L.hc;
+    uint8_t* hs = base + L.hs;
+    float* out32 = reinterpret_cast<float*>(base + L.out32);
+    const int64_t T = a.tokens, H = a.hidden, I = a.inter, S = T * a.topk;
+    const int E = a.num_experts;
+
+    // 1. quantize X
+    hipError_t err = a.fmt == FP4_FMT_MX
+                         ? launch_quantize_mx(a.x, T, H, H, xc, xs, s)
+                         : launch_quantize_nv(a.x, T, H, H, xc, xs, const_cast<float*>(a.act_ts), true, nullptr, s);
+    if (err != hipSuccess) return err;
+    // 2. routing metadata
+    route_count_kernel<<<(unsigned)L.nblk, kRouteSlots, 0, s>>>(a.ids, S, E, blockbase);
+    route_scan_kernel<<<1, 1024, 0, s>>>(blockbase, L.nblk, E, counts, offsets, tile_e, tile_r, ntiles);
+    route_place_kernel<<<(unsigned)L.nblk, kRouteSlots, (size_t)E * (kRouteSlots / 32) * 4, s>>>(a.ids, S, E, blockbase, perm,
+                                                                                  slot_pos);
+    zero_f32_kernel<<<stream_grid(T * H / 4), kThreads, 0, s>>>(reinterpret_cast<float4*>(out32), T * H / 4);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+
+    GemmParams p{};
+    p.fmt = a.fmt;
+    p.H = H;
+    p.I = I;
+    p.topk = a.topk;
+    p.xc = xc;
+    p.xs = xs;
+    p.w13c = a.w13c;
+    p.w13s = a.w13s;
+    p.w2c = a.w2c;
+    p.w2s = a.w2s;
+    p.w13ts = a.w13ts;
+    p.w2ts = a.w2ts;
+    p.act_ts = a.act_ts;
+    p.perm = perm;
+    p.offsets = offsets;
+    p.tile_e = tile_e;
+    p.tile_r = tile_r;
+    p.ntiles = ntiles;
+    p.weights = a.weights;
+    p.hc = hc;
+    p.hs = hs;
+    p.out32 = out32;
+    p.dbg = a.dbg;
+    // 3. gate/up + SiLU*mul + quantize h; 4. down + weighted combine
+    const dim3 g_gu((unsigned)(I / kGuCols), (unsigned)L.max_tiles);
+    const dim3 g_dn((unsigned)(H / kDnCols), (unsigned)L.max_tiles);
+    if (a.fmt == FP4_FMT_MX) {
+        moe_gate_up_kernel<FP4_FMT_MX><<<g_gu, kThreads, 0, s>>>(p);
+        moe_down_kernel<FP4_FMT_MX><<<g_dn, kThreads, 0, s>>>(p);
+    } else {
+        moe_gate_up_kernel<FP4_FMT_NV><<<g_gu, kThreads, 0, s>>>(p);
+        moe_down_kernel<FP4_FMT_NV><<<g_dn, kThreads, 0, s>>>(p);
+    }
+    // 5. fp32 -> bf16
+    cast_bf16_kernel<<<stream_grid(T * H / 4), kThreads, 0, s>>>(reinterpret_cast<const float4*>(out32),
+                                                                   reinterpret_cast<uint2*>(a.out), T * H / 4);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    const int bx = a.fmt == FP4_FMT_MX ? 32 : 16;
+    if (a.dbg.x_codes &&
+        (err = hipMemcpyAsync(a.dbg.x_codes, xc, (size_t)(T * H / 2), hipMemcpyDeviceToDevice, s)))
+        return err;
+    if (a.dbg.x_scales &&
+        (err = hipMemcpyAsync(a.dbg.x_scales, xs, (size_t)(T * H / bx), hipMemcpyDeviceToDevice, s)))
+        return err;
+    if (a.dbg.counts && (err = hipMemcpyAsync(a.dbg.counts, counts, (size_t)E * 4, hipMemcpyDeviceToDevice, s)))
+        return err;
+    if (a.dbg.offsets &&
+        (err = hipMemcpyAsync(a.dbg.offsets, offsets, (size_t)(E + 1) * 4, hipMemcpyDeviceToDevice, s)))
+        return err;
+    if (a.dbg.perm && (err = hipMemcpyAsync(a.dbg.perm, perm, (size_t)S * 4, hipMemcpyDeviceToDevice, s)))
+        return err;
+    return hipSuccess;
+}
 
 }  // namespace fp4

@@ -5,73 +5,55 @@
 // contiguous input per instruction.  An MX block (32 elements) spans 4 adjacent
 // lanes and an NV group (16 elements) 2 lanes; the block/group amax is
 // combined across those lanes with DPP quad permutes (no LDS traffic).
-#include "fp4_internal.h"
+#include "quant_device.h"
 
 namespace fp4 {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kUnroll = 4;      // 16-byte loads in flight per lane
 
-// DPP quad permutations: lane i of each group of 4 reads lane perm[i].
-__device__ __forceinline__ uint32_t quad_swap1(uint32_t v) {   // (1,0,3,2)
-    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
-}
-__device__ __forceinline__ uint32_t quad_swap2(uint32_t v) {   // (2,3,0,1)
-    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);
-}
-
-// |x| of the two bf16 halves of a word, as 15-bit magnitudes (their integer order
-// is the order of the finite values).
-__device__ __forceinline__ uint32_t mag_max2(uint32_t w) {
-    return max(w & 0x7FFFu, (w >> 16) & 0x7FFFu);
-}
-
-inline unsigned grid_for(int64_t units) {
-    int64_t b = (units + kThreads - 1) / kThreads;
+inline unsigned grid_for(int64_t units, int per_thread = 1) {
+    int64_t b = (units + (int64_t)kThreads * per_thread - 1) / ((int64_t)kThreads * per_thread);
     if (b > (1 << 20)) b = 1 << 20;
     return (unsigned)(b < 1 ? 1 : b);
 }
 
+template <bool kContig>
+__device__ __forceinline__ int64_t x_offset(int64_t u, int64_t upr, int64_t ldx) {
+    if (kContig) return u * 8;
+    const int64_t r = u / upr;
+    return r * ldx + (u - r * upr) * 8;
+}
+
 // ------------------------------------------------------------------ MX quantize
-// Per 32-block: amax from the bf16 magnitude bits; the biased exponent field e
-// of amax gives floor(log2 amax) = e - 127 for normal amax, so the block
-// exponent E = e - 129 and the scale byte E + 127 = e - 2, clamped at 0 (which
-// also covers zero and subnormal amax, whose floor(log2) is below -126).
-// Elements are scaled by 2^-E (exact: a power of two applied to a bf16 value,
-// result below 8) and rounded to E2M1 with nearest-even.
+// Lane u owns elements 8u..8u+7 of the row-major [rows, k] input (codes word u,
+// scale byte u/4).  Each lane issues kUnroll loads before converting.
 template <bool kContig>
 __global__ __launch_bounds__(kThreads) void mx_quantize_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t k, int64_t ldx,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
     const int64_t upr = k >> 3;
     const int64_t total = rows * upr;
-    const int64_t stride = (int64_t)gridDim.x * kThreads;
-    for (int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x; u < total; u += stride) {
-        int64_t xo;
-        if (kContig) {
-            xo = u * 8;
-        } else {
-            const int64_t r = u / upr;
-            xo = r * ldx + (u - r * upr) * 8;
-        }
-        const uint4 v = *reinterpret_cast<const uint4*>(x + xo);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-        uint32_t am = max(max(mag_max2(w[0]), mag_max2(w[1])), max(mag_max2(w[2]), mag_max2(w[3])));
-        am = max(am, quad_swap1(am));
-        am = max(am, quad_swap2(am));
-        const uint32_t e = am >> 7;
-        const uint32_t sbyte = e > 2u ? e - 2u : 0u;
-        const float inv = __uint_as_float((254u - sbyte) << 23);      // 2^-E, E = sbyte - 127
-        uint32_t packed = 0;
+    const int64_t step = (int64_t)gridDim.x * kThreads * kUnroll;
+    for (int64_t base = (int64_t)blockIdx.x * kThreads * kUnroll + threadIdx.x; base < total; base += step) {
+        uint4 v[kUnroll];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t b = (i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xFFFFu);
-            const float a = __uint_as_float((b & 0x7FFFu) << 16);
-            const uint32_t idx = e2m1_index_rne(__fmul_rn(a, inv));
-            packed |= (((b >> 12) & 8u) | idx) << (4 * i);
+        for (int j = 0; j < kUnroll; ++j) {
+            const int64_t u = base + (int64_t)j * kThreads;
+            if (u < total) v[j] = *reinterpret_cast<const uint4*>(x + x_offset<kContig>(u, upr, ldx));
         }
-        reinterpret_cast<uint32_t*>(codes)[u] = packed;
-        if ((threadIdx.x & 3) == 0) scales[u >> 2] = (uint8_t)sbyte;
+#pragma unroll
+        for (int j = 0; j < kUnroll; ++j) {
+            const int64_t u = base + (int64_t)j * kThreads;
+            if (u < total) {
+                const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+                uint32_t sbyte;
+                const uint32_t packed = mx_quant8(w, sbyte);
+                reinterpret_cast<uint32_t*>(codes)[u] = packed;
+                if ((threadIdx.x & 3) == 0) scales[u >> 2] = (uint8_t)sbyte;
+            }
+        }
     }
 }
 
@@ -86,14 +68,7 @@ __global__ __launch_bounds__(kThreads) void nv_amax_kernel(
     const int64_t stride = (int64_t)gridDim.x * kThreads;
     uint32_t am = 0;
     for (int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x; u < total; u += stride) {
-        int64_t xo;
-        if (kContig) {
-            xo = u * 8;
-        } else {
-            const int64_t r = u / upr;
-            xo = r * ldx + (u - r * upr) * 8;
-        }
-        const uint4 v = *reinterpret_cast<const uint4*>(x + xo);
+        const uint4 v = *reinterpret_cast<const uint4*>(x + x_offset<kContig>(u, upr, ldx));
         am = max(am, max(max(mag_max2(v.x), mag_max2(v.y)), max(mag_max2(v.z), mag_max2(v.w))));
     }
     for (int off = 32; off > 0; off >>= 1) am = max(am, (uint32_t)__shfl_xor((int)am, off));
@@ -115,75 +90,34 @@ __global__ void nv_tensor_scale_kernel(const uint32_t* amax, float* ts) {
     *ts = (float)((double)a / 2688.0);
 }
 
-// One lane owns 8 elements; a 16-group spans lanes (2i, 2i+1).
-//   s_g = E4M3(amax_g / (6 s_t))  computed in fp64 (exact quotient rounding).
-//   code = E2M1(|x| / d), d = s_g s_t (exact in fp64, <= 28 bits).
-// Codes use a bracket: with r = 1/d, v_lo = |x| * r(1 - 2^-22) and
-// v_hi = |x| * r(1 + 2^-22) in fp32 lie strictly below and above the exact
-// quotient, so equal E2M1 roundings of both are the exact rounding.  Otherwise
-// the quotient is within 2^-21 of the midpoint between the two candidates and
-// |x| is compared with midpoint * d exactly in fp64.
+// Lane u owns 8 elements; a 16-group spans lanes (2i, 2i+1).  The tensor scale
+// is read from device memory (written by the amax pass or supplied).
 template <bool kContig>
 __global__ __launch_bounds__(kThreads) void nv_quantize_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t k, int64_t ldx,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, const float* __restrict__ ts) {
     const int64_t upr = k >> 3;
     const int64_t total = rows * upr;
-    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    const int64_t step = (int64_t)gridDim.x * kThreads * kUnroll;
     const double st = (double)*ts;
-    for (int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x; u < total; u += stride) {
-        int64_t xo;
-        if (kContig) {
-            xo = u * 8;
-        } else {
-            const int64_t r = u / upr;
-            xo = r * ldx + (u - r * upr) * 8;
+    for (int64_t base = (int64_t)blockIdx.x * kThreads * kUnroll + threadIdx.x; base < total; base += step) {
+        uint4 v[kUnroll];
+#pragma unroll
+        for (int j = 0; j < kUnroll; ++j) {
+            const int64_t u = base + (int64_t)j * kThreads;
+            if (u < total) v[j] = *reinterpret_cast<const uint4*>(x + x_offset<kContig>(u, upr, ldx));
         }
-        const uint4 v = *reinterpret_cast<const uint4*>(x + xo);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-        uint32_t am = max(max(mag_max2(w[0]), mag_max2(w[1])), max(mag_max2(w[2]), mag_max2(w[3])));
-        am = max(am, quad_swap1(am));
-        const double amax = (double)__uint_as_float(am << 16);
-        uint32_t sg = (st > 0.0) ? e4m3_rne_sat(amax / (6.0 * st)) : 0u;
-        uint32_t packed = 0;
-        if (sg != 0u) {
-            const double d = (double)e4m3_value(sg) * st;
-            const double r = 1.0 / d;
-            const bool fast = r < 1.0e37;
-            const float r_lo = (float)(r * (1.0 - 0x1p-22));
-            const float r_hi = (float)(r * (1.0 + 0x1p-22));
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const uint32_t b = (i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xFFFFu);
-                const float a = __uint_as_float((b & 0x7FFFu) << 16);
-                uint32_t idx;
-                const uint32_t i_lo = fast ? e2m1_index_rne(__fmul_rn(a, r_lo)) : 0u;
-                const uint32_t i_hi = fast ? e2m1_index_rne(__fmul_rn(a, r_hi)) : 7u;
-                if (i_lo == i_hi) {
-                    idx = i_lo;
-                } else {
-                    // exact decision among all eight magnitudes (rare)
-                    const double ad = (double)a;
-                    idx = 0;
-#pragma unroll
-                    for (uint32_t j = 0; j < 7; ++j) {
-                        const double t = 0.5 * ((double)e2m1_mag(j) + (double)e2m1_mag(j + 1)) * d;
-                        // tie at midpoint j|j+1 goes to the even index
-                        const bool up = (j & 1u) ? (ad >= t) : (ad > t);
-                        idx += up ? 1u : 0u;
-                    }
-                }
-                packed |= (((b >> 12) & 8u) | idx) << (4 * i);
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const uint32_t b = (i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xFFFFu);
-                packed |= ((b >> 12) & 8u) << (4 * i);
+        for (int j = 0; j < kUnroll; ++j) {
+            const int64_t u = base + (int64_t)j * kThreads;
+            if (u < total) {
+                const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+                uint32_t sg;
+                const uint32_t packed = nv_quant8(w, st, sg);
+                reinterpret_cast<uint32_t*>(codes)[u] = packed;
+                if ((threadIdx.x & 1) == 0) scales[u >> 1] = (uint8_t)sg;
             }
         }
-        reinterpret_cast<uint32_t*>(codes)[u] = packed;
-        if ((threadIdx.x & 1) == 0) scales[u >> 1] = (uint8_t)sg;
     }
 }
 
@@ -293,10 +227,11 @@ __global__ __launch_bounds__(kThreads) void remap_kernel(const uint8_t* __restri
 hipError_t launch_quantize_mx(const uint16_t* x, int64_t rows, int64_t k, int64_t ldx,
                               uint8_t* codes, uint8_t* scales, hipStream_t s) {
     const int64_t units = rows * (k / 8);
+    const unsigned g = grid_for(units, kUnroll);
     if (ldx == k)
-        mx_quantize_kernel<true><<<grid_for(units), kThreads, 0, s>>>(x, rows, k, ldx, codes, scales);
+        mx_quantize_kernel<true><<<g, kThreads, 0, s>>>(x, rows, k, ldx, codes, scales);
     else
-        mx_quantize_kernel<false><<<grid_for(units), kThreads, 0, s>>>(x, rows, k, ldx, codes, scales);
+        mx_quantize_kernel<false><<<g, kThreads, 0, s>>>(x, rows, k, ldx, codes, scales);
     return hipGetLastError();
 }
 
@@ -315,10 +250,11 @@ hipError_t launch_quantize_nv(const uint16_t* x, int64_t rows, int64_t k, int64_
             nv_amax_kernel<false><<<g, kThreads, 0, s>>>(x, rows, k, ldx, amax_ws);
         nv_tensor_scale_kernel<<<1, 1, 0, s>>>(amax_ws, ts);
     }
+    const unsigned gq = grid_for(units, kUnroll);
     if (contig)
-        nv_quantize_kernel<true><<<grid_for(units), kThreads, 0, s>>>(x, rows, k, ldx, codes, scales, ts);
+        nv_quantize_kernel<true><<<gq, kThreads, 0, s>>>(x, rows, k, ldx, codes, scales, ts);
     else
-        nv_quantize_kernel<false><<<grid_for(units), kThreads, 0, s>>>(x, rows, k, ldx, codes, scales, ts);
+        nv_quantize_kernel<false><<<gq, kThreads, 0, s>>>(x, rows, k, ldx, codes, scales, ts);
     return hipGetLastError();
 }
 

@@ -151,6 +151,7 @@ int fp4_gemm(fp4_format fmt,
 /*
  * Optional intermediate outputs of fp4_moe_grouped_gemm, for staged testing.
  * Every member may be NULL.  Slot s = t * topk + j (token t, choice j).
+ *   x_codes   uint8 [tokens, hidden/2], x_scales [tokens, hidden/32|16]  Q(x)
  *   counts    int32 [num_experts]    slots routed to each expert
  *   offsets   int32 [num_experts+1]  exclusive prefix sum of counts
  *   perm      int32 [tokens*topk]    slots grouped by expert, stable
@@ -158,8 +159,18 @@ int fp4_gemm(fp4_format fmt,
  *   h_bf16    bf16  [tokens*topk, inter]    SiLU(g)*u rounded to bf16
  *   h_codes   uint8 [tokens*topk, inter/2], h_scales [tokens*topk, inter/32|16]
  *   y         fp32  [tokens*topk, hidden]   down-projection output per slot
+ * Stage inputs, for testing each fused stage on given data (NULL = compute):
+ *   gate_up_in   fp32 [tokens*topk, 2*inter]: g (first inter) then u per slot,
+ *                already including NV tensor scales; replaces the gate/up
+ *                product, and SiLU*mul, the bf16 rounding and the quantization
+ *                of h run on these values.
+ *   h_codes_in, h_scales_in  [tokens*topk, inter/2], [tokens*topk, inter/32|16]:
+ *                quantized h per slot (NV: with s_t = act_tensor_scales[1]);
+ *                replaces the computed Q(h) as the input of the down stage.
  */
 typedef struct fp4_moe_debug {
+    uint8_t* x_codes;
+    uint8_t* x_scales;
     int32_t* counts;
     int32_t* offsets;
     int32_t* perm;
@@ -168,6 +179,9 @@ typedef struct fp4_moe_debug {
     uint8_t* h_codes;
     uint8_t* h_scales;
     float* y;
+    const float* gate_up_in;
+    const uint8_t* h_codes_in;
+    const uint8_t* h_scales_in;
 } fp4_moe_debug;
 
 /*
@@ -188,10 +202,12 @@ typedef struct fp4_moe_debug {
  * NV: w13_tensor_scales, w2_tensor_scales fp32 [E] and act_tensor_scales fp32 [2]
  * (device); MX: all three NULL.  out_bf16 [tokens, hidden].
  * workspace: at least fp4_moe_workspace_bytes(...) bytes of device memory.
- * Errors: hidden or inter not a multiple of 128 -> FP4_ERR_SHAPE; topk < 1 or
- * topk > 16 -> FP4_ERR_INVALID; workspace too small -> FP4_ERR_WORKSPACE.
- * Expert ids outside [0, num_experts) are not checked on the device and are
- * undefined behaviour.
+ * Errors: hidden or inter not a multiple of 128, or tokens*topk above about
+ * 8.2 million -> FP4_ERR_SHAPE; topk outside [1, 16] or num_experts outside
+ * [1, 1024] -> FP4_ERR_INVALID; workspace too small -> FP4_ERR_WORKSPACE.
+ * A slot whose expert id lies outside [0, num_experts) is routed nowhere and
+ * contributes nothing to out.  The fp32 combine uses atomic adds, so out may
+ * differ between runs in the last bit of the fp32 sum before the bf16 rounding.
  */
 int fp4_moe_grouped_gemm(fp4_format fmt, const void* x_bf16, int64_t tokens, int64_t hidden,
                          const int32_t* topk_ids, const float* topk_weights, int topk,

@@ -61,24 +61,26 @@ def e2m1_encode(negative: bool, magnitude: Fraction) -> int:
     return (8 if negative else 0) | best[1]
 
 
+E2M1_MIDPOINTS_F64 = (E2M1_MAG_F64[1:] + E2M1_MAG_F64[:-1]) / 2     # 0.25, 0.75, ..., 5 (exact)
+
+
 def e2m1_index_f64(a: np.ndarray) -> np.ndarray:
     """Vectorised E2M1 index of non-negative fp64 magnitudes ``a``.
 
-    Nearest of the 8 table magnitudes, ties to the even index; a >= 6 is index 7
-    (the top entry is nearest to everything above it; stated explicitly because
-    fp64 distances to the table stop resolving for huge a).  Exact whenever
-    ``a`` is the exact quotient or lies further than fp64 rounding from every
-    midpoint (the callers' arguments): near a midpoint m (0.25 <= m <= 5) the two
-    candidate distances |a - m_i| are exact by Sterbenz's lemma.
+    Nearest table magnitude with ties to the even index, written as: the index
+    is the number of midpoints m_j (between entries j and j+1) that a lies above,
+    where a value exactly on m_j counts as above only when j + 1 is even.
+    Everything above the last midpoint (5) is index 7, so a >= 6 saturates.
+    The midpoints are exact in fp64, so the comparisons are exact for the fp64
+    value given; callers pass either the exact quotient or an fp64 value whose
+    rounding cannot cross a midpoint (their docstrings give the argument).
     """
     a = np.asarray(a, dtype=np.float64)
-    d = np.abs(a[..., None] - E2M1_MAG_F64)            # [..., 8]
-    dmin = d.min(axis=-1, keepdims=True)
-    is_min = d == dmin
-    # among the nearest, prefer an even index: even ones get key 0, odd key 1
-    key = np.where(is_min, (np.arange(8) % 2), 9)
-    idx = np.argmin(key * 16 + np.arange(8), axis=-1)
-    return np.where(a >= 6.0, 7, idx).astype(np.uint8)
+    idx = np.zeros(a.shape, dtype=np.uint8)
+    for j, m in enumerate(E2M1_MIDPOINTS_F64):
+        up = (a > m) | ((a == m) & ((j + 1) % 2 == 0))
+        idx += up.astype(np.uint8)
+    return idx
 
 
 # ---------------------------------------------------------------- generic binary float rounding
