@@ -152,30 +152,29 @@ def main():
         keep = set(args.only.split(","))
         stages = [s for s in stages if s.name in keep]
 
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in stages]
-
-    def step(record):
-        for s, (e0, e1) in zip(stages, evs):
-            if record:
-                e0.record(stream)
-            s.launch()
-            if record:
-                e1.record(stream)
-        st["i"] += 1
-
     for _ in range(args.warmup):
-        step(False)
+        for s in stages:
+            s.launch()
+        st["i"] += 1
     torch.cuda.synchronize()
 
-    per_step_ms = []
+    # one event pair per stage per step; the queue stays full between steps, so
+    # no event interval includes host launch latency
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in stages]
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(True)
-        torch.cuda.synchronize()
-        for s, (e0, e1) in zip(stages, evs):
-            s.times.append(e0.elapsed_time(e1))
+    for k in range(args.steps):
+        for s, (e0, e1) in zip(stages, evs[k]):
+            e0.record(stream)
+            s.launch()
+            e1.record(stream)
+        st["i"] += 1
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    for k in range(args.steps):
+        for s, (e0, e1) in zip(stages, evs[k]):
+            s.times.append(e0.elapsed_time(e1))
     ms_per_step = wall * 1e3 / args.steps
 
     rooflines = {}

@@ -12,6 +12,7 @@
 // each lane expands its 8 codes to bf16 values code * s_g (exact: at most 6
 // significant bits) and uses v_mfma_f32_16x16x32_bf16; the two fp32 tensor
 // scales multiply the fp32 accumulator at the end.
+#include "gemm_mx_tile.h"
 #include "mma_core.h"
 
 namespace fp4 {
@@ -73,13 +74,90 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     store_tile(acc, c, c_f32, ldc, m, n, m0, n0, lane, scale);
 }
 
+// Tile order: consecutive workgroups go to different XCDs (round robin), so
+// workgroup b is given tile (b % 8) * (tiles / 8) + b / 8 when the tile count
+// is a multiple of 8: each XCD then owns a contiguous run of tiles, and tiles
+// are numbered in groups of 4 tile-rows (column-major inside a group), so an
+// XCD's run is a compact block of tiles that shares A and B slabs in its L2.
+__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
+    const int total = tiles_m * tiles_n;
+    int t = blockIdx.x;
+    if ((total & 7) == 0) t = (t & 7) * (total >> 3) + (t >> 3);
+    constexpr int G = 4;
+    const int group = t / (G * tiles_n);
+    const int rows_in_group = min(G, tiles_m - group * G);
+    const int r = t - group * G * tiles_n;
+    tm = group * G + r % rows_in_group;
+    tn = r / rows_in_group;
+}
+
+// MX GEMM on 256 x 256 tiles (LDS-staged, see gemm_mx_tile.h).
+__global__ __launch_bounds__(kTileThreads, 1) void gemm_mx_256_kernel(
+    const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as, const uint8_t* __restrict__ bc,
+    const uint8_t* __restrict__ bs, int64_t m, int64_t n, int64_t k, void* __restrict__ c, int c_f32,
+    int64_t ldc, int tiles_m, int tiles_n) {
+    __shared__ __align__(16) MxSmem sm;
+    int tm, tn;
+    tile_coords(tiles_m, tiles_n, tm, tn);
+    const int64_t m0 = (int64_t)tm * kTileM, n0 = (int64_t)tn * kTileN;
+    const int64_t kbytes = k / 2, kblocks = k / 32;
+    const int t = threadIdx.x;
+    MxSlabSrc A, B;
+    mx_slab_src(A, ac, as, m0, m, kbytes, kblocks);
+    mx_slab_src(B, bc, bs, n0, n, kbytes, kblocks);
+    v4f acc[kWaveFragsN][8];
+#pragma unroll
+    for (int j = 0; j < kWaveFragsN; ++j)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[j][i] = v4f{0.f, 0.f, 0.f, 0.f};
+    mx_tile_mainloop(sm, A, B, kblocks, acc);
+
+    const int lane = t & 63, wave = t >> 6, wm = wave >> 2, wn = wave & 3;
+    const int lr = lane & 15, lk = lane >> 4;
+    const bool vec = (ldc & 3) == 0;
+#pragma unroll
+    for (int j = 0; j < kWaveFragsN; ++j)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int64_t row = m0 + wm * 128 + i * 16 + lr;
+            const int64_t col = n0 + wn * kWaveN + j * 16 + lk * 4;
+            if (row >= m) continue;
+            const v4f v = acc[j][i];
+            if (c_f32) {
+                float* dst = static_cast<float*>(c) + row * ldc + col;
+                if (vec && col + 3 < n) {
+                    *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+                } else {
+                    for (int r = 0; r < 4; ++r)
+                        if (col + r < n) dst[r] = v[r];
+                }
+            } else {
+                uint16_t* dst = static_cast<uint16_t*>(c) + row * ldc + col;
+                if (vec && col + 3 < n) {
+                    *reinterpret_cast<uint2*>(dst) = make_uint2(f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16),
+                                                                f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16));
+                } else {
+                    for (int r = 0; r < 4; ++r)
+                        if (col + r < n) dst[r] = (uint16_t)f32_to_bf16_rne(v[r]);
+                }
+            }
+        }
+}
+
 }  // namespace
 
 hipError_t launch_gemm_mx(const uint8_t* ac, const uint8_t* as, const uint8_t* bc, const uint8_t* bs,
                           int64_t m, int64_t n, int64_t k, void* c, int c_f32, int64_t ldc,
                           hipStream_t s) {
-    dim3 grid((unsigned)((n + kBN - 1) / kBN), (unsigned)((m + kBM - 1) / kBM));
-    gemm_kernel<FP4_FMT_MX><<<grid, kThreads, 0, s>>>(ac, as, nullptr, bc, bs, nullptr, m, n, k, c, c_f32, ldc);
+    const int64_t tiles_m = (m + kTileM - 1) / kTileM, tiles_n = (n + kTileN - 1) / kTileN;
+    const bool small_ops = m * (k / 2) < (1ll << 31) && n * (k / 2) < (1ll << 31);
+    if (k % 512 == 0 && k > 0 && small_ops && tiles_m * tiles_n >= 64 && tiles_m * tiles_n < (1ll << 31)) {
+        gemm_mx_256_kernel<<<(unsigned)(tiles_m * tiles_n), kTileThreads, 0, s>>>(ac, as, bc, bs, m, n, k, c, c_f32, ldc,
+                                                                         (int)tiles_m, (int)tiles_n);
+    } else {
+        dim3 grid((unsigned)((n + kBN - 1) / kBN), (unsigned)((m + kBM - 1) / kBM));
+        gemm_kernel<FP4_FMT_MX><<<grid, kThreads, 0, s>>>(ac, as, nullptr, bc, bs, nullptr, m, n, k, c, c_f32, ldc);
+    }
     return hipGetLastError();
 }
 

@@ -1,0 +1,208 @@
+// LDS-staged MXFP4 block tile for gfx950: 256 x 256 outputs per 256-thread
+// workgroup, K advancing 256 values (8 MX blocks, one 128-byte line per row)
+// per step.
+//
+// Roles: the workgroup's A tile (rows of C) and B tile (columns of C) are both
+// row-major [256][128 B] slabs of packed codes per step; the 8 waves form a
+// 2 x 4 grid and each owns 128 x 64 outputs as 8 x 4 MFMA tiles of 16 x 16.
+// Two waves share a SIMD: while one waits on LDS reads into fragment registers
+// that its own in-flight MFMAs still read, the other keeps the matrix core
+// busy.  The MFMA is issued with the B fragment as its first operand, so a
+// lane's four accumulator values are four consecutive columns of one output
+// row (8-byte bf16 stores).
+//
+// Measured limits on gfx950 shape the loop: L2 -> LDS traffic is bound by the
+// number of requests, and LDS reads by the number of instructions (a 1-byte
+// read costs about as much as a 16-byte one).  So:
+//   - codes go straight from global memory into LDS (global_load_lds_dwordx4:
+//     a wave writes 1 KiB, lane l at byte 16 l), two stages;
+//   - UE8M0 scales travel 16 bytes per row (two steps' worth) per request into
+//     a separate two-deep buffer, and a lane reads one step's 8 scale bytes of
+//     a fragment row with one ds_read_b64, picking its byte with a shift;
+//   - the second half-step's fragment reads are interleaved into the first
+//     half-step's MFMA stream.
+// Slab row r's 16-byte chunk c sits at chunk c ^ (r & 7); a load lane l writes
+// chunk l & 7 of row l >> 3 and so fetches global chunk (l & 7) ^ (l >> 3).
+// The 8 lanes that a ds_read_b128 serves together read 8 different rows of one
+// logical chunk, which land on 8 different bank groups (no conflicts measured).
+#pragma once
+
+#include "mma_core.h"
+
+namespace fp4 {
+
+constexpr int kTileM = 256, kTileN = 256, kRowBytes = 128, kStepBlocks = 8;
+constexpr int kTileThreads = 512;   // 8 waves: 2 along M x 4 along N
+constexpr int kWaveN = 64;          // output columns per wave
+constexpr int kWaveFragsN = kWaveN / 16;
+constexpr int kScaleRow = 16;      // scale bytes per row held in LDS: two steps
+
+struct MxCodes {
+    uint8_t a[kTileM * kRowBytes];
+    uint8_t b[kTileN * kRowBytes];
+};
+struct MxScales {
+    uint8_t a[kTileM * kScaleRow];
+    uint8_t b[kTileN * kScaleRow];
+};
+struct MxSmem {
+    MxCodes codes[2];
+    MxScales scales[2];
+};
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Global sources of this wave's share of one operand.  Load q (q = 0..3) of
+// this lane fills slab row (wave * 4 + q) * 8 + lane / 8 at the lane's swizzled
+// chunk; waves 0-3 fill the A scale rows (wave & 3) * 64 + lane, waves 4-7 the
+// B ones.  Rows past the end of the operand are clamped to its last row (their
+// products only reach outputs that are never stored).  K must be a multiple of
+// 512 and each operand below 2 GiB.
+struct MxSlabSrc {
+    const uint8_t* codes;
+    const uint8_t* scales;
+    int row;               // first slab row of this lane's code loads (absolute)
+    int srow;              // slab row of this lane's scale load (absolute)
+    int last;              // last valid row of the operand
+    int kbytes, kblocks;
+    int chunk16;           // byte offset of the lane's swizzled chunk
+};
+
+__device__ __forceinline__ void mx_slab_src(MxSlabSrc& s, const uint8_t* codes, const uint8_t* scales, int64_t r0,
+                                            int64_t rows, int64_t kbytes, int64_t kblocks) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    s.codes = codes;
+    s.scales = scales;
+    s.row = (int)r0 + wave * 32 + (lane >> 3);
+    s.srow = min((int)r0 + (wave & 3) * 64 + lane, (int)rows - 1);
+    s.last = (int)rows - 1;
+    s.kbytes = (int)kbytes;
+    s.kblocks = (int)kblocks;
+    s.chunk16 = ((lane & 7) ^ (lane >> 3)) * 16;
+}
+
+// Global -> LDS copies issued from inline asm: the LDS base goes to M0 in the
+// same block (with the one wait state the M0 write needs).  The asm has no
+// register results; completion is awaited explicitly (wait_vm_zero) before the
+// barrier that precedes any read of the buffer.  Issued this way, the compiler
+// does not hold the next stage's copies in flight against every LDS read of
+// the current stage.
+__device__ __forceinline__ void dma16(const uint8_t* g, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(lds_ptr_t)const_cast<void*>(p);
+}
+
+__device__ __forceinline__ void wait_vm_zero() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ void mx_issue_codes(MxCodes& st, const MxSlabSrc& A, const MxSlabSrc& B, int ks) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint8_t* ac = A.codes + (int64_t)ks * kRowBytes + A.chunk16;
+    const uint8_t* bc = B.codes + (int64_t)ks * kRowBytes + B.chunk16;
+    const uint32_t la = lds_addr(st.a) + wave * 4 * 1024, lb = lds_addr(st.b) + wave * 4 * 1024;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        dma16(ac + (uint32_t)(min(A.row + q * 8, A.last) * A.kbytes), la + q * 1024);
+        dma16(bc + (uint32_t)(min(B.row + q * 8, B.last) * B.kbytes), lb + q * 1024);
+    }
+}
+
+// Scale bytes of steps 2p and 2p + 1 (blocks 16p .. 16p + 15) of every row:
+// waves 0-3 fetch the A rows, waves 4-7 the B rows.
+__device__ __forceinline__ void mx_issue_scales(MxScales& sc, const MxSlabSrc& A, const MxSlabSrc& B, int p) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (wave < 4)
+        dma16(A.scales + (int64_t)p * 16 + (uint32_t)(A.srow * A.kblocks), lds_addr(sc.a) + wave * 1024);
+    else
+        dma16(B.scales + (int64_t)p * 16 + (uint32_t)(B.srow * B.kblocks), lds_addr(sc.b) + (wave - 4) * 1024);
+}
+
+// Per-lane LDS bases of this wave's fragments (row wm*128 + i*16 + lr has
+// (row & 7) == (lr & 7), so fragment i is the base plus i * 16 rows).
+struct MxLdsBase {
+    int a[2], b[2];        // code byte offset within a stage, per half-step s
+    int sa, sb;            // scale byte offset within a scale buffer
+};
+
+__device__ __forceinline__ MxLdsBase mx_lds_base(int wm, int wn, int lane) {
+    const int lr = lane & 15, lk = lane >> 4;
+    MxLdsBase b;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        const int coff = ((s * 4 + lk) ^ (lr & 7)) * 16;
+        b.a[s] = (wm * 128 + lr) * kRowBytes + coff;
+        b.b[s] = (wn * kWaveN + lr) * kRowBytes + coff;
+    }
+    b.sa = (wm * 128 + lr) * kScaleRow;
+    b.sb = (wn * kWaveN + lr) * kScaleRow;
+    return b;
+}
+
+__device__ __forceinline__ v8i frag_at(const uint8_t* p) {
+    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    return v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+}
+
+// Scale operand for half-step s: byte s*4 + lk of the row's step bytes; the
+// MFMA reads bits 7:0 of the operand.
+__device__ __forceinline__ int scale_at(uint2 w, int s, int lk) {
+    return (int)((s ? w.y : w.x) >> (8 * lk));
+}
+
+// Full K loop of one 256 x 256 tile; acc zeroed by the caller.  The loop runs
+// over half-steps (128 K values), so each accumulator has one MFMA per
+// iteration.  At the start of step ks the copies of step ks have landed (wait +
+// barrier) and those of step ks + 1 (and, when ks + 1 is even, the scales of
+// steps ks + 1 and ks + 2) are issued into the buffers step ks - 1 used.
+__device__ __forceinline__ void mx_tile_mainloop(MxSmem& sm, const MxSlabSrc& A, const MxSlabSrc& B, int64_t kblocks,
+                                                 v4f acc[kWaveFragsN][8]) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave >> 2, wn = wave & 3, lk = lane >> 4;
+    const int nsteps = (int)(kblocks / kStepBlocks);
+    const MxLdsBase lb = mx_lds_base(wm, wn, lane);
+    mx_issue_codes(sm.codes[0], A, B, 0);
+    mx_issue_scales(sm.scales[0], A, B, 0);
+    uint2 wsa[8], wsb[kWaveFragsN];
+    for (int hs = 0; hs < 2 * nsteps; ++hs) {
+        const int ks = hs >> 1, s = hs & 1;
+        if (s == 0) {
+            wait_vm_zero();
+            __syncthreads();
+            if (ks + 1 < nsteps) {
+                mx_issue_codes(sm.codes[(ks + 1) & 1], A, B, ks + 1);
+                if (((ks + 1) & 1) == 0) mx_issue_scales(sm.scales[((ks + 1) >> 1) & 1], A, B, (ks + 1) >> 1);
+            }
+            const uint8_t* sc_a = sm.scales[(ks >> 1) & 1].a + (ks & 1) * 8;
+            const uint8_t* sc_b = sm.scales[(ks >> 1) & 1].b + (ks & 1) * 8;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) wsa[i] = *reinterpret_cast<const uint2*>(sc_a + lb.sa + i * 16 * kScaleRow);
+#pragma unroll
+            for (int j = 0; j < kWaveFragsN; ++j)
+                wsb[j] = *reinterpret_cast<const uint2*>(sc_b + lb.sb + j * 16 * kScaleRow);
+        }
+        const uint8_t* st_a = sm.codes[ks & 1].a + (s ? lb.a[1] : lb.a[0]);
+        const uint8_t* st_b = sm.codes[ks & 1].b + (s ? lb.b[1] : lb.b[0]);
+        v8i a[8], b[kWaveFragsN];
+        int sa[8], sb[kWaveFragsN];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            a[i] = frag_at(st_a + i * 16 * kRowBytes);
+            sa[i] = scale_at(wsa[i], s, lk);
+        }
+#pragma unroll
+        for (int j = 0; j < kWaveFragsN; ++j) {
+            b[j] = frag_at(st_b + j * 16 * kRowBytes);
+            sb[j] = scale_at(wsb[j], s, lk);
+        }
+#pragma unroll
+        for (int j = 0; j < kWaveFragsN; ++j)
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                acc[j][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b[j], a[i], acc[j][i], 4, 4, 0, sb[j], 0,
+                                                                               sa[i]);
+    }
+}
+
+}  // namespace fp4
