@@ -110,7 +110,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void gemm_mx_256_kernel(
     for (int j = 0; j < kWaveFragsN; ++j)
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[j][i] = v4f{0.f, 0.f, 0.f, 0.f};
-    mx_tile_mainloop(sm, A, B, kblocks, acc);
+    mx_tile_mainloop<8>(sm, A, B, kblocks, acc);
 
     const int lane = t & 63, wave = t >> 6, wm = wave >> 2, wn = wave & 3;
     const int lr = lane & 15, lk = lane >> 4;

@@ -52,33 +52,43 @@ struct MxSmem {
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// Global sources of this wave's share of one operand.  Load q (q = 0..3) of
-// this lane fills slab row (wave * 4 + q) * 8 + lane / 8 at the lane's swizzled
-// chunk; waves 0-3 fill the A scale rows (wave & 3) * 64 + lane, waves 4-7 the
-// B ones.  Rows past the end of the operand are clamped to its last row (their
-// products only reach outputs that are never stored).  K must be a multiple of
-// 512 and each operand below 2 GiB.
+// Global sources of one operand's slab, as per-lane byte offsets from a base
+// that is the same for the whole workgroup (so the copies use the scalar-base
+// addressing form).  Code load q (q = 0..3) of a lane fills slab row
+// mx_code_row(q) at the lane's swizzled chunk; off[q] is the byte offset of that
+// row's K-step-0 line plus the chunk.  Waves 0-3 fill the A scale rows, waves
+// 4-7 the B ones, one row per lane (mx_scale_row); soff is the byte offset of
+// that row's scales.  The rows may be any rows of the operand (the grouped MoE
+// GEMMs gather them), so a slab row past the end of the problem is pointed at
+// some valid row; its products only reach outputs that are never stored.
+// Offsets are 32-bit: each operand (from its base) must stay below 4 GiB.
 struct MxSlabSrc {
     const uint8_t* codes;
     const uint8_t* scales;
-    int row;               // first slab row of this lane's code loads (absolute)
-    int srow;              // slab row of this lane's scale load (absolute)
-    int last;              // last valid row of the operand
-    int kbytes, kblocks;
-    int chunk16;           // byte offset of the lane's swizzled chunk
+    uint32_t off[4];
+    uint32_t soff;
 };
 
+__device__ __forceinline__ int mx_code_row(int q) {
+    return (int)(threadIdx.x >> 6) * 32 + q * 8 + (int)((threadIdx.x & 63) >> 3);
+}
+__device__ __forceinline__ int mx_scale_row() { return (int)((threadIdx.x >> 6) & 3) * 64 + (int)(threadIdx.x & 63); }
+__device__ __forceinline__ uint32_t mx_chunk16() {
+    const uint32_t lane = threadIdx.x & 63;
+    return ((lane & 7) ^ (lane >> 3)) * 16;
+}
+
+// Dense operand: slab rows r0 .. r0 + 255 of a [rows, kbytes] code matrix,
+// clamped to its last row.
 __device__ __forceinline__ void mx_slab_src(MxSlabSrc& s, const uint8_t* codes, const uint8_t* scales, int64_t r0,
                                             int64_t rows, int64_t kbytes, int64_t kblocks) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     s.codes = codes;
     s.scales = scales;
-    s.row = (int)r0 + wave * 32 + (lane >> 3);
-    s.srow = min((int)r0 + (wave & 3) * 64 + lane, (int)rows - 1);
-    s.last = (int)rows - 1;
-    s.kbytes = (int)kbytes;
-    s.kblocks = (int)kblocks;
-    s.chunk16 = ((lane & 7) ^ (lane >> 3)) * 16;
+    const int last = (int)rows - 1;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        s.off[q] = (uint32_t)min((int)r0 + mx_code_row(q), last) * (uint32_t)kbytes + mx_chunk16();
+    s.soff = (uint32_t)min((int)r0 + mx_scale_row(), last) * (uint32_t)kblocks;
 }
 
 // Global -> LDS copies issued from inline asm: the LDS base goes to M0 in the
@@ -87,8 +97,9 @@ __device__ __forceinline__ void mx_slab_src(MxSlabSrc& s, const uint8_t* codes, 
 // barrier that precedes any read of the buffer.  Issued this way, the compiler
 // does not hold the next stage's copies in flight against every LDS read of
 // the current stage.
-__device__ __forceinline__ void dma16(const uint8_t* g, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+__device__ __forceinline__ void dma16(const uint8_t* base, uint32_t off, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds)
+                 : "memory", "m0");
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -99,13 +110,13 @@ __device__ __forceinline__ void wait_vm_zero() { asm volatile("s_waitcnt vmcnt(0
 
 __device__ __forceinline__ void mx_issue_codes(MxCodes& st, const MxSlabSrc& A, const MxSlabSrc& B, int ks) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint8_t* ac = A.codes + (int64_t)ks * kRowBytes + A.chunk16;
-    const uint8_t* bc = B.codes + (int64_t)ks * kRowBytes + B.chunk16;
+    const uint8_t* ac = A.codes + (int64_t)ks * kRowBytes;
+    const uint8_t* bc = B.codes + (int64_t)ks * kRowBytes;
     const uint32_t la = lds_addr(st.a) + wave * 4 * 1024, lb = lds_addr(st.b) + wave * 4 * 1024;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        dma16(ac + (uint32_t)(min(A.row + q * 8, A.last) * A.kbytes), la + q * 1024);
-        dma16(bc + (uint32_t)(min(B.row + q * 8, B.last) * B.kbytes), lb + q * 1024);
+        dma16(ac, A.off[q], la + q * 1024);
+        dma16(bc, B.off[q], lb + q * 1024);
     }
 }
 
@@ -114,9 +125,9 @@ __device__ __forceinline__ void mx_issue_codes(MxCodes& st, const MxSlabSrc& A, 
 __device__ __forceinline__ void mx_issue_scales(MxScales& sc, const MxSlabSrc& A, const MxSlabSrc& B, int p) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (wave < 4)
-        dma16(A.scales + (int64_t)p * 16 + (uint32_t)(A.srow * A.kblocks), lds_addr(sc.a) + wave * 1024);
+        dma16(A.scales + (int64_t)p * 16, A.soff, lds_addr(sc.a) + wave * 1024);
     else
-        dma16(B.scales + (int64_t)p * 16 + (uint32_t)(B.srow * B.kblocks), lds_addr(sc.b) + (wave - 4) * 1024);
+        dma16(B.scales + (int64_t)p * 16, B.soff, lds_addr(sc.b) + (wave - 4) * 1024);
 }
 
 // Per-lane LDS bases of this wave's fragments (row wm*128 + i*16 + lr has
@@ -156,6 +167,10 @@ __device__ __forceinline__ int scale_at(uint2 w, int s, int lk) {
 // iteration.  At the start of step ks the copies of step ks have landed (wait +
 // barrier) and those of step ks + 1 (and, when ks + 1 is even, the scales of
 // steps ks + 1 and ks + 2) are issued into the buffers step ks - 1 used.
+// Only the wave's first NF row fragments are computed (the grouped GEMMs pass
+// fewer for a segment's last rows); every wave takes part in the copies and
+// barriers whatever its NF.
+template <int NF>
 __device__ __forceinline__ void mx_tile_mainloop(MxSmem& sm, const MxSlabSrc& A, const MxSlabSrc& B, int64_t kblocks,
                                                  v4f acc[kWaveFragsN][8]) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -174,20 +189,22 @@ __device__ __forceinline__ void mx_tile_mainloop(MxSmem& sm, const MxSlabSrc& A,
                 mx_issue_codes(sm.codes[(ks + 1) & 1], A, B, ks + 1);
                 if (((ks + 1) & 1) == 0) mx_issue_scales(sm.scales[((ks + 1) >> 1) & 1], A, B, (ks + 1) >> 1);
             }
+            if (NF == 0) continue;
             const uint8_t* sc_a = sm.scales[(ks >> 1) & 1].a + (ks & 1) * 8;
             const uint8_t* sc_b = sm.scales[(ks >> 1) & 1].b + (ks & 1) * 8;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) wsa[i] = *reinterpret_cast<const uint2*>(sc_a + lb.sa + i * 16 * kScaleRow);
+            for (int i = 0; i < NF; ++i) wsa[i] = *reinterpret_cast<const uint2*>(sc_a + lb.sa + i * 16 * kScaleRow);
 #pragma unroll
             for (int j = 0; j < kWaveFragsN; ++j)
                 wsb[j] = *reinterpret_cast<const uint2*>(sc_b + lb.sb + j * 16 * kScaleRow);
         }
+        if (NF == 0) continue;
         const uint8_t* st_a = sm.codes[ks & 1].a + (s ? lb.a[1] : lb.a[0]);
         const uint8_t* st_b = sm.codes[ks & 1].b + (s ? lb.b[1] : lb.b[0]);
         v8i a[8], b[kWaveFragsN];
         int sa[8], sb[kWaveFragsN];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < NF; ++i) {
             a[i] = frag_at(st_a + i * 16 * kRowBytes);
             sa[i] = scale_at(wsa[i], s, lk);
         }
@@ -199,9 +216,27 @@ __device__ __forceinline__ void mx_tile_mainloop(MxSmem& sm, const MxSlabSrc& A,
 #pragma unroll
         for (int j = 0; j < kWaveFragsN; ++j)
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
+            for (int i = 0; i < NF; ++i)
                 acc[j][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b[j], a[i], acc[j][i], 4, 4, 0, sb[j], 0,
                                                                                sa[i]);
+    }
+}
+
+// The K loop for a wave of which only `rows` (from its first row on) are
+// needed: ceil(rows / 16) row fragments, at least 0 and at most 8.
+__device__ __forceinline__ void mx_tile_mainloop_rows(MxSmem& sm, const MxSlabSrc& A, const MxSlabSrc& B,
+                                                      int64_t kblocks, v4f acc[kWaveFragsN][8], int64_t rows) {
+    const int nf = rows <= 0 ? 0 : (rows >= 128 ? 8 : (int)((rows + 15) >> 4));
+    switch (__builtin_amdgcn_readfirstlane(nf)) {
+        case 8: mx_tile_mainloop<8>(sm, A, B, kblocks, acc); break;
+        case 7: mx_tile_mainloop<7>(sm, A, B, kblocks, acc); break;
+        case 6: mx_tile_mainloop<6>(sm, A, B, kblocks, acc); break;
+        case 5: mx_tile_mainloop<5>(sm, A, B, kblocks, acc); break;
+        case 4: mx_tile_mainloop<4>(sm, A, B, kblocks, acc); break;
+        case 3: mx_tile_mainloop<3>(sm, A, B, kblocks, acc); break;
+        case 2: mx_tile_mainloop<2>(sm, A, B, kblocks, acc); break;
+        case 1: mx_tile_mainloop<1>(sm, A, B, kblocks, acc); break;
+        default: mx_tile_mainloop<0>(sm, A, B, kblocks, acc); break;
     }
 }
 

@@ -10,11 +10,14 @@
 //      (row, column) positions, so the epilogue forms h = SiLU(g) * u in
 //      registers, rounds it to bf16 and quantizes it (MX or NV) straight from LDS;
 //   4. grouped down GEMM on the quantized h rows, whose epilogue multiplies by
-//      the routing weight and adds into an fp32 [tokens, hidden] buffer;
-//   5. cast of that buffer to bf16.
+//      the routing weight and writes the fp32 row of the slot into a
+//      [slots, hidden] buffer;
+//   5. combine: each token's topk rows summed in fp32 in slot order, then
+//      rounded to bf16 (no atomics, so the output is deterministic).
 // The steps follow the expert path of the routed experts' w1/w3/w2 projections
 // ("DeepSeek-V4.1-Flash-NVFP4" explainer, section 3) and the dispatch /
 // combine of tokens to experts ("DeepSeek-V4" article, section 6.1).
+#include "gemm_mx_tile.h"
 #include "mma_core.h"
 #include "quant_device.h"
 
@@ -27,11 +30,12 @@ constexpr int kBM = 128;            // routed rows per grouped-GEMM tile
 constexpr int kGuCols = 64;         // intermediate columns (of g and of u) per gate/up tile
 constexpr int kDnCols = 128;        // hidden columns per down tile
 constexpr int kThreads = 256;
+constexpr int kScanBatch = 16;     // routing blocks read together by the scan
 
 inline size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
-    size_t xc, xs, counts, offsets, blockbase, perm, slot_pos, tile_e, tile_r, ntiles, hc, hs, out32, total;
+    size_t xc, xs, counts, offsets, blockbase, perm, slot_pos, tile_e, tile_r, ntiles, hc, hs, ybuf, total;
     int64_t nblk, max_tiles;
 };
 
@@ -55,7 +59,7 @@ Layout layout(int fmt, int64_t T, int64_t H, int topk, int E, int64_t I) {
     L.ntiles = take(4);
     L.hc = take((size_t)S * I / 2);
     L.hs = take((size_t)S * I / blk);
-    L.out32 = take((size_t)T * H * 4);
+    L.ybuf = take((size_t)S * H * 4);
     L.total = o;
     return L;
 }
@@ -105,7 +109,7 @@ __device__ void block_scan2(int& a, int& b, int* sh) {
 __global__ __launch_bounds__(1024) void route_scan_kernel(int32_t* __restrict__ blockcount, int64_t nblk, int E,
                                                           int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                           int32_t* __restrict__ tile_e, int32_t* __restrict__ tile_r,
-                                                          int32_t* __restrict__ ntiles) {
+                                                          int32_t* __restrict__ ntiles, int tile_rows) {
     __shared__ int sh[40];
     constexpr int EPT = kMaxExperts / 1024;       // experts per thread (1)
     int tot[EPT];
@@ -114,11 +118,21 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int32_t* __restrict__ 
     for (int q = 0; q < EPT; ++q) {
         const int e = threadIdx.x * EPT + q;
         int t = 0;
-        if (e < E)
-            for (int64_t b = 0; b < nblk; ++b) t += blockcount[b * E + e];
+        if (e < E) {
+            // batches of independent loads: the loop is bound by load latency
+            int64_t b = 0;
+            for (; b + kScanBatch <= nblk; b += kScanBatch) {
+                int v[kScanBatch];
+#pragma unroll
+                for (int u = 0; u < kScanBatch; ++u) v[u] = blockcount[(b + u) * E + e];
+#pragma unroll
+                for (int u = 0; u < kScanBatch; ++u) t += v[u];
+            }
+            for (; b < nblk; ++b) t += blockcount[b * E + e];
+        }
         tot[q] = t;
         rows += t;
-        tiles += (t + kBM - 1) / kBM;
+        tiles += (t + tile_rows - 1) / tile_rows;
         if (e < E) counts[e] = t;
     }
     int prow = rows, ptile = tiles;
@@ -129,15 +143,26 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int32_t* __restrict__ 
         if (e >= E) break;
         offsets[e] = prow;
         int base = prow;
-        for (int64_t b = 0; b < nblk; ++b) {
+        int64_t b = 0;
+        for (; b + kScanBatch <= nblk; b += kScanBatch) {
+            int v[kScanBatch];
+#pragma unroll
+            for (int u = 0; u < kScanBatch; ++u) v[u] = blockcount[(b + u) * E + e];
+#pragma unroll
+            for (int u = 0; u < kScanBatch; ++u) {
+                blockcount[(b + u) * E + e] = base;
+                base += v[u];
+            }
+        }
+        for (; b < nblk; ++b) {
             const int c = blockcount[b * E + e];
             blockcount[b * E + e] = base;
             base += c;
         }
-        const int nt = (tot[q] + kBM - 1) / kBM;
+        const int nt = (tot[q] + tile_rows - 1) / tile_rows;
         for (int i = 0; i < nt; ++i) {
             tile_e[ptile + i] = e;
-            tile_r[ptile + i] = prow + i * kBM;
+            tile_r[ptile + i] = prow + i * tile_rows;
         }
         ptile += nt;
         prow += tot[q];
@@ -187,7 +212,7 @@ struct GemmParams {
     const int32_t *perm, *offsets, *tile_e, *tile_r, *ntiles;
     const float* weights;              // [S]
     uint8_t *hc, *hs;                  // quantized h [S, I/2], [S, I/blk] in routed order
-    float* out32;                      // [T, H]
+    float* ybuf;                       // [S, H]: w * y of slot s in row s
     fp4_moe_debug dbg;
 };
 
@@ -365,7 +390,6 @@ __global__ __launch_bounds__(kThreads) void moe_down_kernel(GemmParams p) {
             const int64_t pos = r0 + wm * 64 + i * 16 + lk * 4 + r;
             if (pos >= rend) continue;
             const int64_t slot = p.perm[pos];
-            const int64_t t = slot / p.topk;
             const float wgt = p.weights[slot];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -373,23 +397,236 @@ __global__ __launch_bounds__(kThreads) void moe_down_kernel(GemmParams p) {
                 float y = acc[i][j][r];
                 if (FMT == FP4_FMT_NV) y = __fmul_rn(y, yscale);
                 if (p.dbg.y) p.dbg.y[slot * H + col] = y;
-                unsafeAtomicAdd(&p.out32[t * H + col], __fmul_rn(wgt, y));
+                p.ybuf[slot * H + col] = __fmul_rn(wgt, y);
             }
         }
 }
 
-__global__ __launch_bounds__(kThreads) void zero_f32_kernel(float4* __restrict__ p, int64_t n4) {
-    const int64_t stride = (int64_t)gridDim.x * kThreads;
-    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n4; i += stride) p[i] = make_float4(0, 0, 0, 0);
+// ------------------------------------------------------------------ MX grouped GEMMs on LDS-staged tiles
+// 256 routed rows x 256 slab rows per workgroup on the MX tile of
+// gemm_mx_tile.h (K a multiple of 512).  A wave (wm, wn) owns routed rows
+// wm*128 .. +127 and slab columns wn*64 .. +63; it computes only the 16-row
+// fragments that hold rows of its expert's segment (it still moves data for
+// the others).  Rows past the segment are pointed at the segment's last row.
+
+// gate/up: slab row wn*64 + q holds w1 row c0 + wn*32 + q (q < 32) or the w3
+// row of the same intermediate column (q >= 32), so fragments j = 0, 1 of a
+// wave carry g and fragments j = 2, 3 the matching u.  The tile covers 128
+// intermediate columns; h (bf16) goes through LDS and is quantized there.
+constexpr int kGu2Cols = 128;
+constexpr int kYRow = kTileN + 4;   // fp32 row pitch of the down tile's combine buffer (bank spread)
+static_assert(128 * kYRow * 4 <= (int)sizeof(MxSmem), "combine buffer exceeds the tile's LDS");
+
+__device__ __forceinline__ int64_t gu_weight_row(int slab_row, int64_t c0, int64_t I) {
+    const int wn = slab_row >> 6, q = slab_row & 63;
+    return (q >= 32 ? I : 0) + c0 + wn * 32 + (q & 31);
 }
 
-__global__ __launch_bounds__(kThreads) void cast_bf16_kernel(const float4* __restrict__ in, uint2* __restrict__ out,
-                                                             int64_t n4) {
+// h tile in LDS: 256 rows x 128 bf16; 16-byte unit u of row r is stored at unit
+// u ^ (r & 15), so the epilogue's column-fragment stores spread over the banks.
+__device__ __forceinline__ int h_unit_off(int row, int unit) { return row * kGu2Cols + ((unit ^ (row & 15)) << 3); }
+
+__global__ __launch_bounds__(kTileThreads, 1) void moe_gate_up_mx256_kernel(GemmParams p) {
+    __shared__ __align__(16) MxSmem sm;
+    const int tile = blockIdx.y;
+    if (tile >= *p.ntiles) return;
+    const int e = p.tile_e[tile];
+    const int64_t r0 = p.tile_r[tile];
+    const int64_t rend = p.offsets[e + 1];
+    const int64_t c0 = (int64_t)blockIdx.x * kGu2Cols;
+    const int64_t H = p.H, I = p.I;
+    const uint32_t kbytes = (uint32_t)(H / 2), kblocks = (uint32_t)(H / 32);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave >> 2, wn = wave & 3, lr = lane & 15, lk = lane >> 4;
+    const bool injected = p.dbg.gate_up_in != nullptr;
+
+    v4f acc[kWaveFragsN][8];
+#pragma unroll
+    for (int j = 0; j < kWaveFragsN; ++j)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[j][i] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    if (!injected) {
+        MxSlabSrc A, B;
+        A.codes = p.xc;
+        A.scales = p.xs;
+        B.codes = p.w13c + (int64_t)e * (2 * I) * (H / 2);
+        B.scales = p.w13s + (int64_t)e * (2 * I) * (H / 32);
+        const uint32_t ch = mx_chunk16();
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int64_t pos = min(r0 + mx_code_row(q), rend - 1);
+            A.off[q] = (uint32_t)(p.perm[pos] / p.topk) * kbytes + ch;
+            B.off[q] = (uint32_t)gu_weight_row(mx_code_row(q), c0, I) * kbytes + ch;
+        }
+        const int64_t spos = min(r0 + mx_scale_row(), rend - 1);
+        A.soff = (uint32_t)(p.perm[spos] / p.topk) * kblocks;
+        B.soff = (uint32_t)gu_weight_row(mx_scale_row(), c0, I) * kblocks;
+        mx_tile_mainloop_rows(sm, A, B, H / 32, acc, rend - (r0 + wm * 128));
+    } else {
+        // g|u given per slot (debug injection): place them in the accumulator layout
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int64_t pos = r0 + wm * 128 + i * 16 + lr;
+            if (pos >= rend) continue;
+            const float* src = p.dbg.gate_up_in + (int64_t)p.perm[pos] * 2 * I;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    acc[j][i][r] = src[(j < 2 ? 0 : I) + c0 + wn * 32 + (j & 1) * 16 + lk * 4 + r];
+        }
+    }
+    __syncthreads();   // every wave is done with the stages; the h tile reuses them
+
+    uint16_t* hsm = reinterpret_cast<uint16_t*>(&sm.codes[0]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int rl = wm * 128 + i * 16 + lr;
+        const int64_t pos = r0 + rl;
+        const bool dbg_row = pos < rend && (p.dbg.gate_up || p.dbg.h_bf16);
+        const int64_t slot = dbg_row ? p.perm[pos] : 0;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int cl = wn * 32 + j * 16 + lk * 4;        // 4 consecutive intermediate columns
+            uint32_t hb[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float g = acc[j][i][r], u = acc[j + 2][i][r];
+                hb[r] = f32_to_bf16_rne(silu_mul(g, u));
+                if (dbg_row && p.dbg.gate_up) {
+                    p.dbg.gate_up[slot * 2 * I + c0 + cl + r] = g;
+                    p.dbg.gate_up[slot * 2 * I + I + c0 + cl + r] = u;
+                }
+                if (dbg_row && p.dbg.h_bf16) static_cast<uint16_t*>(p.dbg.h_bf16)[slot * I + c0 + cl + r] = (uint16_t)hb[r];
+            }
+            *reinterpret_cast<uint2*>(&hsm[h_unit_off(rl, cl >> 3) + (cl & 7)]) =
+                make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
+        }
+    }
+    __syncthreads();
+    // quantize the 256 x 128 h tile: unit = 8 consecutive columns of one row;
+    // the 4 units of an MX block sit in 4 consecutive lanes
+#pragma unroll
+    for (int q = 0; q < (kTileM * kGu2Cols / 8) / kTileThreads; ++q) {
+        const int unit = threadIdx.x + q * kTileThreads;
+        const int rl = unit >> 4, cu = unit & 15;
+        const uint4 v = *reinterpret_cast<const uint4*>(&hsm[h_unit_off(rl, cu)]);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        uint32_t sb;
+        const uint32_t packed = mx_quant8(w, sb);
+        const int64_t pos = r0 + rl;
+        if (pos < rend) {
+            const int64_t col = c0 + cu * 8;
+            reinterpret_cast<uint32_t*>(p.hc + pos * (I / 2) + col / 2)[0] = packed;
+            const bool lead = (cu & 3) == 0;
+            if (lead) p.hs[pos * (I / 32) + col / 32] = (uint8_t)sb;
+            if (p.dbg.h_codes || p.dbg.h_scales) {
+                const int64_t slot = p.perm[pos];
+                if (p.dbg.h_codes) reinterpret_cast<uint32_t*>(p.dbg.h_codes + slot * (I / 2) + col / 2)[0] = packed;
+                if (p.dbg.h_scales && lead) p.dbg.h_scales[slot * (I / 32) + col / 32] = (uint8_t)sb;
+            }
+        }
+    }
+}
+
+// down: routed h rows (or, injected, each slot's given quantized h) times the
+// 256 w2 rows n0 .. n0 + 255; y times the routing weight is added into the
+// fp32 [tokens, hidden] buffer.
+__global__ __launch_bounds__(kTileThreads, 1) void moe_down_mx256_kernel(GemmParams p) {
+    __shared__ __align__(16) MxSmem sm;
+    const int tile = blockIdx.y;
+    if (tile >= *p.ntiles) return;
+    const int e = p.tile_e[tile];
+    const int64_t r0 = p.tile_r[tile];
+    const int64_t rend = p.offsets[e + 1];
+    const int64_t n0 = (int64_t)blockIdx.x * kTileN;
+    const int64_t H = p.H, I = p.I;
+    const uint32_t kbytes = (uint32_t)(I / 2), kblocks = (uint32_t)(I / 32);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave >> 2, wn = wave & 3, lr = lane & 15, lk = lane >> 4;
+
+    MxSlabSrc A, B;
+    const bool inj = p.dbg.h_codes_in != nullptr;
+    A.codes = inj ? p.dbg.h_codes_in : p.hc;
+    A.scales = inj ? p.dbg.h_scales_in : p.hs;
+    const uint32_t ch = mx_chunk16();
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int64_t pos = min(r0 + mx_code_row(q), rend - 1);
+        A.off[q] = (uint32_t)(inj ? p.perm[pos] : pos) * kbytes + ch;
+    }
+    const int64_t spos = min(r0 + mx_scale_row(), rend - 1);
+    A.soff = (uint32_t)(inj ? p.perm[spos] : spos) * kblocks;
+    mx_slab_src(B, p.w2c + (int64_t)e * H * (I / 2), p.w2s + (int64_t)e * H * (I / 32), n0, H, I / 2, I / 32);
+
+    v4f acc[kWaveFragsN][8];
+#pragma unroll
+    for (int j = 0; j < kWaveFragsN; ++j)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[j][i] = v4f{0.f, 0.f, 0.f, 0.f};
+    mx_tile_mainloop_rows(sm, A, B, I / 32, acc, rend - (r0 + wm * 128));
+
+    if (p.dbg.y) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int64_t pos = r0 + wm * 128 + i * 16 + lr;
+            if (pos >= rend) continue;
+            const int64_t slot = p.perm[pos];
+#pragma unroll
+            for (int j = 0; j < kWaveFragsN; ++j)
+                *reinterpret_cast<float4*>(&p.dbg.y[slot * H + n0 + wn * kWaveN + j * 16 + lk * 4]) =
+                    make_float4(acc[j][i][0], acc[j][i][1], acc[j][i][2], acc[j][i][3]);
+        }
+    }
+    // w * y of each routed row goes to its slot's row of the y buffer; the tile
+    // passes through LDS one 128-row band at a time so that each store
+    // instruction writes 1 KiB of one row.
+    float* ysm = reinterpret_cast<float*>(&sm);
+    for (int band = 0; band < 2; ++band) {
+        __syncthreads();
+        if (wm == band) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int j = 0; j < kWaveFragsN; ++j)
+                    *reinterpret_cast<float4*>(&ysm[(i * 16 + lr) * kYRow + wn * kWaveN + j * 16 + lk * 4]) =
+                        make_float4(acc[j][i][0], acc[j][i][1], acc[j][i][2], acc[j][i][3]);
+        }
+        __syncthreads();
+        for (int rr = wave; rr < 128; rr += kTileThreads / 64) {
+            const int64_t pos = r0 + band * 128 + rr;
+            if (pos >= rend) break;     // rows are in order: the rest of this wave's rows are past the end too
+            const int64_t slot = p.perm[pos];
+            const float wgt = p.weights[slot];
+            const float4 v = *reinterpret_cast<const float4*>(&ysm[rr * kYRow + lane * 4]);
+            *reinterpret_cast<float4*>(p.ybuf + slot * H + n0 + lane * 4) =
+                make_float4(__fmul_rn(wgt, v.x), __fmul_rn(wgt, v.y), __fmul_rn(wgt, v.z), __fmul_rn(wgt, v.w));
+        }
+    }
+}
+
+// out[t] = bf16(sum over j of w * y of slot t*topk + j), summed in fp32 in
+// order j = 0 .. topk-1 over the slots whose expert id is in range.
+__global__ __launch_bounds__(kThreads) void combine_kernel(const float4* __restrict__ ybuf,
+                                                           const int32_t* __restrict__ ids, int topk, int E,
+                                                           int64_t T, int64_t H4, uint2* __restrict__ out) {
+    const int64_t n = T * H4;
     const int64_t stride = (int64_t)gridDim.x * kThreads;
-    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n4; i += stride) {
-        const float4 v = in[i];
-        out[i] = make_uint2(f32_to_bf16_rne(v.x) | (f32_to_bf16_rne(v.y) << 16),
-                            f32_to_bf16_rne(v.z) | (f32_to_bf16_rne(v.w) << 16));
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride) {
+        const int64_t t = i / H4, c = i - t * H4;
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int j = 0; j < topk; ++j) {
+            const int64_t slot = t * topk + j;
+            if ((unsigned)ids[slot] >= (unsigned)E) continue;
+            const float4 v = ybuf[slot * H4 + c];
+            acc.x = __fadd_rn(acc.x, v.x);
+            acc.y = __fadd_rn(acc.y, v.y);
+            acc.z = __fadd_rn(acc.z, v.z);
+            acc.w = __fadd_rn(acc.w, v.w);
+        }
+        out[i] = make_uint2(f32_to_bf16_rne(acc.x) | (f32_to_bf16_rne(acc.y) << 16),
+                            f32_to_bf16_rne(acc.z) | (f32_to_bf16_rne(acc.w) << 16));
     }
 }
 
@@ -398,7 +635,6 @@ inline unsigned stream_grid(int64_t n) {
     if (b > 8192) b = 8192;
     return (unsigned)(b < 1 ? 1 : b);
 }
-
 }  // namespace
 
 int64_t moe_max_tiles(int64_t tokens, int topk, int num_experts) {
@@ -425,7 +661,7 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t s) {
     int32_t* ntiles = reinterpret_cast<int32_t*>(base + L.ntiles);
     uint8_t* hc = base + L.hc;
     uint8_t* hs = base + L.hs;
-    float* out32 = reinterpret_cast<float*>(base + L.out32);
+    float* ybuf = reinterpret_cast<float*>(base + L.ybuf);
     const int64_t T = a.tokens, H = a.hidden, I = a.inter, S = T * a.topk;
     const int E = a.num_experts;
 
@@ -436,10 +672,12 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t s) {
     if (err != hipSuccess) return err;
     // 2. routing metadata
     route_count_kernel<<<(unsigned)L.nblk, kRouteSlots, 0, s>>>(a.ids, S, E, blockbase);
-    route_scan_kernel<<<1, 1024, 0, s>>>(blockbase, L.nblk, E, counts, offsets, tile_e, tile_r, ntiles);
+    // MX with hidden and inter multiples of 512: 256-row LDS-staged tiles
+    const bool tiled = a.fmt == FP4_FMT_MX && H % 512 == 0 && I % 512 == 0;
+    route_scan_kernel<<<1, 1024, 0, s>>>(blockbase, L.nblk, E, counts, offsets, tile_e, tile_r, ntiles,
+                                         tiled ? kTileM : kBM);
     route_place_kernel<<<(unsigned)L.nblk, kRouteSlots, (size_t)E * (kRouteSlots / 32) * 4, s>>>(a.ids, S, E, blockbase, perm,
                                                                                   slot_pos);
-    zero_f32_kernel<<<stream_grid(T * H / 4), kThreads, 0, s>>>(reinterpret_cast<float4*>(out32), T * H / 4);
     if ((err = hipGetLastError()) != hipSuccess) return err;
 
     GemmParams p{};
@@ -464,21 +702,28 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t s) {
     p.weights = a.weights;
     p.hc = hc;
     p.hs = hs;
-    p.out32 = out32;
+    p.ybuf = ybuf;
     p.dbg = a.dbg;
     // 3. gate/up + SiLU*mul + quantize h; 4. down + weighted combine
-    const dim3 g_gu((unsigned)(I / kGuCols), (unsigned)L.max_tiles);
-    const dim3 g_dn((unsigned)(H / kDnCols), (unsigned)L.max_tiles);
-    if (a.fmt == FP4_FMT_MX) {
-        moe_gate_up_kernel<FP4_FMT_MX><<<g_gu, kThreads, 0, s>>>(p);
-        moe_down_kernel<FP4_FMT_MX><<<g_dn, kThreads, 0, s>>>(p);
+    if (tiled) {
+        const dim3 g_gu((unsigned)(I / kGu2Cols), (unsigned)L.max_tiles);
+        const dim3 g_dn((unsigned)(H / kTileN), (unsigned)L.max_tiles);
+        moe_gate_up_mx256_kernel<<<g_gu, kTileThreads, 0, s>>>(p);
+        moe_down_mx256_kernel<<<g_dn, kTileThreads, 0, s>>>(p);
     } else {
-        moe_gate_up_kernel<FP4_FMT_NV><<<g_gu, kThreads, 0, s>>>(p);
-        moe_down_kernel<FP4_FMT_NV><<<g_dn, kThreads, 0, s>>>(p);
+        const dim3 g_gu((unsigned)(I / kGuCols), (unsigned)L.max_tiles);
+        const dim3 g_dn((unsigned)(H / kDnCols), (unsigned)L.max_tiles);
+        if (a.fmt == FP4_FMT_MX) {
+            moe_gate_up_kernel<FP4_FMT_MX><<<g_gu, kThreads, 0, s>>>(p);
+            moe_down_kernel<FP4_FMT_MX><<<g_dn, kThreads, 0, s>>>(p);
+        } else {
+            moe_gate_up_kernel<FP4_FMT_NV><<<g_gu, kThreads, 0, s>>>(p);
+            moe_down_kernel<FP4_FMT_NV><<<g_dn, kThreads, 0, s>>>(p);
+        }
     }
-    // 5. fp32 -> bf16
-    cast_bf16_kernel<<<stream_grid(T * H / 4), kThreads, 0, s>>>(reinterpret_cast<const float4*>(out32),
-                                                                   reinterpret_cast<uint2*>(a.out), T * H / 4);
+    // 5. weighted combine
+    combine_kernel<<<stream_grid(T * H / 4), kThreads, 0, s>>>(reinterpret_cast<const float4*>(ybuf), a.ids, a.topk, E,
+                                                                 T, H / 4, reinterpret_cast<uint2*>(a.out));
     if ((err = hipGetLastError()) != hipSuccess) return err;
     const int bx = a.fmt == FP4_FMT_MX ? 32 : 16;
     if (a.dbg.x_codes &&

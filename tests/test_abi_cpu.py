@@ -1,0 +1,126 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library must load, export every function that include/fp4.h declares, and
+reject bad arguments with the documented status before it makes any HIP call
+(so these calls are safe without a device: no pointer is dereferenced).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp4.h")
+
+OK, INVALID, SHAPE, ALIGN, UNSUPPORTED, WORKSPACE, HIPERR = 0, -1, -2, -3, -4, -5, -6
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    names = re.findall(r"\b(fp4_[a-z0-9_]+)\s*\(", src)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def F():
+    import block_scaled_fp4_mx_amd as pkg
+    return pkg
+
+
+def test_header_declares_the_six_entry_points():
+    names = declared_functions()
+    for n in ("fp4_quantize_mx", "fp4_quantize_nv", "fp4_remap_mx_to_nv", "fp4_dequant", "fp4_gemm",
+              "fp4_moe_grouped_gemm"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(F):
+    lib = ctypes.CDLL(F.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, f"not exported: {missing}"
+    # the binding wraps every declared entry point under the same name
+    for n in declared_functions():
+        if n not in ("fp4_status_string", "fp4_last_error"):
+            assert hasattr(F, n), n
+
+
+def test_version_and_status_strings(F):
+    assert F.lib.fp4_abi_version() >= 1
+    for st in (OK, INVALID, SHAPE, ALIGN, UNSUPPORTED, WORKSPACE, HIPERR):
+        assert F.lib.fp4_status_string(st)
+    assert F.lib.fp4_status_string(12345) == b"unknown status"
+
+
+FAKE = 1 << 20          # 16-byte aligned, never dereferenced by rejected calls
+MISALIGNED = FAKE + 8
+
+
+def test_quantize_mx_rejections(F):
+    q = F.lib.fp4_quantize_mx
+    assert q(FAKE, 4, 48, 48, FAKE, FAKE, None) == SHAPE            # k % 32
+    assert q(FAKE, -1, 32, 32, FAKE, FAKE, None) == INVALID
+    assert q(None, 4, 32, 32, FAKE, FAKE, None) == INVALID
+    assert b"x_bf16" in F.lib.fp4_last_error()
+    assert q(MISALIGNED, 4, 32, 32, FAKE, FAKE, None) == ALIGN
+    assert q(FAKE, 4, 32, 16, FAKE, FAKE, None) == INVALID          # ld_x < k
+    assert q(FAKE, 4, 32, 36, FAKE, FAKE, None) == ALIGN            # ld_x % 8
+    assert q(None, 0, 32, 32, None, None, None) == OK               # empty: no-op
+    assert q(None, 5, 0, 0, None, None, None) == OK
+
+
+def test_quantize_nv_rejections(F):
+    q = F.lib.fp4_quantize_nv
+    assert q(FAKE, 4, 40, 40, FAKE, FAKE, FAKE, 0, FAKE, 4096, None) == SHAPE   # k % 16
+    assert q(FAKE, 4, 32, 32, FAKE, FAKE, None, 0, FAKE, 4096, None) == INVALID  # no tensor scale
+    assert q(FAKE, 4, 32, 32, FAKE, FAKE, FAKE + 2, 0, FAKE, 4096, None) == ALIGN
+    need = F.lib.fp4_quantize_nv_workspace_bytes(4, 32)
+    assert need > 0
+    assert q(FAKE, 4, 32, 32, FAKE, FAKE, FAKE, 0, None, 0, None) == WORKSPACE
+    assert q(FAKE, 4, 32, 32, FAKE, FAKE, FAKE, 0, FAKE, need - 1, None) == WORKSPACE
+    assert q(None, 0, 32, 32, None, None, None, 0, None, 0, None) == OK
+
+
+def test_remap_and_dequant_rejections(F):
+    r = F.lib.fp4_remap_mx_to_nv
+    assert r(FAKE, FAKE, 4, 48, FAKE, FAKE, FAKE, None) == SHAPE
+    assert r(FAKE, FAKE, 4, 64, FAKE, FAKE, None, None) == INVALID
+    d = F.lib.fp4_dequant
+    assert d(7, FAKE, FAKE, FAKE, 4, 32, FAKE, 0, 32, None) == INVALID         # format
+    assert d(0, FAKE, FAKE, FAKE, 4, 32, FAKE, 9, 32, None) == INVALID         # dtype
+    assert d(1, FAKE, FAKE, FAKE, 4, 24, FAKE, 0, 24, None) == SHAPE           # NV k % 16
+    assert d(1, FAKE, FAKE, None, 4, 32, FAKE, 0, 32, None) == INVALID         # NV needs s_t
+    assert d(0, FAKE, FAKE, None, 4, 32, FAKE, 0, 16, None) == INVALID         # ld_out < k
+
+
+def test_gemm_rejections(F):
+    g = F.lib.fp4_gemm
+    args = lambda fmt, m, n, k, ldc, ats=FAKE, c=FAKE: (fmt, FAKE, FAKE, ats, FAKE, FAKE, FAKE, m, n, k, c, 0, ldc,
+                                                        None)
+    assert g(*args(0, 8, 8, 48, 8)) == SHAPE
+    assert g(*args(1, 8, 8, 40, 8)) == SHAPE
+    assert g(*args(0, 8, 8, 64, 4)) == INVALID     # ldc < n
+    assert g(*args(1, 8, 8, 64, 8, ats=None)) == INVALID
+    assert g(*args(0, 8, 8, 64, 8, c=MISALIGNED)) == ALIGN
+    assert g(*args(0, 0, 8, 64, 8, c=None)) == OK  # empty
+
+
+def test_moe_rejections_and_workspace(F):
+    m = F.lib.fp4_moe_grouped_gemm
+    ws = F.lib.fp4_moe_workspace_bytes(0, 64, 256, 2, 8, 128)
+    assert ws > 0
+    assert F.lib.fp4_moe_workspace_bytes(0, 64, 256, 0, 8, 128) == 0
+
+    def call(fmt=0, tokens=64, hidden=256, topk=2, E=8, inter=128, ws_bytes=ws, ws_ptr=FAKE, act=None):
+        return m(fmt, FAKE, tokens, hidden, FAKE, FAKE, topk, E, inter, FAKE, FAKE, None, FAKE, FAKE, None, act,
+                 FAKE, ws_ptr, ws_bytes, None, None)
+
+    assert call(hidden=192) == SHAPE
+    assert call(topk=17) == INVALID
+    assert call(E=2000) == INVALID
+    assert call(ws_bytes=ws - 1) == WORKSPACE
+    assert call(ws_ptr=None) == WORKSPACE
+    assert call(fmt=1) == INVALID                   # NV needs tensor scales
+    assert call(tokens=0, ws_ptr=None, ws_bytes=0) == OK

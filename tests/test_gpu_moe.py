@@ -55,6 +55,16 @@ def test_moe_multi_tile_segments(fmt):
     _all_checks(case, oracle_expect(case, np.arange(case.T), eq))
 
 
+def test_moe_tiled_mx_segments():
+    """Hidden and intermediate multiples of 512 take the 256-row LDS-staged MX
+    tiles: segments spanning several tiles, ragged last tiles, and last tiles of
+    at most 128 rows (whose second row band skips the matrix work)."""
+    case, eq = _small_case("mx", 104, 700, 512, 512, 4, 2)
+    counts = np.bincount(case.ids.ravel(), minlength=4)
+    assert counts.max() > 256 and ((counts % 256) <= 128).any()
+    _all_checks(case, oracle_expect(case, np.arange(case.T), eq))
+
+
 def test_moe_single_expert_topk1():
     T, H, I, E = 33, 128, 256, 5
     ids = np.full((T, 1), 3, np.int32)
