@@ -52,7 +52,7 @@ int check_ld(int64_t ld, int64_t width, const char* name) {
     return FP4_OK;
 }
 
-size_t nv_ws_bytes() { return 256; }
+size_t nv_ws_bytes() { return 4096; }   // pass-1 partial maxima of the tensor amax (1024 words)
 
 }  // namespace
 

@@ -11,7 +11,9 @@ namespace fp4 {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;      // 16-byte loads in flight per lane
+constexpr int kUnroll = 4;      // 16-byte loads in flight per lane (tensor amax pass)
+constexpr int kMxUnroll = 2;    // MX quantize: 16-byte loads per lane per iteration
+constexpr unsigned kMxMaxBlocks = 2048;
 
 inline unsigned grid_for(int64_t units, int per_thread = 1) {
     int64_t b = (units + (int64_t)kThreads * per_thread - 1) / ((int64_t)kThreads * per_thread);
@@ -28,23 +30,23 @@ __device__ __forceinline__ int64_t x_offset(int64_t u, int64_t upr, int64_t ldx)
 
 // ------------------------------------------------------------------ MX quantize
 // Lane u owns elements 8u..8u+7 of the row-major [rows, k] input (codes word u,
-// scale byte u/4).  Each lane issues kUnroll loads before converting.
+// scale byte u/4).  Each lane issues kMxUnroll loads before converting.
 template <bool kContig>
 __global__ __launch_bounds__(kThreads) void mx_quantize_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t k, int64_t ldx,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
     const int64_t upr = k >> 3;
     const int64_t total = rows * upr;
-    const int64_t step = (int64_t)gridDim.x * kThreads * kUnroll;
-    for (int64_t base = (int64_t)blockIdx.x * kThreads * kUnroll + threadIdx.x; base < total; base += step) {
-        uint4 v[kUnroll];
+    const int64_t step = (int64_t)gridDim.x * kThreads * kMxUnroll;
+    for (int64_t base = (int64_t)blockIdx.x * kThreads * kMxUnroll + threadIdx.x; base < total; base += step) {
+        uint4 v[kMxUnroll];
 #pragma unroll
-        for (int j = 0; j < kUnroll; ++j) {
+        for (int j = 0; j < kMxUnroll; ++j) {
             const int64_t u = base + (int64_t)j * kThreads;
             if (u < total) v[j] = *reinterpret_cast<const uint4*>(x + x_offset<kContig>(u, upr, ldx));
         }
 #pragma unroll
-        for (int j = 0; j < kUnroll; ++j) {
+        for (int j = 0; j < kMxUnroll; ++j) {
             const int64_t u = base + (int64_t)j * kThreads;
             if (u < total) {
                 const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
@@ -58,18 +60,31 @@ __global__ __launch_bounds__(kThreads) void mx_quantize_kernel(
 }
 
 // ------------------------------------------------------------------ NV quantize
-__global__ void nv_amax_init_kernel(uint32_t* amax) { *amax = 0u; }
+// Two passes when s_t is computed: (1) per-workgroup maxima of |x| into the
+// workspace; (2) every quantize workgroup reduces those partials itself (the
+// first reads of x already in flight), derives s_t, and workgroup 0 stores it.
+// The second read of x mostly hits the last-level cache for tensors that fit.
+constexpr int kNvAmaxBlocks = 1024;   // partial maxima written by pass 1
+constexpr int kNvDepth = 1;           // 16-groups per lane whose loads are in flight (32 B each)
+constexpr unsigned kNvMaxBlocks = 1024;
 
 template <bool kContig>
 __global__ __launch_bounds__(kThreads) void nv_amax_kernel(
-    const uint16_t* __restrict__ x, int64_t rows, int64_t k, int64_t ldx, uint32_t* amax_out) {
+    const uint16_t* __restrict__ x, int64_t rows, int64_t k, int64_t ldx, uint32_t* __restrict__ part) {
     const int64_t upr = k >> 3;
     const int64_t total = rows * upr;
-    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    const int64_t step = (int64_t)gridDim.x * kThreads * kUnroll;
     uint32_t am = 0;
-    for (int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x; u < total; u += stride) {
-        const uint4 v = *reinterpret_cast<const uint4*>(x + x_offset<kContig>(u, upr, ldx));
-        am = max(am, max(max(mag_max2(v.x), mag_max2(v.y)), max(mag_max2(v.z), mag_max2(v.w))));
+    for (int64_t base = (int64_t)blockIdx.x * kThreads * kUnroll + threadIdx.x; base < total; base += step) {
+        uint4 v[kUnroll];
+#pragma unroll
+        for (int j = 0; j < kUnroll; ++j) {
+            const int64_t u = base + (int64_t)j * kThreads;
+            v[j] = u < total ? *reinterpret_cast<const uint4*>(x + x_offset<kContig>(u, upr, ldx)) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < kUnroll; ++j)
+            am = max(am, max(max(mag_max2(v[j].x), mag_max2(v[j].y)), max(mag_max2(v[j].z), mag_max2(v[j].w))));
     }
     for (int off = 32; off > 0; off >>= 1) am = max(am, (uint32_t)__shfl_xor((int)am, off));
     __shared__ uint32_t red[kThreads / 64];
@@ -78,44 +93,90 @@ __global__ __launch_bounds__(kThreads) void nv_amax_kernel(
     if (threadIdx.x == 0) {
         uint32_t m = red[0];
         for (int i = 1; i < kThreads / 64; ++i) m = max(m, red[i]);
-        atomicMax(amax_out, m);
+        part[blockIdx.x] = m;
     }
 }
 
-// s_t = fp32(amax / 2688): the fp64 quotient is correctly rounded, and rounding
-// it again to fp32 is exact because an 8-bit numerator over 21 * 2^7 is either
-// a short dyadic (exact) or far from every fp32 rounding midpoint.
-__global__ void nv_tensor_scale_kernel(const uint32_t* amax, float* ts) {
-    const float a = __uint_as_float(*amax << 16);
-    *ts = (float)((double)a / 2688.0);
+template <bool kContig>
+__device__ __forceinline__ void nv_load16(const uint16_t* __restrict__ x, int64_t u, int64_t gpr, int64_t ldx,
+                                          uint4& a, uint4& b) {
+    int64_t o;
+    if (kContig) {
+        o = u * 16;
+    } else {
+        const int64_t r = u / gpr;
+        o = r * ldx + (u - r * gpr) * 16;
+    }
+    const uint4* p = reinterpret_cast<const uint4*>(x + o);
+    a = p[0];
+    b = p[1];
 }
 
-// Lane u owns 8 elements; a 16-group spans lanes (2i, 2i+1).  The tensor scale
-// is read from device memory (written by the amax pass or supplied).
+// Lane u owns 16-groups u, u + stride, ... (elements 16u .. 16u + 15 of their
+// rows): 8 code bytes and one scale byte each.  The loads of the next two
+// groups are in flight while one is converted.  npart > 0: s_t comes from the
+// pass-1 partial maxima (and is stored by workgroup 0); npart == 0: s_t is read
+// from *ts.
 template <bool kContig>
 __global__ __launch_bounds__(kThreads) void nv_quantize_kernel(
-    const uint16_t* __restrict__ x, int64_t rows, int64_t k, int64_t ldx,
-    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, const float* __restrict__ ts) {
-    const int64_t upr = k >> 3;
-    const int64_t total = rows * upr;
-    const int64_t step = (int64_t)gridDim.x * kThreads * kUnroll;
-    const double st = (double)*ts;
-    for (int64_t base = (int64_t)blockIdx.x * kThreads * kUnroll + threadIdx.x; base < total; base += step) {
-        uint4 v[kUnroll];
+    const uint16_t* __restrict__ x, int64_t rows, int64_t k, int64_t ldx, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ scales, float* __restrict__ ts, const uint32_t* __restrict__ part, int npart) {
+    __shared__ NvRecip rtab[128];
+    __shared__ uint32_t red[kThreads / 64];
+    __shared__ float st_sh;
+    const int64_t gpr = k >> 4;
+    const int64_t total = rows * gpr;
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    uint4 va[kNvDepth], vb[kNvDepth];
 #pragma unroll
-        for (int j = 0; j < kUnroll; ++j) {
-            const int64_t u = base + (int64_t)j * kThreads;
-            if (u < total) v[j] = *reinterpret_cast<const uint4*>(x + x_offset<kContig>(u, upr, ldx));
+    for (int j = 0; j < kNvDepth; ++j) {
+        const int64_t uj = u + j * stride;
+        if (uj < total) nv_load16<kContig>(x, uj, gpr, ldx, va[j], vb[j]);
+    }
+    if (npart > 0) {
+        uint32_t am = 0;
+        for (int i = threadIdx.x; i < npart; i += kThreads) am = max(am, part[i]);
+        for (int off = 32; off > 0; off >>= 1) am = max(am, (uint32_t)__shfl_xor((int)am, off));
+        if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = am;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            uint32_t m = red[0];
+            for (int i = 1; i < kThreads / 64; ++i) m = max(m, red[i]);
+            // s_t = fp32(amax / 2688): the fp64 quotient is correctly rounded, and
+            // rounding it again to fp32 is exact (an 8-bit numerator over 21 * 2^7
+            // is a short dyadic or far from every fp32 rounding midpoint)
+            const float st = (float)((double)__uint_as_float(m << 16) / 2688.0);
+            st_sh = st;
+            if (blockIdx.x == 0) *ts = st;
         }
+    } else if (threadIdx.x == 0) {
+        st_sh = *ts;
+    }
+    __syncthreads();
+    const double st = (double)st_sh;
+    const bool live = st > 0.0;
+    const double inv_st = live ? 1.0 / st : 0.0;
+    if (threadIdx.x < 128) {
+        const uint32_t g = threadIdx.x;
+        rtab[g] = (live && g > 0 && g < 127) ? nv_recip_entry(g, inv_st) : NvRecip{0.f, 0.f};
+    }
+    __syncthreads();
+    const double inv6st = live ? 1.0 / (6.0 * st) : 0.0;
+    const bool fast = inv6st >= 0x1p-126 && inv6st < 0x1p127;
+    const float inv6st32 = fast ? (float)inv6st : 0.0f;
+    for (; u < total; u += kNvDepth * stride) {
 #pragma unroll
-        for (int j = 0; j < kUnroll; ++j) {
-            const int64_t u = base + (int64_t)j * kThreads;
-            if (u < total) {
-                const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
-                uint32_t sg;
-                const uint32_t packed = nv_quant8(w, st, sg);
-                reinterpret_cast<uint32_t*>(codes)[u] = packed;
-                if ((threadIdx.x & 1) == 0) scales[u >> 1] = (uint8_t)sg;
+        for (int j = 0; j < kNvDepth; ++j) {
+            const int64_t uj = u + j * stride;
+            if (uj < total) {
+                const uint32_t w[8] = {va[j].x, va[j].y, va[j].z, va[j].w, vb[j].x, vb[j].y, vb[j].z, vb[j].w};
+                const int64_t un = uj + kNvDepth * stride;      // refill this slot
+                if (un < total) nv_load16<kContig>(x, un, gpr, ldx, va[j], vb[j]);
+                const uint32_t sg = nv_group_scale(amax16_bits(w), inv6st32, inv6st, fast);
+                const uint2 c = nv_codes16(w, sg, st, rtab[sg]);
+                *reinterpret_cast<uint2*>(codes + uj * 8) = c;
+                scales[uj] = (uint8_t)sg;
             }
         }
     }
@@ -227,7 +288,8 @@ __global__ __launch_bounds__(kThreads) void remap_kernel(const uint8_t* __restri
 hipError_t launch_quantize_mx(const uint16_t* x, int64_t rows, int64_t k, int64_t ldx,
                               uint8_t* codes, uint8_t* scales, hipStream_t s) {
     const int64_t units = rows * (k / 8);
-    const unsigned g = grid_for(units, kUnroll);
+    unsigned g = grid_for(units, kMxUnroll);
+    if (g > kMxMaxBlocks) g = kMxMaxBlocks;
     if (ldx == k)
         mx_quantize_kernel<true><<<g, kThreads, 0, s>>>(x, rows, k, ldx, codes, scales);
     else
@@ -238,23 +300,23 @@ hipError_t launch_quantize_mx(const uint16_t* x, int64_t rows, int64_t k, int64_
 hipError_t launch_quantize_nv(const uint16_t* x, int64_t rows, int64_t k, int64_t ldx,
                               uint8_t* codes, uint8_t* scales, float* ts, bool ts_is_input,
                               uint32_t* amax_ws, hipStream_t s) {
-    const int64_t units = rows * (k / 8);
     const bool contig = ldx == k;
+    int npart = 0;
     if (!ts_is_input) {
-        nv_amax_init_kernel<<<1, 1, 0, s>>>(amax_ws);
-        unsigned g = grid_for(units);
-        if (g > 2048) g = 2048;
+        unsigned g = grid_for(rows * (k / 8), kUnroll);
+        if (g > (unsigned)kNvAmaxBlocks) g = kNvAmaxBlocks;
+        npart = (int)g;
         if (contig)
             nv_amax_kernel<true><<<g, kThreads, 0, s>>>(x, rows, k, ldx, amax_ws);
         else
             nv_amax_kernel<false><<<g, kThreads, 0, s>>>(x, rows, k, ldx, amax_ws);
-        nv_tensor_scale_kernel<<<1, 1, 0, s>>>(amax_ws, ts);
     }
-    const unsigned gq = grid_for(units, kUnroll);
+    unsigned gq = grid_for(rows * (k / 16));
+    if (gq > kNvMaxBlocks) gq = kNvMaxBlocks;
     if (contig)
-        nv_quantize_kernel<true><<<gq, kThreads, 0, s>>>(x, rows, k, ldx, codes, scales, ts);
+        nv_quantize_kernel<true><<<gq, kThreads, 0, s>>>(x, rows, k, ldx, codes, scales, ts, amax_ws, npart);
     else
-        nv_quantize_kernel<false><<<gq, kThreads, 0, s>>>(x, rows, k, ldx, codes, scales, ts);
+        nv_quantize_kernel<false><<<gq, kThreads, 0, s>>>(x, rows, k, ldx, codes, scales, ts, amax_ws, npart);
     return hipGetLastError();
 }
 

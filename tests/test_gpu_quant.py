@@ -140,6 +140,27 @@ def test_nv_quantize_power_of_two_scale_ties():
     _check_nv(bits, s_t=2.0 ** -3)
 
 
+def test_nv_quantize_group_scale_midpoints():
+    """Group maxima whose quotient amax_g / (6 s_t) is exactly an E4M3 rounding
+    midpoint (normal and subnormal, even and odd neighbours): with s_t = 2^-3,
+    amax_g = 0.75 m is a bf16 value for every midpoint m.  Both tie directions
+    and the neighbours just above and below each midpoint are covered."""
+    pos = OF.E4M3_POS_F64
+    mids = (pos[:-1] + pos[1:]) / 2
+    rng = np.random.default_rng(11)
+    centre = W.bf16_bits(W.to_bf16(0.75 * mids)).astype(np.int64)      # exact: 0.75 m has <= 7 bits
+    rows = []
+    for c in centre:
+        for amax_bits in (c - 1, c, c + 1):                            # bf16 neighbours of the tie
+            amax = OF.bf16_bits_to_f64(np.array([amax_bits], np.uint16))[0]
+            g = W.bf16_bits(W.to_bf16(rng.uniform(-1, 1, 16) * amax))
+            g[rng.integers(16)] = amax_bits | (0x8000 if rng.random() < 0.5 else 0)
+            rows.append(g)
+    flat = np.concatenate(rows)
+    bits = np.concatenate([flat, np.zeros((-flat.size) % 256, np.uint16)]).reshape(-1, 256).astype(np.uint16)
+    _check_nv(bits, s_t=2.0 ** -3)
+
+
 @pytest.mark.parametrize("fmt", ["mx", "nv"])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_dequant_bit_exact(fmt, dtype):
