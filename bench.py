@@ -1,27 +1,45 @@
 """Benchmark of the block-scaled FP4 hot path on one MI355X.
 
-One step runs every stage of the path once on seeded synthetic inputs that are
-already resident in HBM:
-  quantize  MX and NV quantization of the 4096x4096 weight and 2048x4096
-            activation of the single-linear workload, the lossless MX->NV remap
-            and an MX dequantize of the weight;
+One step runs every stage of the path once, on seeded synthetic inputs that
+are already resident in HBM:
+  quantize  MX and NV quantization of the 4096x4096 weight and the 2048x4096
+            activation of the single-linear workload (NV with the tensor scale
+            computed, and for the activation also with a calibrated one), the
+            lossless MX->NV remap and an MX dequantize of the weight;
   gemm      the 4096^3 W4A4 MXFP4 GEMM (activations quantized on the fly,
             weights pre-quantized, fp32 accumulation, bf16 output);
   moe       the MoE layer at hidden 4096 (384 experts, top-6, intermediate
-            2048, 8192 tokens, MXFP4 weights and activations).
-Each stage is bracketed by HIP events on the stream the kernels run on.  The
-input of every HBM-bound stage rotates through copies whose total exceeds the
-256 MB last-level cache, so each launch reads HBM, not cache.
+            2048, 8192 tokens, MXFP4 weights and activations), and the NVFP4
+            MoE layer at hidden 7168 (intermediate 3072) on a decode batch of
+            64 tokens.
+The input of every HBM-bound stage rotates through copies whose total exceeds
+the 256 MB last-level cache, so each launch reads HBM, not cache.
+
+Timing.  W warmup steps, then K steps of the whole path back to back, with no
+markers in between; ms_per_step is their wall time between two device
+synchronizations.  Then each stage is launched K times back to back between
+two HIP events recorded on its stream, behind a spin kernel that keeps the
+device busy while the host queues the launches (so host launch latency never
+shows): the stage's duration is the event interval over K.  An event marker
+costs the device about 6 us, so it is kept out of these intervals.  For the
+MoE stages a second pass records the entry point's stage events between its
+kernels, which gives each kernel's duration (each interval then also holds one
+marker, small against these kernels).
 
 Output: one JSON line.  `value` is the W4A4 GEMM throughput (TFLOP/s), the
-first quantity of the metric; the quantize GB/s and MoE tokens/s are in
-`components`; `roofline` describes the kernel with the largest share of the
-step time and `rooflines` every timed kernel.  `cpu_baseline` times the CPU
-oracle on a bounded sample of the GEMM workload.
+first quantity of the metric; the quantize GB/s and the MoE tokens/s are in
+`components`.  `roofline` describes the kernel with the largest share of the
+step time (algorithmic work per launch over its event-measured duration) and
+`rooflines` every timed stage and MoE kernel.  `traffic` comes from
+rocprofv3 FETCH_SIZE / WRITE_SIZE counters recorded in profiles/traffic.json
+(written by profile_counters.sh), scaled by what the same counters read for a
+plain copy of known size; it is null when the kernel sources changed since.
+`cpu_baseline` times the CPU oracle on a bounded sample of the GEMM workload.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -34,6 +52,10 @@ PEAK_HBM_GBS = 8000.0
 PEAK_FP4_TFLOPS = 10100.0
 PEAK_BF16_TFLOPS = 2500.0
 MALL_BYTES = 256 << 20
+HERE = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(HERE, "profiles", "traffic.json")
+MOE_KERNELS = ("quantize_x", "routing", "gate_up", "down", "combine")
+SPACER_CYCLES = 4_000_000
 
 
 def parse():
@@ -42,25 +64,63 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--no-moe", action="store_true", help="skip the MoE stage (profiling runs)")
+    p.add_argument("--no-moe", action="store_true", help="skip the MoE stages")
     p.add_argument("--only", default="", help="comma list of stages to run (profiling runs)")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run a plain 256 MiB device copy per step (counter calibration runs)")
     return p.parse_args()
 
 
+def source_digest():
+    """Digest of the kernel sources, so recorded counters can be matched to the
+    code they were taken on."""
+    h = hashlib.sha256()
+    csrc = os.path.join(HERE, "block_scaled_fp4_mx_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
 class Stage:
-    def __init__(self, name, launch, bound, work, unit_work, kernel=None, per_launch=1):
+    def __init__(self, name, launch, bound, work, per_unit, kernel, moe=None):
         self.name, self.launch, self.bound = name, launch, bound
         self.work = work            # algorithmic bytes (hbm) or flops (mfma) per launch
-        self.unit_work = unit_work  # description of the per-unit figure
-        self.kernel = kernel or name
+        self.per_unit = per_unit    # the per-unit figure the work is built from
+        self.kernel = kernel        # kernel name(s) as rocprofv3 reports them
+        self.moe = moe              # MoE: dict with the stage events and per-kernel work
         self.times = []             # ms per launch
+
+
+def roofline_entry(bound, work, ms, per_unit, kernel, extra=None):
+    if bound == "hbm":
+        ach = work / (ms * 1e-3) / 1e9
+        peak, unit = PEAK_HBM_GBS, "GB/s"
+    else:
+        ach = work / (ms * 1e-3) / 1e12
+        peak, unit = (PEAK_BF16_TFLOPS, "TFLOP/s") if bound == "mfma_bf16" else (PEAK_FP4_TFLOPS, "TFLOP/s")
+    e = dict(bound="mfma" if bound.startswith("mfma") else bound, achieved=round(ach, 1), peak=peak, unit=unit,
+             frac=round(ach / peak, 4), traffic=None, avg_us=round(ms * 1e3, 2), work_per_launch=work,
+             per_unit=per_unit, kernel=kernel)
+    if extra:
+        e.update(extra)
+    return e
+
+
+def load_traffic():
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    return t if t.get("source_digest") == source_digest() else None
 
 
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
-                          "n_gpus_requested": args.gpus}))
+        print(json.dumps({"error": "this benchmark runs on one GPU; multi-GPU runs are not part of it "
+                                   "(--gpus must be 1)", "n_gpus_requested": args.gpus}))
         sys.exit(2)
 
     import torch
@@ -75,30 +135,28 @@ def main():
         n = max(2, int(np.ceil(1.5 * MALL_BYTES / per_copy_bytes)))
         return [t.clone() for _ in range(n)]
 
-    # ---------------------------------------------------------------- inputs
-    wl2 = W.workload2()
-    W2 = wl2.W.to(dev)
-    A2 = wl2.A.to(dev)
-    pair_bytes = (W2.numel() + A2.numel()) * 2
-    nrot2 = max(2, int(np.ceil(1.5 * MALL_BYTES / pair_bytes)))
-    W2s = [W2.clone() for _ in range(nrot2)]
-    A2s = [A2.clone() for _ in range(nrot2)]
-
     def qbufs(x, blk):
         r, k = x.shape
         return (torch.empty((r, k // 2), dtype=torch.uint8, device=dev),
                 torch.empty((r, k // blk), dtype=torch.uint8, device=dev))
 
+    # ---------------------------------------------------------------- inputs
+    wl2 = W.workload2()
+    W2, A2 = wl2.W.to(dev), wl2.A.to(dev)
+    pair_bytes = (W2.numel() + A2.numel()) * 2
+    nrot2 = max(2, int(np.ceil(1.5 * MALL_BYTES / pair_bytes)))
+    W2s = [W2.clone() for _ in range(nrot2)]
+    A2s = [A2.clone() for _ in range(nrot2)]
     W2mx, A2mx = qbufs(W2, 32), qbufs(A2, 32)
     W2nv, A2nv = qbufs(W2, 16), qbufs(A2, 16)
     tsW = torch.zeros(1, dtype=torch.float32, device=dev)
     tsA = torch.zeros(1, dtype=torch.float32, device=dev)
+    tsA_cal = (A2.abs().max().float() / 2688.0).reshape(1).contiguous()   # a calibrated activation scale
     nvws = torch.empty(F.fp4_quantize_nv_workspace_bytes(4096, 4096), dtype=torch.uint8, device=dev)
     rem_s = torch.empty((4096, 4096 // 16), dtype=torch.uint8, device=dev)
     rem_ts = torch.zeros(1, dtype=torch.float32, device=dev)
     rem_n = torch.zeros(1, dtype=torch.int32, device=dev)
     deq = torch.empty((4096, 4096), dtype=torch.bfloat16, device=dev)
-    # pre-quantized weight codes rotate for the remap and dequant inputs
     W2mx_rot = []
     for i in range(nrot2):
         c, s = qbufs(W2, 32)
@@ -120,34 +178,38 @@ def main():
     def cur(lst):
         return lst[st["i"] % len(lst)]
 
-    M2 = 4096 * 4096
-    M2a = 2048 * 4096
+    M2, M2a = 4096 * 4096, 2048 * 4096
+    MXB, NVB = 2 + 0.5 + 1 / 32, 2 + 0.5 + 1 / 16
     stages = [
-        Stage("quantize_mx_W", lambda: F.fp4_quantize_mx(cur(W2s), *W2mx), "hbm", M2 * (2 + 0.5 + 1 / 32),
-              "2.53125 B/elem (2 bf16 in, 0.5 codes, 1/32 scale)", "mx_quantize_kernel"),
-        Stage("quantize_mx_A", lambda: F.fp4_quantize_mx(cur(A2s), *A2mx), "hbm", M2a * (2 + 0.5 + 1 / 32),
+        Stage("quantize_mx_W", lambda: F.fp4_quantize_mx(cur(W2s), *W2mx), "hbm", M2 * MXB,
+              "2.53125 B/elem (2 bf16 in, 0.5 codes, 1/32 scale out)", "mx_quantize_kernel"),
+        Stage("quantize_mx_A", lambda: F.fp4_quantize_mx(cur(A2s), *A2mx), "hbm", M2a * MXB,
               "2.53125 B/elem", "mx_quantize_kernel"),
-        Stage("quantize_nv_W", lambda: F.fp4_quantize_nv(cur(W2s), *W2nv, tsW, False, nvws), "hbm",
-              M2 * (2 + 0.5 + 1 / 16), "2.5625 B/elem (2 in, 0.5 codes, 1/16 scale; tensor amax re-read not counted)",
-              "nv_amax+nv_quantize"),
-        Stage("quantize_nv_A", lambda: F.fp4_quantize_nv(cur(A2s), *A2nv, tsA, False, nvws), "hbm",
-              M2a * (2 + 0.5 + 1 / 16), "2.5625 B/elem", "nv_amax+nv_quantize"),
+        Stage("quantize_nv_W", lambda: F.fp4_quantize_nv(cur(W2s), *W2nv, tsW, False, nvws), "hbm", M2 * NVB,
+              "2.5625 B/elem (2 in, 0.5 codes, 1/16 scale out); the tensor-amax read is not counted",
+              "nv_amax_kernel + nv_quantize_kernel"),
+        Stage("quantize_nv_A", lambda: F.fp4_quantize_nv(cur(A2s), *A2nv, tsA, False, nvws), "hbm", M2a * NVB,
+              "2.5625 B/elem; the tensor-amax read is not counted", "nv_amax_kernel + nv_quantize_kernel"),
+        Stage("quantize_nv_A_calibrated", lambda: F.fp4_quantize_nv(cur(A2s), *A2nv, tsA_cal, True, nvws), "hbm",
+              M2a * NVB, "2.5625 B/elem (calibrated s_t: one pass)", "nv_quantize_kernel"),
         Stage("remap_W", lambda: F.fp4_remap_mx_to_nv(cur(W2mx_rot)[0], cur(W2mx_rot)[1], rem_s, rem_ts, rem_n),
-              "hbm", M2 * (1 / 32 + 1 / 16), "0.09375 B/elem (scale bytes in and out)", "remap kernels"),
+              "hbm", M2 * (1 / 32 + 1 / 16), "0.09375 B/elem (scale bytes in and out)",
+              "remap_max_kernel + remap_kernel"),
         Stage("dequant_mx_W", lambda: F.fp4_dequant(F.FMT_MX, cur(W2mx_rot)[0], cur(W2mx_rot)[1], None, deq), "hbm",
-              M2 * (0.5 + 1 / 32 + 2), "2.53125 B/elem (codes+scale in, bf16 out)", "dequant_kernel"),
-        Stage("gemm_quantize_A", lambda: F.fp4_quantize_mx(cur(A3s), *A3q), "hbm", 4096 * 4096 * (2 + 0.5 + 1 / 32),
+              M2 * (0.5 + 1 / 32 + 2), "2.53125 B/elem (codes + scale in, bf16 out)", "dequant_kernel"),
+        Stage("gemm_quantize_A", lambda: F.fp4_quantize_mx(cur(A3s), *A3q), "hbm", 4096 * 4096 * MXB,
               "2.53125 B/elem", "mx_quantize_kernel"),
         Stage("gemm_mx_4096", lambda: F.fp4_gemm(F.FMT_MX, A3q[0], A3q[1], W3q[0], W3q[1], C3), "mfma",
-              2.0 * 4096 ** 3, "2*M*N*K flop", "gemm_mx_kernel"),
+              2.0 * 4096 ** 3, "2*M*N*K flop", "gemm_mx_256_kernel"),
     ]
-
-    moe = None
     if not args.no_moe:
-        moe = build_moe(torch, F, W, dev)
-        if moe is not None:
-            stages.append(Stage("moe_h4096", moe["launch"], moe["bound"], moe["work"], moe["unit"], "moe (all kernels)"))
-
+        stages.append(build_moe_h4096(torch, F, W, dev))
+        stages.append(build_moe_decode(torch, F, W, dev))
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        stages.append(Stage("copy_256MiB", lambda: dst.copy_(src), "hbm", 2.0 * (256 << 20),
+                            "256 MiB read + 256 MiB written", "copy"))
     if args.only:
         keep = set(args.only.split(","))
         stages = [s for s in stages if s.name in keep]
@@ -158,45 +220,76 @@ def main():
         st["i"] += 1
     torch.cuda.synchronize()
 
-    # one event pair per stage per step; the queue stays full between steps, so
-    # no event interval includes host launch latency
-    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in stages]
-           for _ in range(args.steps)]
+    # timed steps: the whole path, back to back, with no markers in between
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for k in range(args.steps):
-        for s, (e0, e1) in zip(stages, evs[k]):
-            e0.record(stream)
+    for _ in range(args.steps):
+        for s in stages:
             s.launch()
-            e1.record(stream)
         st["i"] += 1
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    for k in range(args.steps):
-        for s, (e0, e1) in zip(stages, evs[k]):
-            s.times.append(e0.elapsed_time(e1))
     ms_per_step = wall * 1e3 / args.steps
 
-    rooflines = {}
+    # per-stage durations: `steps` launches of the stage between two events on
+    # its stream, queued behind a spin kernel so the host's launch rate never
+    # leaves the device idle between them
+    def spacer():
+        torch.cuda._sleep(SPACER_CYCLES)
+
+    moe_marks = {}
     for s in stages:
-        avg_ms = float(np.mean(s.times))
-        if s.bound == "hbm":
-            ach = s.work / (avg_ms * 1e-3) / 1e9
-            rooflines[s.name] = dict(bound="hbm", achieved=round(ach, 1), peak=PEAK_HBM_GBS, unit="GB/s",
-                                     frac=round(ach / PEAK_HBM_GBS, 4), traffic=None, avg_us=round(avg_ms * 1e3, 2),
-                                     best_us=round(min(s.times) * 1e3, 2), work_per_launch=s.work,
-                                     per_unit=s.unit_work, kernel=s.kernel)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        spacer()
+        e0.record(stream)
+        for _ in range(args.steps):
+            s.launch()
+            st["i"] += 1
+        e1.record(stream)
+        torch.cuda.synchronize()
+        s.times = [e0.elapsed_time(e1) / args.steps]
+        if s.moe:
+            # the MoE entry point records its stage events between its kernels
+            evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+            for row in evs:                 # materialize the events the library records
+                for e in row:
+                    e.record(stream)
+            spacer()
+            for k in range(args.steps):
+                s.moe["set_events"]([e.cuda_event for e in evs[k]])
+                s.launch()
+            torch.cuda.synchronize()
+            s.moe["set_events"]([None] * 6)
+            moe_marks[s.name] = evs
+
+    traffic = load_traffic()
+    rooflines = {}
+    kernel_rows = []                        # (ms, name, entry) for the dominant-kernel choice
+    for s in stages:
+        ms = float(np.mean(s.times))
+        e = roofline_entry(s.bound, s.work, ms, s.per_unit, s.kernel)
+        if s.moe:
+            e["kernels"] = {}
+            evs = moe_marks[s.name]
+            for i, kname in enumerate(MOE_KERNELS):
+                kms = float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps)]))
+                bound, work, unit = s.moe["work"][kname]
+                ke = roofline_entry(bound, work, kms, unit, s.moe["kernel_names"][kname])
+                e["kernels"][kname] = ke
+                kernel_rows.append((kms, f"{s.name}.{kname}", ke))
         else:
-            peak = s.bound == "mfma_bf16" and PEAK_BF16_TFLOPS or PEAK_FP4_TFLOPS
-            ach = s.work / (avg_ms * 1e-3) / 1e12
-            rooflines[s.name] = dict(bound="mfma", achieved=round(ach, 1), peak=peak, unit="TFLOP/s",
-                                     frac=round(ach / peak, 4), traffic=None, avg_us=round(avg_ms * 1e3, 2),
-                                     best_us=round(min(s.times) * 1e3, 2), work_per_launch=s.work,
-                                     per_unit=s.unit_work, kernel=s.kernel)
-    dom = max(stages, key=lambda s: np.mean(s.times))
+            kernel_rows.append((ms, s.name, e))
+        rooflines[s.name] = e
+    if traffic:
+        for _, name, e in kernel_rows:
+            t = traffic["kernels"].get(name)
+            if t is not None:
+                e["traffic"] = t["bytes_per_launch"]
+
+    dom_ms, dom_name, dom = max(kernel_rows, key=lambda r: r[0])
+    comps = {}
     gemm = rooflines.get("gemm_mx_4096")
     value = gemm["achieved"] if gemm else None
-    comps = {}
     if gemm:
         comps["gemm_tflops"] = gemm["achieved"]
         comps["gemm_frac_fp4_peak"] = gemm["frac"]
@@ -204,12 +297,19 @@ def main():
         if qa:
             comps["gemm_with_onthefly_quantize_tflops"] = round(
                 2.0 * 4096 ** 3 / ((gemm["avg_us"] + qa["avg_us"]) * 1e-6) / 1e12, 1)
-    for n in ("quantize_mx_W", "quantize_mx_A", "quantize_nv_W", "quantize_nv_A"):
+    for n in ("quantize_mx_W", "quantize_mx_A", "quantize_nv_W", "quantize_nv_A", "quantize_nv_A_calibrated",
+              "gemm_quantize_A"):
         if n in rooflines:
             comps[n + "_GBps"] = rooflines[n]["achieved"]
-    if moe is not None and "moe_h4096" in rooflines:
-        comps["moe_tokens_per_s"] = round(8192 / (rooflines["moe_h4096"]["avg_us"] * 1e-6), 1)
-        comps["moe_active_experts"] = moe["active"]
+    if "moe_h4096" in rooflines:
+        m = rooflines["moe_h4096"]
+        comps["moe_h4096_tokens_per_s"] = round(8192 / (m["avg_us"] * 1e-6), 1)
+        comps["moe_h4096_tflops"] = m["achieved"]
+    if "moe_h7168_decode64" in rooflines:
+        m = rooflines["moe_h7168_decode64"]
+        comps["moe_h7168_decode_tokens_per_s"] = round(64 / (m["avg_us"] * 1e-6), 1)
+        comps["moe_h7168_decode_weight_GBps"] = m["achieved"]
+        comps["moe_h7168_decode_frac_hbm"] = m["frac"]
     out = {
         "metric": METRIC,
         "value": value,
@@ -223,13 +323,14 @@ def main():
         "vs_baseline": None,
         "dtype": "e2m1",
         "data": "synthetic",
-        "config": {"workload": "linear 4096x4096 W + 2048x4096 A quantize/remap/dequant; "
-                               "W4A4 MXFP4 GEMM 4096^3 (bf16 out, fp32 accumulate); "
-                               "MoE hidden 4096, 384 experts, top-6, inter 2048, 8192 tokens (MXFP4)",
-                   "accumulate": "fp32"},
+        "config": {"workload": "W4A4 MXFP4 GEMM M=N=K=4096 (bf16 out, fp32 accumulate) for value; per step also "
+                               "MX/NV quantize of linear 4096x4096 W and 2048x4096 A, MX->NV remap, MX dequant, "
+                               "MoE hidden 4096 (384 experts, top-6, inter 2048, 8192 tokens, MXFP4) and "
+                               "NVFP4 MoE hidden 7168 (inter 3072, 64 decode tokens)",
+                   "accumulate": "fp32", "traffic_source": "profiles/traffic.json" if traffic else None},
         "components": comps,
-        "roofline": {k: v for k, v in rooflines[dom.name].items()
-                     if k in ("bound", "achieved", "peak", "unit", "frac", "traffic")} | {"kernel": dom.name},
+        "roofline": {k: v for k, v in dom.items() if k in ("bound", "achieved", "peak", "unit", "frac", "traffic")}
+                    | {"kernel": dom_name},
         "rooflines": rooflines,
     }
     if not args.no_cpu_baseline:
@@ -237,14 +338,54 @@ def main():
     print(json.dumps(out))
 
 
-def build_moe(torch, F, W, dev):
-    """MoE workload at hidden 4096; returns None while the library reports the
-    MoE entry point as unsupported."""
+def moe_stage(torch, F, name, fmt, m, E, w13c, w13s, w2c, w2s, w13ts, w2ts, act, out, ws, weight_bytes, flops_gu,
+              flops_dn, bound):
+    """A MoE stage: one fp4_moe_grouped_gemm call with stage events."""
+    dbg = F.MoeDebug()
+    X = m.X.to("cuda")
+    ids = torch.from_numpy(m.ids).to("cuda")
+    wts = torch.from_numpy(m.weights).to("cuda")
+    T, H = X.shape
+    I, k = m.inter, m.ids.shape[1]
+
+    def set_events(handles):
+        for i, h in enumerate(handles):
+            dbg.stage_events[i] = h
+
+    def launch():
+        F.fp4_moe_grouped_gemm(fmt, X, ids, wts, E, I, w13c, w13s, w2c, w2s, out, ws, w13_tensor_scales=w13ts,
+                               w2_tensor_scales=w2ts, act_tensor_scales=act, debug=dbg)
+
+    S = T * k
+    blk = 32 if fmt == F.FMT_MX else 16
+    qb = 2 + 0.5 + 1 / blk
+    work = {
+        "quantize_x": ("hbm", T * H * qb, f"{qb} B/elem of x"),
+        "routing": ("hbm", S * 4 * 4, "16 B per slot (ids in, perm/slot_pos/placement out)"),
+        "gate_up": (bound, flops_gu, "4*H*I flop per routed slot (g and u)"),
+        "down": (bound, flops_dn, "2*H*I flop per routed slot"),
+        "combine": ("hbm", S * H * 4 + T * H * 2, "4 B per slot per hidden column in, 2 B per token column out"),
+    }
+    names = {"quantize_x": "mx_quantize_kernel" if fmt == F.FMT_MX else "nv_quantize_kernel",
+             "routing": "route_count_kernel + route_scan_kernel + route_place_kernel",
+             "gate_up": "moe_gate_up_mx256_kernel" if fmt == F.FMT_MX else "moe_gate_up_kernel<1>",
+             "down": "moe_down_mx256_kernel" if fmt == F.FMT_MX else "moe_down_kernel<1>",
+             "combine": "combine_kernel"}
+    if bound == "hbm":
+        # decode: the expert weights dominate the bytes of both GEMMs
+        work["gate_up"] = ("hbm", weight_bytes * 2 / 3, "active experts' w1/w3 codes + scales")
+        work["down"] = ("hbm", weight_bytes / 3, "active experts' w2 codes + scales")
+        total_work, unit = weight_bytes, "active experts' weight bytes (codes + scales) per launch"
+    else:
+        total_work, unit = flops_gu + flops_dn, "6*H*I flop per routed slot"
+    return Stage(name, launch, bound, total_work, unit, "MoE (all kernels)",
+                 moe={"set_events": set_events, "work": work, "kernel_names": names})
+
+
+def build_moe_h4096(torch, F, W, dev):
+    """MXFP4 MoE layer at hidden 4096 (8192 tokens)."""
     m = W.moe_workload(4)
-    T, H, I, E = 8192, m.hidden, m.inter, m.num_experts
-    X = m.X.to(dev)
-    ids = torch.from_numpy(m.ids).to(dev)
-    wts = torch.from_numpy(m.weights).to(dev)
+    T, H, I, E = 8192, m.hidden, m.inter, 384
     active = sorted(set(m.ids.ravel().tolist()))
     w13c = torch.zeros((E, 2 * I, H // 2), dtype=torch.uint8, device=dev)
     w13s = torch.full((E, 2 * I, H // 32), 127, dtype=torch.uint8, device=dev)
@@ -256,17 +397,48 @@ def build_moe(torch, F, W, dev):
             F.fp4_quantize_mx(b, w2c[e], w2s[e])
     out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     ws = torch.empty(F.fp4_moe_workspace_bytes(F.FMT_MX, T, H, 6, E, I), dtype=torch.uint8, device=dev)
-    launch = lambda: F.fp4_moe_grouped_gemm(F.FMT_MX, X, ids, wts, E, I, w13c, w13s, w2c, w2s, out, ws)
-    try:
-        launch()
-        torch.cuda.synchronize()
-    except F.Fp4Error as e:
-        if e.status == -4:
-            return None
-        raise
-    counts = np.bincount(m.ids.ravel(), minlength=E)
-    flops = float(6 * counts.sum() * H * I)
-    return dict(launch=launch, bound="mfma", work=flops, unit="6*H*I flop per routed slot", active=len(active))
+    S = int(m.ids.size)
+    per_expert = 3 * H * I * (0.5 + 1 / 32)
+    return moe_stage(torch, F, "moe_h4096", F.FMT_MX, m, E, w13c, w13s, w2c, w2s, None, None, None, out, ws,
+                     len(active) * per_expert, 4.0 * S * H * I, 2.0 * S * H * I, "mfma")
+
+
+def build_moe_decode(torch, F, W, dev):
+    """NVFP4 MoE layer at hidden 7168 on a decode batch of 64 tokens: the
+    active experts' weights stream from HBM.  The activation tensor scales are
+    calibrated: s_x from amax(x), s_h from amax(h) of one calibration call."""
+    m = W.moe_workload(5, 64)
+    T, H, I, E = 64, m.hidden, m.inter, 384
+    active = sorted(set(m.ids.ravel().tolist()))
+    w13c = torch.zeros((E, 2 * I, H // 2), dtype=torch.uint8, device=dev)
+    w13s = torch.zeros((E, 2 * I, H // 16), dtype=torch.uint8, device=dev)
+    w2c = torch.zeros((E, H, I // 2), dtype=torch.uint8, device=dev)
+    w2s = torch.zeros((E, H, I // 16), dtype=torch.uint8, device=dev)
+    w13ts = torch.zeros(E, dtype=torch.float32, device=dev)
+    w2ts = torch.zeros(E, dtype=torch.float32, device=dev)
+    nvws = torch.empty(F.fp4_quantize_nv_workspace_bytes(1, 1), dtype=torch.uint8, device=dev)
+    for e, a, b in W.expert_weights_device(5, E, H, I, dev):
+        if e in active:
+            F.fp4_quantize_nv(a, w13c[e], w13s[e], w13ts[e:e + 1], False, nvws)
+            F.fp4_quantize_nv(b, w2c[e], w2s[e], w2ts[e:e + 1], False, nvws)
+    X = m.X.to(dev)
+    act = torch.tensor([float(X.abs().max()) / 2688.0, 1.0], dtype=torch.float32, device=dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(F.fp4_moe_workspace_bytes(F.FMT_NV, T, H, 6, E, I), dtype=torch.uint8, device=dev)
+    S = int(m.ids.size)
+    # calibration call: amax of h over this batch
+    h = torch.empty((S, I), dtype=torch.bfloat16, device=dev)
+    dbg = F.MoeDebug()
+    dbg.h_bf16 = h.data_ptr()
+    F.fp4_moe_grouped_gemm(F.FMT_NV, X, torch.from_numpy(m.ids).to(dev), torch.from_numpy(m.weights).to(dev), E, I,
+                           w13c, w13s, w2c, w2s, out, ws, w13_tensor_scales=w13ts, w2_tensor_scales=w2ts,
+                           act_tensor_scales=act, debug=dbg)
+    torch.cuda.synchronize()
+    act[1] = float(h.float().abs().max()) / 2688.0
+    del h
+    per_expert = 3 * H * I * (0.5 + 1 / 16)
+    return moe_stage(torch, F, "moe_h7168_decode64", F.FMT_NV, m, E, w13c, w13s, w2c, w2s, w13ts, w2ts, act, out, ws,
+                     len(active) * per_expert, 4.0 * S * H * I, 2.0 * S * H * I, "hbm")
 
 
 def cpu_baseline():

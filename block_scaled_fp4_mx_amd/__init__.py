@@ -31,7 +31,7 @@ class MoeDebug(_c.Structure):
     """Mirror of struct fp4_moe_debug (all members nullable device pointers)."""
     _fields_ = [("x_codes", _vp), ("x_scales", _vp), ("counts", _vp), ("offsets", _vp), ("perm", _vp), ("gate_up", _vp),
                 ("h_bf16", _vp), ("h_codes", _vp), ("h_scales", _vp), ("y", _vp),
-                ("gate_up_in", _vp), ("h_codes_in", _vp), ("h_scales_in", _vp)]
+                ("gate_up_in", _vp), ("h_codes_in", _vp), ("h_scales_in", _vp), ("stage_events", _vp * 6)]
 
 
 _SIGS = {

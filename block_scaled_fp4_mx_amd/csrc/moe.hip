@@ -665,11 +665,15 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t s) {
     const int64_t T = a.tokens, H = a.hidden, I = a.inter, S = T * a.topk;
     const int E = a.num_experts;
 
+    auto mark = [&](int i) {
+        return a.dbg.stage_events[i] ? hipEventRecord(static_cast<hipEvent_t>(a.dbg.stage_events[i]), s) : hipSuccess;
+    };
+    if (hipError_t e0 = mark(0)) return e0;
     // 1. quantize X
     hipError_t err = a.fmt == FP4_FMT_MX
                          ? launch_quantize_mx(a.x, T, H, H, xc, xs, s)
                          : launch_quantize_nv(a.x, T, H, H, xc, xs, const_cast<float*>(a.act_ts), true, nullptr, s);
-    if (err != hipSuccess) return err;
+    if (err != hipSuccess || (err = mark(1)) != hipSuccess) return err;
     // 2. routing metadata
     route_count_kernel<<<(unsigned)L.nblk, kRouteSlots, 0, s>>>(a.ids, S, E, blockbase);
     // MX with hidden and inter multiples of 512: 256-row LDS-staged tiles
@@ -678,7 +682,7 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t s) {
                                          tiled ? kTileM : kBM);
     route_place_kernel<<<(unsigned)L.nblk, kRouteSlots, (size_t)E * (kRouteSlots / 32) * 4, s>>>(a.ids, S, E, blockbase, perm,
                                                                                   slot_pos);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if ((err = hipGetLastError()) != hipSuccess || (err = mark(2)) != hipSuccess) return err;
 
     GemmParams p{};
     p.fmt = a.fmt;
@@ -709,22 +713,23 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t s) {
         const dim3 g_gu((unsigned)(I / kGu2Cols), (unsigned)L.max_tiles);
         const dim3 g_dn((unsigned)(H / kTileN), (unsigned)L.max_tiles);
         moe_gate_up_mx256_kernel<<<g_gu, kTileThreads, 0, s>>>(p);
+        if ((err = hipGetLastError()) != hipSuccess || (err = mark(3)) != hipSuccess) return err;
         moe_down_mx256_kernel<<<g_dn, kTileThreads, 0, s>>>(p);
+        if ((err = hipGetLastError()) != hipSuccess || (err = mark(4)) != hipSuccess) return err;
     } else {
         const dim3 g_gu((unsigned)(I / kGuCols), (unsigned)L.max_tiles);
         const dim3 g_dn((unsigned)(H / kDnCols), (unsigned)L.max_tiles);
-        if (a.fmt == FP4_FMT_MX) {
-            moe_gate_up_kernel<FP4_FMT_MX><<<g_gu, kThreads, 0, s>>>(p);
-            moe_down_kernel<FP4_FMT_MX><<<g_dn, kThreads, 0, s>>>(p);
-        } else {
-            moe_gate_up_kernel<FP4_FMT_NV><<<g_gu, kThreads, 0, s>>>(p);
-            moe_down_kernel<FP4_FMT_NV><<<g_dn, kThreads, 0, s>>>(p);
-        }
+        if (a.fmt == FP4_FMT_MX) moe_gate_up_kernel<FP4_FMT_MX><<<g_gu, kThreads, 0, s>>>(p);
+        else moe_gate_up_kernel<FP4_FMT_NV><<<g_gu, kThreads, 0, s>>>(p);
+        if ((err = hipGetLastError()) != hipSuccess || (err = mark(3)) != hipSuccess) return err;
+        if (a.fmt == FP4_FMT_MX) moe_down_kernel<FP4_FMT_MX><<<g_dn, kThreads, 0, s>>>(p);
+        else moe_down_kernel<FP4_FMT_NV><<<g_dn, kThreads, 0, s>>>(p);
+        if ((err = hipGetLastError()) != hipSuccess || (err = mark(4)) != hipSuccess) return err;
     }
     // 5. weighted combine
     combine_kernel<<<stream_grid(T * H / 4), kThreads, 0, s>>>(reinterpret_cast<const float4*>(ybuf), a.ids, a.topk, E,
                                                                  T, H / 4, reinterpret_cast<uint2*>(a.out));
-    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if ((err = hipGetLastError()) != hipSuccess || (err = mark(5)) != hipSuccess) return err;
     const int bx = a.fmt == FP4_FMT_MX ? 32 : 16;
     if (a.dbg.x_codes &&
         (err = hipMemcpyAsync(a.dbg.x_codes, xc, (size_t)(T * H / 2), hipMemcpyDeviceToDevice, s)))

@@ -232,30 +232,42 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(
 }
 
 // ------------------------------------------------------------------ MX -> NV remap
-// Pass 1 reduces the largest scale byte into *n_inexact (used as scratch);
-// pass 2 turns it into s_t = 2^(E_max - 8) and clears the counter; pass 3 writes
+// Pass 1 (one workgroup): the largest scale byte E_max + 127 over the tensor,
+// s_t = 2^(E_max - 8), and the inexact-block counter cleared.  Pass 2 writes
 // both E4M3 group scales of every block and counts blocks that lose precision.
-__global__ void remap_init_kernel(int32_t* n) { *n = 0; }
+constexpr int kRemapMaxThreads = 1024;
 
-__global__ __launch_bounds__(kThreads) void remap_max_kernel(const uint8_t* __restrict__ s, int64_t nb,
-                                                             int32_t* mx) {
+__global__ __launch_bounds__(kRemapMaxThreads) void remap_max_kernel(const uint8_t* __restrict__ s, int64_t nb,
+                                                                     float* __restrict__ ts,
+                                                                     int32_t* __restrict__ n_inexact) {
     uint32_t m = 0;
-    const int64_t stride = (int64_t)gridDim.x * kThreads;
-    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nb; i += stride) m = max(m, (uint32_t)s[i]);
+    const int64_t n16 = nb >> 4;
+    const uint4* s16 = reinterpret_cast<const uint4*>(s);
+    for (int64_t i = threadIdx.x; i < n16; i += 4 * kRemapMaxThreads) {
+        uint4 v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t q = i + (int64_t)j * kRemapMaxThreads;
+            v[j] = q < n16 ? s16[q] : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                m = max(m, max(max(w[t] & 0xFFu, (w[t] >> 8) & 0xFFu), max((w[t] >> 16) & 0xFFu, w[t] >> 24)));
+        }
+    }
+    for (int64_t i = (n16 << 4) + threadIdx.x; i < nb; i += kRemapMaxThreads) m = max(m, (uint32_t)s[i]);
     for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
-    __shared__ uint32_t red[kThreads / 64];
+    __shared__ uint32_t red[kRemapMaxThreads / 64];
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
     __syncthreads();
     if (threadIdx.x == 0) {
-        for (int i = 1; i < kThreads / 64; ++i) m = max(m, red[i]);
-        atomicMax(mx, (int32_t)m);
+        for (int i = 0; i < kRemapMaxThreads / 64; ++i) m = max(m, red[i]);
+        *ts = ldexpf(1.0f, (int)m - 127 - 8);    // 2^-135 .. 2^119; below 2^-126 a subnormal
+        *n_inexact = 0;
     }
-}
-
-__global__ void remap_scale_kernel(int32_t* n, float* ts) {
-    const int emax = *n - 127;
-    *ts = ldexpf(1.0f, emax - 8);          // 2^-135 .. 2^119; below 2^-126 a subnormal
-    *n = 0;
 }
 
 __global__ __launch_bounds__(kThreads) void remap_kernel(const uint8_t* __restrict__ codes,
@@ -323,11 +335,7 @@ hipError_t launch_quantize_nv(const uint16_t* x, int64_t rows, int64_t k, int64_
 hipError_t launch_remap(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t k,
                         uint8_t* scales_nv, float* ts, int32_t* n_inexact, hipStream_t s) {
     const int64_t nb = rows * (k / 32);
-    remap_init_kernel<<<1, 1, 0, s>>>(n_inexact);
-    unsigned g = grid_for(nb);
-    if (g > 1024) g = 1024;
-    remap_max_kernel<<<g, kThreads, 0, s>>>(scales, nb, n_inexact);
-    remap_scale_kernel<<<1, 1, 0, s>>>(n_inexact, ts);
+    remap_max_kernel<<<1, kRemapMaxThreads, 0, s>>>(scales, nb, ts, n_inexact);
     remap_kernel<<<grid_for(nb), kThreads, 0, s>>>(codes, scales, nb, scales_nv, ts, n_inexact);
     return hipGetLastError();
 }

@@ -167,6 +167,10 @@ int fp4_gemm(fp4_format fmt,
  *   h_codes_in, h_scales_in  [tokens*topk, inter/2], [tokens*topk, inter/32|16]:
  *                quantized h per slot (NV: with s_t = act_tensor_scales[1]);
  *                replaces the computed Q(h) as the input of the down stage.
+ * Stage timing: stage_events[i], when not NULL, is a hipEvent_t recorded on
+ * the call's stream at stage boundary i: 0 entry, 1 after Q(x), 2 after the
+ * routing metadata, 3 after gate/up (with SiLU*mul and Q(h)), 4 after down,
+ * 5 after the combine.
  */
 typedef struct fp4_moe_debug {
     uint8_t* x_codes;
@@ -182,6 +186,7 @@ typedef struct fp4_moe_debug {
     const float* gate_up_in;
     const uint8_t* h_codes_in;
     const uint8_t* h_scales_in;
+    void* stage_events[6];
 } fp4_moe_debug;
 
 /*
@@ -206,8 +211,8 @@ typedef struct fp4_moe_debug {
  * 8.2 million -> FP4_ERR_SHAPE; topk outside [1, 16] or num_experts outside
  * [1, 1024] -> FP4_ERR_INVALID; workspace too small -> FP4_ERR_WORKSPACE.
  * A slot whose expert id lies outside [0, num_experts) is routed nowhere and
- * contributes nothing to out.  The fp32 combine uses atomic adds, so out may
- * differ between runs in the last bit of the fp32 sum before the bf16 rounding.
+ * contributes nothing to out.  The combine sums each token's weighted rows in
+ * fp32 in order j = 0 .. topk-1 without atomics, so out is deterministic.
  */
 int fp4_moe_grouped_gemm(fp4_format fmt, const void* x_bf16, int64_t tokens, int64_t hidden,
                          const int32_t* topk_ids, const float* topk_weights, int topk,
