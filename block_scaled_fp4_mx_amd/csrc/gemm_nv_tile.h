@@ -1,0 +1,159 @@
+// LDS-staged NVFP4 block tile for gfx950: 64 rows of A (activations already
+// expanded to fp16) x 256 rows of B (NVFP4 codes + E4M3 group scales), K
+// advancing 256 values per step; 512 threads, 8 waves, each wave all 64 A rows
+// x 32 B rows (two 16-row fragments).
+//
+// NVFP4 group scales are not a matrix-core scale format, so B is expanded in
+// registers to the exact fp16 values code * s_g (at most 6 significant bits,
+// inside fp16's normal range for every E4M3 scale) and fed to
+// v_mfma_f32_16x16x32_f16; the tensor scales multiply the fp32 result.  The
+// expansion costs two instructions per pair of codes: v_cvt_scalef32_pk_f16_fp4
+// gives code * 2^e for the power-of-two part of s_g (it multiplies by
+// 2^floor(log2 scale)), and a packed fp16 multiply by the E4M3 mantissa
+// (1 + m/8, or m for a subnormal byte) finishes the exact value.
+//
+// Stage layout per K step (two stages): A 64 rows x 512 B (16-byte chunk c of
+// row r at c ^ (r & 15)), B codes 256 rows x 128 B (chunk c of row r at
+// c ^ (r & 7)), B scales 256 rows x 16 B.  All of it goes from global memory
+// straight into LDS (global_load_lds_dwordx4), as in the MX tile.
+#pragma once
+
+#include "gemm_mx_tile.h"
+
+namespace fp4 {
+
+constexpr int kNvTileM = 64, kNvTileN = 256, kNvThreads = 512;
+constexpr int kNvARow = 512;        // bytes of one A row per step (256 fp16)
+constexpr int kNvBRow = 128;        // code bytes of one B row per step
+constexpr int kNvSRow = 16;         // scale bytes of one B row per step
+
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+
+struct NvStage {
+    uint8_t a[kNvTileM * kNvARow];      // 32 KiB
+    uint8_t b[kNvTileN * kNvBRow];      // 32 KiB
+    uint8_t s[kNvTileN * kNvSRow];      // 4 KiB
+};
+struct NvSmem {
+    NvStage st[2];
+};
+
+// Sources of one tile, as per-lane byte offsets from bases that are the same
+// for the whole workgroup.  A: DMA q (q = 0..3) of a lane fills 1 KiB block
+// wave * 4 + q, i.e. row 2 * (wave * 4 + q) + lane / 32, LDS chunk lane % 32,
+// from global chunk (lane % 32) ^ (row & 15); aoff[q] is that row's byte offset
+// (row start of K step 0) plus the chunk.  B codes: DMA q fills rows
+// (wave * 4 + q) * 8 + lane / 8 ... as in the MX tile; boff[q] likewise.
+// B scales: DMA of thread t fills row t / ... (waves 0-3: rows wave * 64 + lane).
+struct NvSrc {
+    const uint8_t* a;       // fp16 activations, row pitch a_pitch bytes
+    const uint8_t* b;       // codes, row pitch K/2
+    const uint8_t* s;       // E4M3 bytes, row pitch K/16
+    uint32_t aoff[4], boff[4], soff;
+};
+
+__device__ __forceinline__ int nv_a_row(int q) {
+    return 2 * ((int)(threadIdx.x >> 6) * 4 + q) + (int)((threadIdx.x & 63) >> 5);
+}
+__device__ __forceinline__ uint32_t nv_a_chunk(int row) {
+    return (((threadIdx.x & 31) ^ (uint32_t)(row & 15)) * 16);
+}
+
+__device__ __forceinline__ void nv_issue(NvStage& sm, const NvSrc& S, int ks) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint8_t* a = S.a + (int64_t)ks * kNvARow;
+    const uint8_t* b = S.b + (int64_t)ks * kNvBRow;
+    const uint32_t la = lds_addr(sm.a) + wave * 4 * 1024, lb = lds_addr(sm.b) + wave * 4 * 1024;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        dma16(a, S.aoff[q], la + q * 1024);
+        dma16(b, S.boff[q], lb + q * 1024);
+    }
+    if (wave < 4) dma16(S.s + (int64_t)ks * kNvSRow, S.soff, lds_addr(sm.s) + wave * 1024);
+}
+
+// fp32 scale operand (2^e) and fp16 multiplier pair of an E4M3 group byte g:
+// normal (e_f > 0): s_g = 2^(e_f - 7) (1 + m/8); subnormal: s_g = 2^-9 m; g = 0
+// gives the multiplier 0.
+__device__ __forceinline__ void nv_scale_parts(uint32_t g, float& p2, h2_t& mult) {
+    const uint32_t ef = (g >> 3) & 15u, m = g & 7u;
+    const bool normal = ef != 0u;
+    p2 = __uint_as_float((normal ? ef + 120u : 118u) << 23);
+    const uint16_t mb = normal ? (uint16_t)(0x3C00u | (m << 7)) : __builtin_bit_cast(uint16_t, (_Float16)(float)m);
+    const h2_t mm = __builtin_bit_cast(h2_t, (uint32_t)mb * 0x10001u);
+    mult = mm;
+}
+
+// Eight codes (one word) of one group -> 8 exact fp16 values code * s_g.
+__device__ __forceinline__ h8_t nv_expand8(uint32_t w, float p2, h2_t mult) {
+    const h2_t a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, p2, 0) * mult;
+    const h2_t b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, p2, 1) * mult;
+    const h2_t c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, p2, 2) * mult;
+    const h2_t d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, p2, 3) * mult;
+    return h8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// Full K loop of one 64 x 256 tile for the MF A fragments (16 rows each) that
+// hold rows of the problem.  acc[mf][nf]: A rows mf*16 .., B rows of the wave's
+// fragment nf (wave * 32 + nf * 16 ..); D row = A row, D column = B row.
+// Every wave takes part in the copies and barriers.
+template <int MF>
+__device__ __forceinline__ void nv_tile_mainloop(NvSmem& sm, const NvSrc& S, int nsteps, v4f acc[4][2]) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lr = lane & 15, lq = lane >> 4;
+    nv_issue(sm.st[0], S, 0);
+    for (int ks = 0; ks < nsteps; ++ks) {
+        wait_vm_zero();
+        __syncthreads();
+        if (ks + 1 < nsteps) nv_issue(sm.st[(ks + 1) & 1], S, ks + 1);
+        if (MF == 0) continue;
+        const NvStage& st = sm.st[ks & 1];
+#pragma unroll
+        for (int hs = 0; hs < 2; ++hs) {
+            // B: the lane's 32 codes (K hs*128 + 32 lq ..) of its row in each fragment
+            h8_t bx[2][4];
+#pragma unroll
+            for (int nf = 0; nf < 2; ++nf) {
+                const int row = wave * 32 + nf * 16 + lr;
+                const uint4 c = *reinterpret_cast<const uint4*>(&st.b[row * kNvBRow + (((hs * 4 + lq) ^ (row & 7)) * 16)]);
+                const uint32_t sg = *reinterpret_cast<const uint16_t*>(&st.s[row * kNvSRow + hs * 8 + lq * 2]);
+                float p0, p1;
+                h2_t m0, m1;
+                nv_scale_parts(sg & 0xFFu, p0, m0);
+                nv_scale_parts(sg >> 8, p1, m1);
+                bx[nf][0] = nv_expand8(c.x, p0, m0);
+                bx[nf][1] = nv_expand8(c.y, p0, m0);
+                bx[nf][2] = nv_expand8(c.z, p1, m1);
+                bx[nf][3] = nv_expand8(c.w, p1, m1);
+            }
+            // A: fp16 rows, chunk hs*16 + 4 lq + i of each row
+#pragma unroll
+            for (int mf = 0; mf < MF; ++mf) {
+                const int row = mf * 16 + lr;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int ch = (hs * 16 + lq * 4 + i) ^ (row & 15);
+                    const h8_t a = *reinterpret_cast<const h8_t*>(&st.a[row * kNvARow + ch * 16]);
+#pragma unroll
+                    for (int nf = 0; nf < 2; ++nf)
+                        acc[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bx[nf][i], acc[mf][nf], 0, 0, 0);
+                }
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ void nv_tile_mainloop_rows(NvSmem& sm, const NvSrc& S, int nsteps, v4f acc[4][2],
+                                                      int64_t rows) {
+    const int mf = rows <= 0 ? 0 : (rows >= 64 ? 4 : (int)((rows + 15) >> 4));
+    switch (__builtin_amdgcn_readfirstlane(mf)) {
+        case 4: nv_tile_mainloop<4>(sm, S, nsteps, acc); break;
+        case 3: nv_tile_mainloop<3>(sm, S, nsteps, acc); break;
+        case 2: nv_tile_mainloop<2>(sm, S, nsteps, acc); break;
+        case 1: nv_tile_mainloop<1>(sm, S, nsteps, acc); break;
+        default: nv_tile_mainloop<0>(sm, S, nsteps, acc); break;
+    }
+}
+
+}  // namespace fp4

@@ -18,6 +18,7 @@
 // ("DeepSeek-V4.1-Flash-NVFP4" explainer, section 3) and the dispatch /
 // combine of tokens to experts ("DeepSeek-V4" article, section 6.1).
 #include "gemm_mx_tile.h"
+#include "gemm_nv_tile.h"
 #include "mma_core.h"
 #include "quant_device.h"
 
@@ -26,7 +27,8 @@ namespace {
 
 constexpr int kRouteSlots = 512;    // slots per routing block (bit masks of 16 words per expert)
 constexpr int kMaxExperts = 1024;
-constexpr int kBM = 128;            // routed rows per grouped-GEMM tile
+constexpr int kBM = 128;            // routed rows per fallback grouped-GEMM tile
+constexpr int kMinTileRows = 64;    // smallest row tile of any path
 constexpr int kGuCols = 64;         // intermediate columns (of g and of u) per gate/up tile
 constexpr int kDnCols = 128;        // hidden columns per down tile
 constexpr int kThreads = 256;
@@ -35,7 +37,7 @@ constexpr int kScanBatch = 16;     // routing blocks read together by the scan
 inline size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
-    size_t xc, xs, counts, offsets, blockbase, perm, slot_pos, tile_e, tile_r, ntiles, hc, hs, ybuf, total;
+    size_t xc, xs, counts, offsets, blockbase, perm, slot_pos, tile_e, tile_r, ntiles, hc, hs, ybuf, x16, h16, total;
     int64_t nblk, max_tiles;
 };
 
@@ -44,7 +46,9 @@ Layout layout(int fmt, int64_t T, int64_t H, int topk, int E, int64_t I) {
     const int64_t S = T * topk;
     const int blk = fmt == FP4_FMT_MX ? 32 : 16;
     L.nblk = (S + kRouteSlots - 1) / kRouteSlots;
-    L.max_tiles = (S + kBM - 1) / kBM + (E < S ? E : S);
+    // row tiles are 64 (NV tiles), 128 (fallback) or 256 (MX tiles) routed rows:
+    // at most ceil(S / 64) + one partial tile per expert
+    L.max_tiles = (S + kMinTileRows - 1) / kMinTileRows + (E < S ? E : S);
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t at = o; o += a256(bytes); return at; };
     L.xc = take((size_t)T * H / 2);
@@ -60,6 +64,10 @@ Layout layout(int fmt, int64_t T, int64_t H, int topk, int E, int64_t I) {
     L.hc = take((size_t)S * I / 2);
     L.hs = take((size_t)S * I / blk);
     L.ybuf = take((size_t)S * H * 4);
+    if (fmt == FP4_FMT_NV) {            // fp16 expansions of Q(x) and Q(h) for the NV tiles
+        L.x16 = take((size_t)T * H * 2);
+        L.h16 = take((size_t)S * I * 2);
+    }
     L.total = o;
     return L;
 }
@@ -213,6 +221,8 @@ struct GemmParams {
     const float* weights;              // [S]
     uint8_t *hc, *hs;                  // quantized h [S, I/2], [S, I/blk] in routed order
     float* ybuf;                       // [S, H]: w * y of slot s in row s
+    const uint16_t *x16, *h16;         // NV: fp16 code * s_g of Q(x) [T, H] and Q(h) [S, I]
+    int h16_by_slot;                   // NV: h16 rows are slots (injected Q(h)), else routed positions
     fp4_moe_debug dbg;
 };
 
@@ -606,6 +616,204 @@ __global__ __launch_bounds__(kTileThreads, 1) void moe_down_mx256_kernel(GemmPar
     }
 }
 
+// ------------------------------------------------------------------ NV grouped GEMMs on LDS-staged tiles
+// 64 routed rows x 256 weight rows per workgroup on the NV tile of
+// gemm_nv_tile.h (hidden and intermediate multiples of 256).  A is the fp16
+// expansion (code * s_g) of the quantized activations; each wave computes only
+// the 16-row fragments that hold rows of its expert's segment.
+
+// Rows of one NV operand -> exact fp16 values code * s_g (the tensor scale is
+// left to the GEMM epilogue).  Lane per 16-group.
+__global__ __launch_bounds__(kThreads) void expand_nv16_kernel(const uint8_t* __restrict__ codes,
+                                                               const uint8_t* __restrict__ scales, int64_t rows,
+                                                               int64_t k, uint16_t* __restrict__ out) {
+    const int64_t gpr = k >> 4, total = rows * gpr;
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    for (int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x; u < total; u += stride) {
+        const uint2 c = *reinterpret_cast<const uint2*>(codes + u * 8);
+        float p2;
+        h2_t mult;
+        nv_scale_parts(scales[u], p2, mult);
+        const h8_t a = nv_expand8(c.x, p2, mult), b = nv_expand8(c.y, p2, mult);
+        uint4* o = reinterpret_cast<uint4*>(out + u * 16);
+        o[0] = __builtin_bit_cast(uint4, a);
+        o[1] = __builtin_bit_cast(uint4, b);
+    }
+}
+
+// gate/up: wave w owns slab rows w*32 .. +31: 16 w1 rows (intermediate columns
+// c0 + w*16 ..) then the 16 w3 rows of the same columns, so fragment 0 holds g
+// and fragment 1 the matching u.  A tile covers 128 intermediate columns.
+constexpr int kNvGuCols = 128;
+
+__device__ __forceinline__ int64_t gu_nv_row(int slab_row, int64_t c0, int64_t I) {
+    const int w = slab_row >> 5, q = slab_row & 31;
+    return (q >= 16 ? I : 0) + c0 + w * 16 + (q & 15);
+}
+
+__global__ __launch_bounds__(kNvThreads, 1) void moe_gate_up_nv_kernel(GemmParams p) {
+    __shared__ __align__(16) NvSmem sm;
+    const int tile = blockIdx.y;
+    if (tile >= *p.ntiles) return;
+    const int e = p.tile_e[tile];
+    const int64_t r0 = p.tile_r[tile];
+    const int64_t rend = p.offsets[e + 1];
+    const int64_t c0 = (int64_t)blockIdx.x * kNvGuCols;
+    const int64_t H = p.H, I = p.I;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lr = lane & 15, lq = lane >> 4;
+    const bool injected = p.dbg.gate_up_in != nullptr;
+
+    v4f acc[4][2];
+#pragma unroll
+    for (int mf = 0; mf < 4; ++mf)
+#pragma unroll
+        for (int nf = 0; nf < 2; ++nf) acc[mf][nf] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    if (!injected) {
+        NvSrc S;
+        S.a = reinterpret_cast<const uint8_t*>(p.x16);
+        S.b = p.w13c + (int64_t)e * (2 * I) * (H / 2);
+        S.s = p.w13s + (int64_t)e * (2 * I) * (H / 16);
+        const uint32_t apitch = (uint32_t)(H * 2), bpitch = (uint32_t)(H / 2), spitch = (uint32_t)(H / 16);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int arow = nv_a_row(q);
+            const int64_t pos = min(r0 + arow, rend - 1);
+            S.aoff[q] = (uint32_t)(p.perm[pos] / p.topk) * apitch + nv_a_chunk(arow);
+            S.boff[q] = (uint32_t)gu_nv_row(mx_code_row(q), c0, I) * bpitch + mx_chunk16();
+        }
+        S.soff = (uint32_t)gu_nv_row(mx_scale_row(), c0, I) * spitch;
+        nv_tile_mainloop_rows(sm, S, (int)(H / 256), acc, rend - r0);
+    } else {
+        // g|u given per slot (debug injection, tensor scales included)
+#pragma unroll
+        for (int mf = 0; mf < 4; ++mf)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t pos = r0 + mf * 16 + lq * 4 + r;
+                if (pos >= rend) continue;
+                const float* src = p.dbg.gate_up_in + (int64_t)p.perm[pos] * 2 * I;
+                acc[mf][0][r] = src[c0 + wave * 16 + lr];
+                acc[mf][1][r] = src[I + c0 + wave * 16 + lr];
+            }
+    }
+    __syncthreads();   // the h tile reuses the stages
+
+    const float gscale = injected ? 1.0f : __fmul_rn(p.act_ts[0], p.w13ts[e]);
+    uint16_t* hsm = reinterpret_cast<uint16_t*>(&sm);      // 64 rows x 128 bf16
+#pragma unroll
+    for (int mf = 0; mf < 4; ++mf)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int rl = mf * 16 + lq * 4 + r;
+            const int cl = wave * 16 + lr;
+            const float g = injected ? acc[mf][0][r] : __fmul_rn(acc[mf][0][r], gscale);
+            const float u = injected ? acc[mf][1][r] : __fmul_rn(acc[mf][1][r], gscale);
+            const uint32_t hb = f32_to_bf16_rne(silu_mul(g, u));
+            hsm[rl * kNvGuCols + cl] = (uint16_t)hb;
+            const int64_t pos = r0 + rl;
+            if (pos < rend && (p.dbg.gate_up || p.dbg.h_bf16)) {
+                const int64_t slot = p.perm[pos];
+                if (p.dbg.gate_up) {
+                    p.dbg.gate_up[slot * 2 * I + c0 + cl] = g;
+                    p.dbg.gate_up[slot * 2 * I + I + c0 + cl] = u;
+                }
+                if (p.dbg.h_bf16) static_cast<uint16_t*>(p.dbg.h_bf16)[slot * I + c0 + cl] = (uint16_t)hb;
+            }
+        }
+    __syncthreads();
+    // quantize the 64 x 128 h tile: unit = 8 consecutive columns of one row; a
+    // 16-group spans 2 consecutive lanes
+    const double st_h = (double)p.act_ts[1];
+#pragma unroll
+    for (int q = 0; q < (kNvTileM * kNvGuCols / 8) / kNvThreads; ++q) {
+        const int unit = threadIdx.x + q * kNvThreads;
+        const int rl = unit / (kNvGuCols / 8), cu = unit % (kNvGuCols / 8);
+        const uint4 v = *reinterpret_cast<const uint4*>(&hsm[rl * kNvGuCols + cu * 8]);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        uint32_t sb;
+        const uint32_t packed = nv_quant8(w, st_h, sb);
+        const int64_t pos = r0 + rl;
+        if (pos < rend) {
+            const int64_t col = c0 + cu * 8;
+            reinterpret_cast<uint32_t*>(p.hc + pos * (I / 2) + col / 2)[0] = packed;
+            const bool lead = (cu & 1) == 0;
+            if (lead) p.hs[pos * (I / 16) + col / 16] = (uint8_t)sb;
+            if (p.dbg.h_codes || p.dbg.h_scales) {
+                const int64_t slot = p.perm[pos];
+                if (p.dbg.h_codes) reinterpret_cast<uint32_t*>(p.dbg.h_codes + slot * (I / 2) + col / 2)[0] = packed;
+                if (p.dbg.h_scales && lead) p.dbg.h_scales[slot * (I / 16) + col / 16] = (uint8_t)sb;
+            }
+        }
+    }
+}
+
+// down: the fp16 expansion of Q(h) for the tile's rows times w2 rows n0 .. n0 + 255.
+constexpr int kNvYRow = kNvTileN + 4;   // fp32 row pitch of the combine staging tile
+static_assert(kNvTileM * kNvYRow * 4 <= (int)sizeof(NvSmem), "staging tile exceeds the NV tile's LDS");
+
+__global__ __launch_bounds__(kNvThreads, 1) void moe_down_nv_kernel(GemmParams p) {
+    __shared__ __align__(16) NvSmem sm;
+    const int tile = blockIdx.y;
+    if (tile >= *p.ntiles) return;
+    const int e = p.tile_e[tile];
+    const int64_t r0 = p.tile_r[tile];
+    const int64_t rend = p.offsets[e + 1];
+    const int64_t n0 = (int64_t)blockIdx.x * kNvTileN;
+    const int64_t H = p.H, I = p.I;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lr = lane & 15, lq = lane >> 4;
+
+    NvSrc S;
+    S.a = reinterpret_cast<const uint8_t*>(p.h16);
+    S.b = p.w2c + (int64_t)e * H * (I / 2);
+    S.s = p.w2s + (int64_t)e * H * (I / 16);
+    const uint32_t apitch = (uint32_t)(I * 2), bpitch = (uint32_t)(I / 2), spitch = (uint32_t)(I / 16);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int arow = nv_a_row(q);
+        const int64_t pos = min(r0 + arow, rend - 1);
+        S.aoff[q] = (uint32_t)(p.h16_by_slot ? p.perm[pos] : pos) * apitch + nv_a_chunk(arow);
+        S.boff[q] = (uint32_t)min(n0 + mx_code_row(q), H - 1) * bpitch + mx_chunk16();
+    }
+    S.soff = (uint32_t)min(n0 + mx_scale_row(), H - 1) * spitch;
+
+    v4f acc[4][2];
+#pragma unroll
+    for (int mf = 0; mf < 4; ++mf)
+#pragma unroll
+        for (int nf = 0; nf < 2; ++nf) acc[mf][nf] = v4f{0.f, 0.f, 0.f, 0.f};
+    nv_tile_mainloop_rows(sm, S, (int)(I / 256), acc, rend - r0);
+    __syncthreads();   // the staging tile reuses the stages
+
+    const float yscale = __fmul_rn(p.act_ts[1], p.w2ts[e]);
+    float* ysm = reinterpret_cast<float*>(&sm);
+#pragma unroll
+    for (int mf = 0; mf < 4; ++mf)
+#pragma unroll
+        for (int nf = 0; nf < 2; ++nf)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int rl = mf * 16 + lq * 4 + r;
+                const int cl = wave * 32 + nf * 16 + lr;
+                const float y = __fmul_rn(acc[mf][nf][r], yscale);
+                ysm[rl * kNvYRow + cl] = y;
+                const int64_t pos = r0 + rl;
+                if (p.dbg.y && pos < rend) p.dbg.y[(int64_t)p.perm[pos] * H + n0 + cl] = y;
+            }
+    __syncthreads();
+    for (int rr = wave; rr < kNvTileM; rr += kNvThreads / 64) {
+        const int64_t pos = r0 + rr;
+        if (pos >= rend) break;     // rows are in order: the rest of this wave's rows are past the end too
+        const int64_t slot = p.perm[pos];
+        const float wgt = p.weights[slot];
+        const float4 v = *reinterpret_cast<const float4*>(&ysm[rr * kNvYRow + lane * 4]);
+        *reinterpret_cast<float4*>(p.ybuf + slot * H + n0 + lane * 4) =
+            make_float4(__fmul_rn(wgt, v.x), __fmul_rn(wgt, v.y), __fmul_rn(wgt, v.z), __fmul_rn(wgt, v.w));
+    }
+}
+
 // out[t] = bf16(sum over j of w * y of slot t*topk + j), summed in fp32 in
 // order j = 0 .. topk-1 over the slots whose expert id is in range.
 __global__ __launch_bounds__(kThreads) void combine_kernel(const float4* __restrict__ ybuf,
@@ -676,10 +884,12 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t s) {
     if (err != hipSuccess || (err = mark(1)) != hipSuccess) return err;
     // 2. routing metadata
     route_count_kernel<<<(unsigned)L.nblk, kRouteSlots, 0, s>>>(a.ids, S, E, blockbase);
-    // MX with hidden and inter multiples of 512: 256-row LDS-staged tiles
+    // LDS-staged tiles: MX with hidden and inter multiples of 512 (256 routed
+    // rows per tile), NV with multiples of 256 (64 routed rows per tile)
     const bool tiled = a.fmt == FP4_FMT_MX && H % 512 == 0 && I % 512 == 0;
+    const bool nv_tiled = a.fmt == FP4_FMT_NV && H % 256 == 0 && I % 256 == 0;
     route_scan_kernel<<<1, 1024, 0, s>>>(blockbase, L.nblk, E, counts, offsets, tile_e, tile_r, ntiles,
-                                         tiled ? kTileM : kBM);
+                                         tiled ? kTileM : (nv_tiled ? kNvTileM : kBM));
     route_place_kernel<<<(unsigned)L.nblk, kRouteSlots, (size_t)E * (kRouteSlots / 32) * 4, s>>>(a.ids, S, E, blockbase, perm,
                                                                                   slot_pos);
     if ((err = hipGetLastError()) != hipSuccess || (err = mark(2)) != hipSuccess) return err;
@@ -708,8 +918,26 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t s) {
     p.hs = hs;
     p.ybuf = ybuf;
     p.dbg = a.dbg;
+    uint16_t* x16 = reinterpret_cast<uint16_t*>(base + L.x16);
+    uint16_t* h16 = reinterpret_cast<uint16_t*>(base + L.h16);
+    p.x16 = x16;
+    p.h16 = h16;
+    p.h16_by_slot = a.dbg.h_codes_in != nullptr;
     // 3. gate/up + SiLU*mul + quantize h; 4. down + weighted combine
-    if (tiled) {
+    if (nv_tiled) {
+        expand_nv16_kernel<<<stream_grid(T * H / 16), kThreads, 0, s>>>(xc, xs, T, H, x16);
+        const dim3 g_gu((unsigned)(I / kNvGuCols), (unsigned)L.max_tiles);
+        const dim3 g_dn((unsigned)(H / kNvTileN), (unsigned)L.max_tiles);
+        moe_gate_up_nv_kernel<<<g_gu, kNvThreads, 0, s>>>(p);
+        if ((err = hipGetLastError()) != hipSuccess || (err = mark(3)) != hipSuccess) return err;
+        if (a.dbg.h_codes_in)
+            expand_nv16_kernel<<<stream_grid(S * I / 16), kThreads, 0, s>>>(a.dbg.h_codes_in, a.dbg.h_scales_in, S, I,
+                                                                             h16);
+        else
+            expand_nv16_kernel<<<stream_grid(S * I / 16), kThreads, 0, s>>>(hc, hs, S, I, h16);
+        moe_down_nv_kernel<<<g_dn, kNvThreads, 0, s>>>(p);
+        if ((err = hipGetLastError()) != hipSuccess || (err = mark(4)) != hipSuccess) return err;
+    } else if (tiled) {
         const dim3 g_gu((unsigned)(I / kGu2Cols), (unsigned)L.max_tiles);
         const dim3 g_dn((unsigned)(H / kTileN), (unsigned)L.max_tiles);
         moe_gate_up_mx256_kernel<<<g_gu, kTileThreads, 0, s>>>(p);

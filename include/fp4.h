@@ -208,7 +208,7 @@ typedef struct fp4_moe_debug {
  * (device); MX: all three NULL.  out_bf16 [tokens, hidden].
  * workspace: at least fp4_moe_workspace_bytes(...) bytes of device memory.
  * Errors: hidden or inter not a multiple of 128, or tokens*topk above about
- * 8.2 million -> FP4_ERR_SHAPE; topk outside [1, 16] or num_experts outside
+ * 4.1 million -> FP4_ERR_SHAPE; topk outside [1, 16] or num_experts outside
  * [1, 1024] -> FP4_ERR_INVALID; workspace too small -> FP4_ERR_WORKSPACE.
  * A slot whose expert id lies outside [0, num_experts) is routed nowhere and
  * contributes nothing to out.  The combine sums each token's weighted rows in

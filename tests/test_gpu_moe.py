@@ -65,6 +65,16 @@ def test_moe_tiled_mx_segments():
     _all_checks(case, oracle_expect(case, np.arange(case.T), eq))
 
 
+def test_moe_tiled_nv_segments():
+    """Hidden and intermediate multiples of 256 take the 64-row LDS-staged NV
+    tiles (fp16 expansion of the codes): segments spanning several tiles and
+    ragged last tiles of 1 to 4 row fragments."""
+    case, eq = _small_case("nv", 105, 300, 256, 256, 4, 2)
+    counts = np.bincount(case.ids.ravel(), minlength=4)
+    assert counts.max() > 64 and len(set((counts % 64 + 15) // 16)) > 1
+    _all_checks(case, oracle_expect(case, np.arange(case.T), eq))
+
+
 def test_moe_single_expert_topk1():
     T, H, I, E = 33, 128, 256, 5
     ids = np.full((T, 1), 3, np.int32)
