@@ -202,17 +202,19 @@ def main():
         Stage("gemm_mx_4096", lambda: F.fp4_gemm(F.FMT_MX, A3q[0], A3q[1], W3q[0], W3q[1], C3), "mfma",
               2.0 * 4096 ** 3, "2*M*N*K flop", "gemm_mx_256_kernel"),
     ]
+    want = set(args.only.split(",")) if args.only else None
     if not args.no_moe:
-        stages.append(build_moe_h4096(torch, F, W, dev))
-        stages.append(build_moe_decode(torch, F, W, dev))
+        if want is None or "moe_h4096" in want:
+            stages.append(build_moe_h4096(torch, F, W, dev))
+        if want is None or "moe_h7168_decode64" in want:
+            stages.append(build_moe_decode(torch, F, W, dev))
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         stages.append(Stage("copy_256MiB", lambda: dst.copy_(src), "hbm", 2.0 * (256 << 20),
                             "256 MiB read + 256 MiB written", "copy"))
-    if args.only:
-        keep = set(args.only.split(","))
-        stages = [s for s in stages if s.name in keep]
+    if want is not None:
+        stages = [s for s in stages if s.name in want]
 
     for _ in range(args.warmup):
         for s in stages:
