@@ -112,36 +112,59 @@ __global__ __launch_bounds__(kTileThreads, 1) void gemm_mx_256_kernel(
         for (int i = 0; i < 8; ++i) acc[j][i] = v4f{0.f, 0.f, 0.f, 0.f};
     mx_tile_mainloop<8>(sm, A, B, kblocks, acc);
 
+    // Epilogue through LDS: the tile (bf16: all 256 rows; fp32: 128 rows per
+    // pass) is written in the accumulator layout, then stored row by row in
+    // 16-byte pieces, so every global store instruction writes whole rows of
+    // the tile.  A row's 16-byte chunk c sits at chunk c ^ (row & 15), which
+    // spreads the 16 rows a fragment store touches over the banks.
     const int lane = t & 63, wave = t >> 6, wm = wave >> 2, wn = wave & 3;
     const int lr = lane & 15, lk = lane >> 4;
-    const bool vec = (ldc & 3) == 0;
+    const int esz = c_f32 ? 4 : 2;
+    const int rowb = kTileN * esz;                   // bytes of one tile row
+    const int rows_pass = c_f32 ? 128 : 256;
+    const int chunks_row = rowb / 16;
+    const bool vec = ((ldc * esz) & 15) == 0;
+    uint8_t* csm = reinterpret_cast<uint8_t*>(&sm);
+    for (int pass = 0; pass < kTileM / rows_pass; ++pass) {
+        __syncthreads();                             // the stages (or the previous pass) are free
+        if (!c_f32 || wm == pass) {
 #pragma unroll
-    for (int j = 0; j < kWaveFragsN; ++j)
+            for (int j = 0; j < kWaveFragsN; ++j)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int64_t row = m0 + wm * 128 + i * 16 + lr;
-            const int64_t col = n0 + wn * kWaveN + j * 16 + lk * 4;
-            if (row >= m) continue;
-            const v4f v = acc[j][i];
-            if (c_f32) {
-                float* dst = static_cast<float*>(c) + row * ldc + col;
-                if (vec && col + 3 < n) {
-                    *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
-                } else {
-                    for (int r = 0; r < 4; ++r)
-                        if (col + r < n) dst[r] = v[r];
+                for (int i = 0; i < 8; ++i) {
+                    const int row = (c_f32 ? 0 : wm * 128) + i * 16 + lr;   // row within the pass
+                    const int colb = (wn * kWaveN + j * 16 + lk * 4) * esz;  // byte within the row
+                    uint8_t* dst = csm + row * rowb + ((((colb >> 4) ^ (row & 15)) << 4) | (colb & 15));
+                    const v4f v = acc[j][i];
+                    if (c_f32)
+                        *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+                    else
+                        *reinterpret_cast<uint2*>(dst) =
+                            make_uint2(f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16),
+                                       f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16));
                 }
+        }
+        __syncthreads();
+        for (int q = t; q < rows_pass * chunks_row; q += kTileThreads) {
+            const int row = q / chunks_row, ch = q - row * chunks_row;
+            const int64_t grow = m0 + pass * rows_pass + row;
+            const int64_t gcol = n0 + ch * (16 / esz);
+            if (grow >= m || gcol >= n) continue;
+            const uint4 v = *reinterpret_cast<const uint4*>(csm + row * rowb + ((ch ^ (row & 15)) << 4));
+            uint8_t* dst = static_cast<uint8_t*>(c) + (grow * ldc + gcol) * esz;
+            if (vec && gcol + 16 / esz <= n) {
+                *reinterpret_cast<uint4*>(dst) = v;
             } else {
-                uint16_t* dst = static_cast<uint16_t*>(c) + row * ldc + col;
-                if (vec && col + 3 < n) {
-                    *reinterpret_cast<uint2*>(dst) = make_uint2(f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16),
-                                                                f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16));
-                } else {
-                    for (int r = 0; r < 4; ++r)
-                        if (col + r < n) dst[r] = (uint16_t)f32_to_bf16_rne(v[r]);
+                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+                for (int e = 0; e < 16 / esz && gcol + e < n; ++e) {
+                    if (c_f32)
+                        reinterpret_cast<uint32_t*>(dst)[e] = w[e];
+                    else
+                        reinterpret_cast<uint16_t*>(dst)[e] = (uint16_t)(w[e >> 1] >> ((e & 1) * 16));
                 }
             }
         }
+    }
 }
 
 }  // namespace

@@ -58,6 +58,27 @@ def test_gemm_mx_ragged(m, n, k):
     _mx_case(W.random_linear(m * 1000 + n + k, m, n, k, outlier_p=0.01), torch.float32)
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("pad", [0, 4, 16])
+def test_gemm_mx_tiled_ragged_strided(dtype, pad):
+    """K a multiple of 512 and at least 64 tiles: the 256x256 LDS-staged tile,
+    with ragged M and N, both output types and a padded output row pitch (pad 4
+    leaves bf16 rows off 16-byte alignment, which takes the scalar stores)."""
+    m, n, k = 2000, 2100, 1024
+    wl = W.random_linear(4242 + pad, m, n, k, outlier_p=0.01)
+    ab, wb = W.bf16_bits(wl.A), W.bf16_bits(wl.W)
+    a = quantize_mx(dev_bf16(ab))
+    b = quantize_mx(dev_bf16(wb))
+    buf = torch.full((m, n + pad), float("nan"), dtype=dtype, device=DEV)
+    c = buf[:, :n]
+    F.fp4_gemm(F.FMT_MX, a[0], a[1], b[0], b[1], c)
+    torch.cuda.synchronize()
+    Cref, S = G.gemm_ref("mx", *Q.mx_quantize(ab), *Q.mx_quantize(wb))
+    _assert_within(c, Cref, S)
+    if pad:
+        assert torch.isnan(buf[:, n:].float()).all()    # the padding is never written
+
+
 def test_gemm_mx_workload3_full_sampled():
     """Workload 3 (4096^3) at full size, in the launch the bench times; every
     output of 48 sampled rows and 48 sampled columns is checked."""
