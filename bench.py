@@ -7,7 +7,8 @@ are already resident in HBM:
             computed, and for the activation also with a calibrated one), the
             lossless MX->NV remap and an MX dequantize of the weight;
   gemm      the 4096^3 W4A4 MXFP4 GEMM (activations quantized on the fly,
-            weights pre-quantized, fp32 accumulation, bf16 output);
+            weights pre-quantized, fp32 accumulation, bf16 output), and the
+            same product in NVFP4;
   moe       the MoE layer at hidden 4096 (384 experts, top-6, intermediate
             2048, 8192 tokens, MXFP4 weights and activations), and the NVFP4
             MoE layer at hidden 7168 (intermediate 3072) on a decode batch of
@@ -171,6 +172,14 @@ def main():
     F.fp4_quantize_mx(W3, *W3q)
     A3q = qbufs(A3, 32)
     C3 = torch.empty((4096, 4096), dtype=torch.bfloat16, device=dev)
+
+    def nv_quantized(x):
+        c, s = qbufs(x, 16)
+        ts = torch.zeros(1, dtype=torch.float32, device=dev)
+        F.fp4_quantize_nv(x, c, s, ts, False, nvws)
+        return c, s, ts
+
+    A3n, W3n = nv_quantized(A3), nv_quantized(W3)
     del W3
 
     st = {"i": 0}
@@ -201,6 +210,9 @@ def main():
               "2.53125 B/elem", "mx_quantize_kernel"),
         Stage("gemm_mx_4096", lambda: F.fp4_gemm(F.FMT_MX, A3q[0], A3q[1], W3q[0], W3q[1], C3), "mfma",
               2.0 * 4096 ** 3, "2*M*N*K flop", "gemm_mx_256_kernel"),
+        Stage("gemm_nv_4096", lambda: F.fp4_gemm(F.FMT_NV, A3n[0], A3n[1], W3n[0], W3n[1], C3, A3n[2], W3n[2]),
+              "mfma_bf16", 2.0 * 4096 ** 3, "2*M*N*K flop (fp16 MFMA on the exact expansion; 16-bit peak)",
+              "gemm_nv_tile_kernel"),
     ]
     want = set(args.only.split(",")) if args.only else None
     if not args.no_moe:
@@ -299,6 +311,9 @@ def main():
         if qa:
             comps["gemm_with_onthefly_quantize_tflops"] = round(
                 2.0 * 4096 ** 3 / ((gemm["avg_us"] + qa["avg_us"]) * 1e-6) / 1e12, 1)
+    if "gemm_nv_4096" in rooflines:
+        comps["gemm_nv_tflops"] = rooflines["gemm_nv_4096"]["achieved"]
+        comps["gemm_nv_frac_16bit_peak"] = rooflines["gemm_nv_4096"]["frac"]
     for n in ("quantize_mx_W", "quantize_mx_A", "quantize_nv_W", "quantize_nv_A", "quantize_nv_A_calibrated",
               "gemm_quantize_A"):
         if n in rooflines:

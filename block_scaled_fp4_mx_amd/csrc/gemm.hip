@@ -13,6 +13,7 @@
 // significant bits) and uses v_mfma_f32_16x16x32_bf16; the two fp32 tensor
 // scales multiply the fp32 accumulator at the end.
 #include "gemm_mx_tile.h"
+#include "gemm_nv_tile.h"
 #include "mma_core.h"
 
 namespace fp4 {
@@ -167,6 +168,78 @@ __global__ __launch_bounds__(kTileThreads, 1) void gemm_mx_256_kernel(
     }
 }
 
+// NV GEMM on 64 x 256 tiles (gemm_nv_tile.h): B expanded to fp16 in
+// registers, A expanded into LDS each step, fp16 MFMA, tensor scales in the
+// epilogue; C goes through LDS and leaves in whole-row 16-byte pieces.
+__global__ __launch_bounds__(kNvThreads, 1) void gemm_nv_tile_kernel(
+    const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as, const float* __restrict__ ats,
+    const uint8_t* __restrict__ bc, const uint8_t* __restrict__ bs, const float* __restrict__ bts, int64_t m,
+    int64_t n, int64_t k, void* __restrict__ c, int c_f32, int64_t ldc, int tiles_m, int tiles_n) {
+    __shared__ __align__(16) NvSmem sm;
+    int tm, tn;
+    tile_coords(tiles_m, tiles_n, tm, tn);
+    const int64_t m0 = (int64_t)tm * kNvTileM, n0 = (int64_t)tn * kNvTileN;
+    const uint32_t kb = (uint32_t)(k / 2), kg = (uint32_t)(k / 16);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lr = lane & 15, lq = lane >> 4;
+    NvSrc S{};
+    S.ac = ac;
+    S.as = as;
+    S.b = bc;
+    S.s = bs;
+    S.acoff = (uint32_t)min(m0 + wave * 8 + (lane >> 3), m - 1) * kb + (uint32_t)(lane & 7) * 16;
+    S.asoff = (uint32_t)min(m0 + lane, m - 1) * kg;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) S.boff[q] = (uint32_t)min(n0 + mx_code_row(q), n - 1) * kb + mx_chunk16();
+    S.soff = (uint32_t)min(n0 + mx_scale_row(), n - 1) * kg;
+    v4f acc[4][2];
+#pragma unroll
+    for (int mf = 0; mf < 4; ++mf)
+#pragma unroll
+        for (int nf = 0; nf < 2; ++nf) acc[mf][nf] = v4f{0.f, 0.f, 0.f, 0.f};
+    nv_tile_mainloop_rows<true>(sm, S, (int)(k / 256), acc, m - m0);
+
+    const float scale = __fmul_rn(*ats, *bts);
+    const int esz = c_f32 ? 4 : 2;
+    const int rowb = kNvTileN * esz + 16;            // padded LDS row pitch (bytes)
+    uint8_t* csm = reinterpret_cast<uint8_t*>(&sm);
+    __syncthreads();                                 // the stages are free
+#pragma unroll
+    for (int mf = 0; mf < 4; ++mf)
+#pragma unroll
+        for (int nf = 0; nf < 2; ++nf)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = mf * 16 + lq * 4 + r, col = wave * 32 + nf * 16 + lr;
+                const float v = __fmul_rn(acc[mf][nf][r], scale);
+                if (c_f32)
+                    *reinterpret_cast<float*>(csm + row * rowb + col * 4) = v;
+                else
+                    *reinterpret_cast<uint16_t*>(csm + row * rowb + col * 2) = (uint16_t)f32_to_bf16_rne(v);
+            }
+    __syncthreads();
+    const int chunks_row = kNvTileN * esz / 16;
+    const bool vec = ((ldc * esz) & 15) == 0;
+    for (int q = threadIdx.x; q < kNvTileM * chunks_row; q += kNvThreads) {
+        const int row = q / chunks_row, ch = q - row * chunks_row;
+        const int64_t grow = m0 + row, gcol = n0 + ch * (16 / esz);
+        if (grow >= m || gcol >= n) continue;
+        const uint4 v = *reinterpret_cast<const uint4*>(csm + row * rowb + ch * 16);
+        uint8_t* dst = static_cast<uint8_t*>(c) + (grow * ldc + gcol) * esz;
+        if (vec && gcol + 16 / esz <= n) {
+            *reinterpret_cast<uint4*>(dst) = v;
+        } else {
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+            for (int e = 0; e < 16 / esz && gcol + e < n; ++e) {
+                if (c_f32)
+                    reinterpret_cast<uint32_t*>(dst)[e] = w[e];
+                else
+                    reinterpret_cast<uint16_t*>(dst)[e] = (uint16_t)(w[e >> 1] >> ((e & 1) * 16));
+            }
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_gemm_mx(const uint8_t* ac, const uint8_t* as, const uint8_t* bc, const uint8_t* bs,
@@ -188,8 +261,15 @@ hipError_t launch_gemm_nv(const uint8_t* ac, const uint8_t* as, const float* ats
                           const uint8_t* bc, const uint8_t* bs, const float* bts,
                           int64_t m, int64_t n, int64_t k, void* c, int c_f32, int64_t ldc,
                           hipStream_t s) {
-    dim3 grid((unsigned)((n + kBN - 1) / kBN), (unsigned)((m + kBM - 1) / kBM));
-    gemm_kernel<FP4_FMT_NV><<<grid, kThreads, 0, s>>>(ac, as, ats, bc, bs, bts, m, n, k, c, c_f32, ldc);
+    const int64_t tiles_m = (m + kNvTileM - 1) / kNvTileM, tiles_n = (n + kNvTileN - 1) / kNvTileN;
+    const bool small_ops = m * (k / 2) < (1ll << 31) && n * (k / 2) < (1ll << 31);
+    if (k % 256 == 0 && k > 0 && small_ops && tiles_m * tiles_n >= 64 && tiles_m * tiles_n < (1ll << 31)) {
+        gemm_nv_tile_kernel<<<(unsigned)(tiles_m * tiles_n), kNvThreads, 0, s>>>(
+            ac, as, ats, bc, bs, bts, m, n, k, c, c_f32, ldc, (int)tiles_m, (int)tiles_n);
+    } else {
+        dim3 grid((unsigned)((n + kBN - 1) / kBN), (unsigned)((m + kBM - 1) / kBM));
+        gemm_kernel<FP4_FMT_NV><<<grid, kThreads, 0, s>>>(ac, as, ats, bc, bs, bts, m, n, k, c, c_f32, ldc);
+    }
     return hipGetLastError();
 }
 

@@ -15,7 +15,9 @@
 // Stage layout per K step (two stages): A 64 rows x 512 B (16-byte chunk c of
 // row r at c ^ (r & 15)), B codes 256 rows x 128 B (chunk c of row r at
 // c ^ (r & 7)), B scales 256 rows x 16 B.  All of it goes from global memory
-// straight into LDS (global_load_lds_dwordx4), as in the MX tile.
+// straight into LDS (global_load_lds_dwordx4), as in the MX tile.  A may also
+// arrive as NVFP4 codes and scales (the dense GEMM), expanded into the fp16 A
+// in LDS by the whole workgroup each step.
 #pragma once
 
 #include "gemm_mx_tile.h"
@@ -31,9 +33,11 @@ typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 
 struct NvStage {
-    uint8_t a[kNvTileM * kNvARow];      // 32 KiB
+    uint8_t a[kNvTileM * kNvARow];      // 32 KiB: fp16 A
     uint8_t b[kNvTileN * kNvBRow];      // 32 KiB
     uint8_t s[kNvTileN * kNvSRow];      // 4 KiB
+    uint8_t ac[kNvTileM * kNvBRow];     // 8 KiB: A codes, when A comes as NVFP4 (row-major)
+    uint8_t as[kNvTileM * kNvSRow];     // 1 KiB: A scales, likewise
 };
 struct NvSmem {
     NvStage st[2];
@@ -51,6 +55,11 @@ struct NvSrc {
     const uint8_t* b;       // codes, row pitch K/2
     const uint8_t* s;       // E4M3 bytes, row pitch K/16
     uint32_t aoff[4], boff[4], soff;
+    // A as NVFP4 codes + E4M3 bytes (expanded to fp16 in LDS each step): the
+    // code DMA of wave w fills rows w*8 + lane/8, chunk lane & 7 (acoff); wave 0's
+    // scale DMA fills row lane (asoff)
+    const uint8_t *ac, *as;
+    uint32_t acoff, asoff;
 };
 
 __device__ __forceinline__ int nv_a_row(int q) {
@@ -60,16 +69,22 @@ __device__ __forceinline__ uint32_t nv_a_chunk(int row) {
     return (((threadIdx.x & 31) ^ (uint32_t)(row & 15)) * 16);
 }
 
+template <bool ACODES>
 __device__ __forceinline__ void nv_issue(NvStage& sm, const NvSrc& S, int ks) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint8_t* a = S.a + (int64_t)ks * kNvARow;
     const uint8_t* b = S.b + (int64_t)ks * kNvBRow;
-    const uint32_t la = lds_addr(sm.a) + wave * 4 * 1024, lb = lds_addr(sm.b) + wave * 4 * 1024;
+    const uint32_t lb = lds_addr(sm.b) + wave * 4 * 1024;
+    if (ACODES) {
+        dma16(S.ac + (int64_t)ks * kNvBRow, S.acoff, lds_addr(sm.ac) + wave * 1024);
+        if (wave == 0) dma16(S.as + (int64_t)ks * kNvSRow, S.asoff, lds_addr(sm.as));
+    } else {
+        const uint8_t* a = S.a + (int64_t)ks * kNvARow;
+        const uint32_t la = lds_addr(sm.a) + wave * 4 * 1024;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        dma16(a, S.aoff[q], la + q * 1024);
-        dma16(b, S.boff[q], lb + q * 1024);
+        for (int q = 0; q < 4; ++q) dma16(a, S.aoff[q], la + q * 1024);
     }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) dma16(b, S.boff[q], lb + q * 1024);
     if (wave < 4) dma16(S.s + (int64_t)ks * kNvSRow, S.soff, lds_addr(sm.s) + wave * 1024);
 }
 
@@ -94,19 +109,40 @@ __device__ __forceinline__ h8_t nv_expand8(uint32_t w, float p2, h2_t mult) {
     return h8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
+// A given as codes: the step's 64 x 256 A values expanded to fp16 into st.a
+// (two 16-groups per thread), in the swizzled layout the fragment reads use.
+__device__ __forceinline__ void nv_expand_a(NvStage& st) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int id = (int)threadIdx.x + q * kNvThreads;
+        const int row = id >> 4, g = id & 15;
+        const uint2 c = *reinterpret_cast<const uint2*>(&st.ac[row * kNvBRow + g * 8]);
+        float p2;
+        h2_t mult;
+        nv_scale_parts(st.as[row * kNvSRow + g], p2, mult);
+        *reinterpret_cast<h8_t*>(&st.a[row * kNvARow + (((2 * g) ^ (row & 15)) << 4)]) = nv_expand8(c.x, p2, mult);
+        *reinterpret_cast<h8_t*>(&st.a[row * kNvARow + (((2 * g + 1) ^ (row & 15)) << 4)]) = nv_expand8(c.y, p2, mult);
+    }
+}
+
 // Full K loop of one 64 x 256 tile for the MF A fragments (16 rows each) that
 // hold rows of the problem.  acc[mf][nf]: A rows mf*16 .., B rows of the wave's
 // fragment nf (wave * 32 + nf * 16 ..); D row = A row, D column = B row.
-// Every wave takes part in the copies and barriers.
-template <int MF>
+// Every wave takes part in the copies and barriers.  ACODES: A arrives as
+// NVFP4 codes and scales and is expanded into the stage's fp16 A each step.
+template <int MF, bool ACODES = false>
 __device__ __forceinline__ void nv_tile_mainloop(NvSmem& sm, const NvSrc& S, int nsteps, v4f acc[4][2]) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int lr = lane & 15, lq = lane >> 4;
-    nv_issue(sm.st[0], S, 0);
+    nv_issue<ACODES>(sm.st[0], S, 0);
     for (int ks = 0; ks < nsteps; ++ks) {
         wait_vm_zero();
         __syncthreads();
-        if (ks + 1 < nsteps) nv_issue(sm.st[(ks + 1) & 1], S, ks + 1);
+        if (ks + 1 < nsteps) nv_issue<ACODES>(sm.st[(ks + 1) & 1], S, ks + 1);
+        if (ACODES) {
+            nv_expand_a(sm.st[ks & 1]);
+            __syncthreads();
+        }
         if (MF == 0) continue;
         const NvStage& st = sm.st[ks & 1];
 #pragma unroll
@@ -144,15 +180,16 @@ __device__ __forceinline__ void nv_tile_mainloop(NvSmem& sm, const NvSrc& S, int
     }
 }
 
+template <bool ACODES = false>
 __device__ __forceinline__ void nv_tile_mainloop_rows(NvSmem& sm, const NvSrc& S, int nsteps, v4f acc[4][2],
                                                       int64_t rows) {
     const int mf = rows <= 0 ? 0 : (rows >= 64 ? 4 : (int)((rows + 15) >> 4));
     switch (__builtin_amdgcn_readfirstlane(mf)) {
-        case 4: nv_tile_mainloop<4>(sm, S, nsteps, acc); break;
-        case 3: nv_tile_mainloop<3>(sm, S, nsteps, acc); break;
-        case 2: nv_tile_mainloop<2>(sm, S, nsteps, acc); break;
-        case 1: nv_tile_mainloop<1>(sm, S, nsteps, acc); break;
-        default: nv_tile_mainloop<0>(sm, S, nsteps, acc); break;
+        case 4: nv_tile_mainloop<4, ACODES>(sm, S, nsteps, acc); break;
+        case 3: nv_tile_mainloop<3, ACODES>(sm, S, nsteps, acc); break;
+        case 2: nv_tile_mainloop<2, ACODES>(sm, S, nsteps, acc); break;
+        case 1: nv_tile_mainloop<1, ACODES>(sm, S, nsteps, acc); break;
+        default: nv_tile_mainloop<0, ACODES>(sm, S, nsteps, acc); break;
     }
 }
 

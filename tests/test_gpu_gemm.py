@@ -125,3 +125,46 @@ def test_gemm_nv_small(dtype):
 @pytest.mark.parametrize("m,n,k", [(1, 3, 16), (37, 75, 112), (130, 260, 4096)])
 def test_gemm_nv_ragged(m, n, k):
     _nv_case(W.random_linear(m * 7 + n + k, m, n, k), torch.float32)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("pad", [0, 4])
+def test_gemm_nv_tiled_ragged_strided(dtype, pad):
+    """K a multiple of 256 and at least 64 tiles: the 64x256 LDS-staged NV tile
+    (A expanded to fp16 in LDS, B in registers), ragged M and N, both output
+    types and a padded output row pitch."""
+    m, n, k = 1000, 1100, 1024
+    wl = W.random_linear(5151 + pad, m, n, k, outlier_p=0.01)
+    ab, wb = W.bf16_bits(wl.A), W.bf16_bits(wl.W)
+    ac, as_, ats = quantize_nv(dev_bf16(ab))
+    bc, bs, bts = quantize_nv(dev_bf16(wb))
+    buf = torch.full((m, n + pad), float("nan"), dtype=dtype, device=DEV)
+    c = buf[:, :n]
+    F.fp4_gemm(F.FMT_NV, ac, as_, bc, bs, c, ats, bts)
+    torch.cuda.synchronize()
+    ea, eb = Q.nv_quantize(ab), Q.nv_quantize(wb)
+    Cref, S = G.gemm_ref("nv", ea[0], ea[1], eb[0], eb[1], ea[2], eb[2])
+    _assert_within(c, Cref, S)
+    if pad:
+        assert torch.isnan(buf[:, n:].float()).all()
+
+
+def test_gemm_nv_4096_sampled():
+    """NVFP4 GEMM at 4096^3 (the tiled path): every output of 32 sampled rows
+    and 32 sampled columns within the bound."""
+    wl = W.workload3()
+    ab, wb = W.bf16_bits(wl.A), W.bf16_bits(wl.W)
+    ac, as_, ats = quantize_nv(dev_bf16(ab))
+    bc, bs, bts = quantize_nv(dev_bf16(wb))
+    c = _run_gemm("nv", (ac, as_), (bc, bs), torch.bfloat16, (ats, bts))
+    rng = np.random.default_rng(4)
+    rows = np.sort(rng.choice(4096, 32, replace=False))
+    cols = np.sort(rng.choice(4096, 32, replace=False))
+    sa, sb = Q.nv_tensor_scale(ab), Q.nv_tensor_scale(wb)
+    ea = Q.nv_quantize(ab[rows], s_t=sa)
+    eb = chunked(Q.nv_quantize, wb, s_t=sb)
+    Cref, S = G.gemm_ref("nv", ea[0], ea[1], eb[0], eb[1], sa, sb)
+    _assert_within(c[rows], Cref, S)
+    ea2 = chunked(Q.nv_quantize, ab, s_t=sa)
+    Cref2, S2 = G.gemm_ref("nv", ea2[0], ea2[1], eb[0][cols], eb[1][cols], sa, sb)
+    _assert_within(c[:, cols], Cref2, S2)
