@@ -20,6 +20,7 @@ namespace fp4 {
 namespace {
 
 constexpr int kBM = 128, kBN = 128, kThreads = 256;
+constexpr int kNvGemmM = 64;    // A rows per NV GEMM tile
 
 // 16x16 accumulator layout: lane holds rows 4*(lane/16) + r, column lane % 16.
 __device__ __forceinline__ void store_tile(const v4f acc[4][4], void* c, int c_f32, int64_t ldc, int64_t m,
@@ -175,10 +176,10 @@ __global__ __launch_bounds__(kNvThreads, 1) void gemm_nv_tile_kernel(
     const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as, const float* __restrict__ ats,
     const uint8_t* __restrict__ bc, const uint8_t* __restrict__ bs, const float* __restrict__ bts, int64_t m,
     int64_t n, int64_t k, void* __restrict__ c, int c_f32, int64_t ldc, int tiles_m, int tiles_n) {
-    __shared__ __align__(16) NvSmem sm;
+    __shared__ __align__(16) NvSmemT<kNvGemmM, 2, true> sm;
     int tm, tn;
     tile_coords(tiles_m, tiles_n, tm, tn);
-    const int64_t m0 = (int64_t)tm * kNvTileM, n0 = (int64_t)tn * kNvTileN;
+    const int64_t m0 = (int64_t)tm * kNvGemmM, n0 = (int64_t)tn * kNvTileN;
     const uint32_t kb = (uint32_t)(k / 2), kg = (uint32_t)(k / 16);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int lr = lane & 15, lq = lane >> 4;
@@ -197,7 +198,7 @@ __global__ __launch_bounds__(kNvThreads, 1) void gemm_nv_tile_kernel(
     for (int mf = 0; mf < 4; ++mf)
 #pragma unroll
         for (int nf = 0; nf < 2; ++nf) acc[mf][nf] = v4f{0.f, 0.f, 0.f, 0.f};
-    nv_tile_mainloop_rows<true>(sm, S, (int)(k / 256), acc, m - m0);
+    nv_tile_mainloop_rows(sm, S, (int)(k / 256), acc, m - m0);
 
     const float scale = __fmul_rn(*ats, *bts);
     const int esz = c_f32 ? 4 : 2;
@@ -220,7 +221,7 @@ __global__ __launch_bounds__(kNvThreads, 1) void gemm_nv_tile_kernel(
     __syncthreads();
     const int chunks_row = kNvTileN * esz / 16;
     const bool vec = ((ldc * esz) & 15) == 0;
-    for (int q = threadIdx.x; q < kNvTileM * chunks_row; q += kNvThreads) {
+    for (int q = threadIdx.x; q < kNvGemmM * chunks_row; q += kNvThreads) {
         const int row = q / chunks_row, ch = q - row * chunks_row;
         const int64_t grow = m0 + row, gcol = n0 + ch * (16 / esz);
         if (grow >= m || gcol >= n) continue;
@@ -261,7 +262,7 @@ hipError_t launch_gemm_nv(const uint8_t* ac, const uint8_t* as, const float* ats
                           const uint8_t* bc, const uint8_t* bs, const float* bts,
                           int64_t m, int64_t n, int64_t k, void* c, int c_f32, int64_t ldc,
                           hipStream_t s) {
-    const int64_t tiles_m = (m + kNvTileM - 1) / kNvTileM, tiles_n = (n + kNvTileN - 1) / kNvTileN;
+    const int64_t tiles_m = (m + kNvGemmM - 1) / kNvGemmM, tiles_n = (n + kNvTileN - 1) / kNvTileN;
     const bool small_ops = m * (k / 2) < (1ll << 31) && n * (k / 2) < (1ll << 31);
     if (k % 256 == 0 && k > 0 && small_ops && tiles_m * tiles_n >= 64 && tiles_m * tiles_n < (1ll << 31)) {
         gemm_nv_tile_kernel<<<(unsigned)(tiles_m * tiles_n), kNvThreads, 0, s>>>(

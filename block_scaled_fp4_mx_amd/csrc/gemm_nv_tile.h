@@ -1,7 +1,6 @@
-// LDS-staged NVFP4 block tile for gfx950: 64 rows of A (activations already
-// expanded to fp16) x 256 rows of B (NVFP4 codes + E4M3 group scales), K
-// advancing 256 values per step; 512 threads, 8 waves, each wave all 64 A rows
-// x 32 B rows (two 16-row fragments).
+// LDS-staged NVFP4 block tile for gfx950: TM rows of A (fp16) x 256 rows of B
+// (NVFP4 codes + E4M3 group scales), K advancing 256 values per step; 512
+// threads, 8 waves, each wave all TM A rows x 32 B rows (two 16-row fragments).
 //
 // NVFP4 group scales are not a matrix-core scale format, so B is expanded in
 // registers to the exact fp16 values code * s_g (at most 6 significant bits,
@@ -12,19 +11,24 @@
 // 2^floor(log2 scale)), and a packed fp16 multiply by the E4M3 mantissa
 // (1 + m/8, or m for a subnormal byte) finishes the exact value.
 //
-// Stage layout per K step (two stages): A 64 rows x 512 B (16-byte chunk c of
-// row r at c ^ (r & 15)), B codes 256 rows x 128 B (chunk c of row r at
-// c ^ (r & 7)), B scales 256 rows x 16 B.  All of it goes from global memory
-// straight into LDS (global_load_lds_dwordx4), as in the MX tile.  A may also
-// arrive as NVFP4 codes and scales (the dense GEMM), expanded into the fp16 A
-// in LDS by the whole workgroup each step.
+// Stage layout per K step: A TM rows x 512 B (16-byte chunk c of row r at
+// c ^ (r & 15)), B codes 256 rows x 128 B (chunk c of row r at c ^ (r & 7)), B
+// scales 256 rows x 16 B.  All of it goes from global memory straight into LDS
+// (global_load_lds_dwordx4 / _dword), as in the MX tile.  A may also arrive as
+// NVFP4 codes and scales (the dense GEMM), expanded into the fp16 A in LDS by
+// the whole workgroup each step.
+//
+// Configurations: 64 A rows with two stages (prefill-sized MoE segments, dense
+// GEMM) and 32 A rows with three stages (decode: few rows per expert, the
+// expert weights stream from HBM, and the third stage keeps two K steps of
+// weights in flight per workgroup).
 #pragma once
 
 #include "gemm_mx_tile.h"
 
 namespace fp4 {
 
-constexpr int kNvTileM = 64, kNvTileN = 256, kNvThreads = 512;
+constexpr int kNvTileN = 256, kNvThreads = 512;
 constexpr int kNvARow = 512;        // bytes of one A row per step (256 fp16)
 constexpr int kNvBRow = 128;        // code bytes of one B row per step
 constexpr int kNvSRow = 16;         // scale bytes of one B row per step
@@ -32,45 +36,66 @@ constexpr int kNvSRow = 16;         // scale bytes of one B row per step
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 
-struct NvStage {
-    uint8_t a[kNvTileM * kNvARow];      // 32 KiB: fp16 A
-    uint8_t b[kNvTileN * kNvBRow];      // 32 KiB
-    uint8_t s[kNvTileN * kNvSRow];      // 4 KiB
-    uint8_t ac[kNvTileM * kNvBRow];     // 8 KiB: A codes, when A comes as NVFP4 (row-major)
-    uint8_t as[kNvTileM * kNvSRow];     // 1 KiB: A scales, likewise
+template <int TM, bool ACODES>
+struct NvStageT {
+    uint8_t a[TM * kNvARow];                        // fp16 A
+    uint8_t b[kNvTileN * kNvBRow];
+    uint8_t s[kNvTileN * kNvSRow];
+    uint8_t ac[ACODES ? TM * kNvBRow : 16];         // A codes (row-major), when A comes as NVFP4
+    uint8_t as[ACODES ? TM * kNvSRow : 16];         // A scales, likewise
 };
-struct NvSmem {
-    NvStage st[2];
+template <int TM, int NS, bool ACODES>
+struct NvSmemT {
+    NvStageT<TM, ACODES> st[NS];
 };
 
 // Sources of one tile, as per-lane byte offsets from bases that are the same
-// for the whole workgroup.  A: DMA q (q = 0..3) of a lane fills 1 KiB block
-// wave * 4 + q, i.e. row 2 * (wave * 4 + q) + lane / 32, LDS chunk lane % 32,
-// from global chunk (lane % 32) ^ (row & 15); aoff[q] is that row's byte offset
-// (row start of K step 0) plus the chunk.  B codes: DMA q fills rows
-// (wave * 4 + q) * 8 + lane / 8 ... as in the MX tile; boff[q] likewise.
-// B scales: DMA of thread t fills row t / ... (waves 0-3: rows wave * 64 + lane).
+// for the whole workgroup.  A (fp16): DMA q of a lane fills 1 KiB block
+// wave * (TM/16) + q, i.e. row nv_a_row<TM>(q), LDS chunk lane % 32, from global
+// chunk (lane % 32) ^ (row & 15); aoff[q] is that row's byte offset plus the
+// chunk.  B codes: DMA q fills rows (wave * 4 + q) * 8 + lane / 8 as in the MX
+// tile (boff[q]).  B scales: two stages: waves 0-3 fill rows wave * 64 + lane
+// with one 16-byte DMA (soff); three stages: every wave fills its 512 bytes with
+// two 4-byte DMAs (sdw[j]: byte wave*512 + j*256 + 4*lane of the scale slab).
 struct NvSrc {
-    const uint8_t* a;       // fp16 activations, row pitch a_pitch bytes
+    const uint8_t* a;       // fp16 activations
     const uint8_t* b;       // codes, row pitch K/2
     const uint8_t* s;       // E4M3 bytes, row pitch K/16
-    uint32_t aoff[4], boff[4], soff;
-    // A as NVFP4 codes + E4M3 bytes (expanded to fp16 in LDS each step): the
-    // code DMA of wave w fills rows w*8 + lane/8, chunk lane & 7 (acoff); wave 0's
-    // scale DMA fills row lane (asoff)
+    uint32_t aoff[4], boff[4], soff, sdw[2];
+    // A as NVFP4 codes + E4M3 bytes: the code DMA of wave w fills rows
+    // w*8 + lane/8, chunk lane & 7 (acoff); wave 0's scale DMA fills row lane (asoff)
     const uint8_t *ac, *as;
     uint32_t acoff, asoff;
 };
 
+template <int TM>
 __device__ __forceinline__ int nv_a_row(int q) {
-    return 2 * ((int)(threadIdx.x >> 6) * 4 + q) + (int)((threadIdx.x & 63) >> 5);
+    return 2 * ((int)(threadIdx.x >> 6) * (TM / 16) + q) + (int)((threadIdx.x & 63) >> 5);
 }
 __device__ __forceinline__ uint32_t nv_a_chunk(int row) {
     return (((threadIdx.x & 31) ^ (uint32_t)(row & 15)) * 16);
 }
+// Three-stage scale DMA j of this lane: slab row, and byte within the row's 16.
+__device__ __forceinline__ int nv_sdw_row(int j) {
+    return ((int)(threadIdx.x >> 6) * 512 + j * 256 + 4 * (int)(threadIdx.x & 63)) >> 4;
+}
+__device__ __forceinline__ uint32_t nv_sdw_col() { return (uint32_t)((4 * (threadIdx.x & 63)) & 15); }
 
-template <bool ACODES>
-__device__ __forceinline__ void nv_issue(NvStage& sm, const NvSrc& S, int ks) {
+__device__ __forceinline__ void dma4(const uint8_t* base, uint32_t off, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base), "s"(lds)
+                 : "memory", "m0");
+}
+
+// DMA instructions each wave issues per K step in the three-stage
+// configuration (A 2, B codes 4, B scales 2): the count the waits rely on.
+constexpr int kNvDmaPerStep3 = 8;
+
+// Copies of one K step.  With two stages only the A rows of the MF fragments
+// in use are fetched (a decode-sized segment needs a quarter of the A bytes);
+// with three stages every wave issues the same fixed number of copies.
+template <int TM, int NS, bool ACODES, int MF>
+__device__ __forceinline__ void nv_issue(NvStageT<TM, ACODES>& sm, const NvSrc& S, int ks) {
+    static_assert(NS == 2 || (TM == 32 && !ACODES), "the three-stage copy count assumes 32 fp16 A rows");
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint8_t* b = S.b + (int64_t)ks * kNvBRow;
     const uint32_t lb = lds_addr(sm.b) + wave * 4 * 1024;
@@ -78,14 +103,21 @@ __device__ __forceinline__ void nv_issue(NvStage& sm, const NvSrc& S, int ks) {
         dma16(S.ac + (int64_t)ks * kNvBRow, S.acoff, lds_addr(sm.ac) + wave * 1024);
         if (wave == 0) dma16(S.as + (int64_t)ks * kNvSRow, S.asoff, lds_addr(sm.as));
     } else {
+        constexpr int QA = TM / 16;
         const uint8_t* a = S.a + (int64_t)ks * kNvARow;
-        const uint32_t la = lds_addr(sm.a) + wave * 4 * 1024;
+        const uint32_t la = lds_addr(sm.a) + wave * QA * 1024;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) dma16(a, S.aoff[q], la + q * 1024);
+        for (int q = 0; q < QA; ++q)
+            if (NS != 2 || wave * QA + q < MF * 8) dma16(a, S.aoff[q], la + q * 1024);   // block = 2 rows
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q) dma16(b, S.boff[q], lb + q * 1024);
-    if (wave < 4) dma16(S.s + (int64_t)ks * kNvSRow, S.soff, lds_addr(sm.s) + wave * 1024);
+    if (NS == 2) {
+        if (wave < 4) dma16(S.s + (int64_t)ks * kNvSRow, S.soff, lds_addr(sm.s) + wave * 1024);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) dma4(S.s + (int64_t)ks * kNvSRow, S.sdw[j], lds_addr(sm.s) + wave * 512 + j * 256);
+    }
 }
 
 // fp32 scale operand (2^e) and fp16 multiplier pair of an E4M3 group byte g:
@@ -109,11 +141,12 @@ __device__ __forceinline__ h8_t nv_expand8(uint32_t w, float p2, h2_t mult) {
     return h8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-// A given as codes: the step's 64 x 256 A values expanded to fp16 into st.a
-// (two 16-groups per thread), in the swizzled layout the fragment reads use.
-__device__ __forceinline__ void nv_expand_a(NvStage& st) {
+// A given as codes: the step's TM x 256 A values expanded to fp16 into st.a
+// (TM*16 groups over the workgroup), in the swizzled layout the fragment reads use.
+template <int TM>
+__device__ __forceinline__ void nv_expand_a(NvStageT<TM, true>& st) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < TM * 16 / kNvThreads; ++q) {
         const int id = (int)threadIdx.x + q * kNvThreads;
         const int row = id >> 4, g = id & 15;
         const uint2 c = *reinterpret_cast<const uint2*>(&st.ac[row * kNvBRow + g * 8]);
@@ -124,27 +157,39 @@ __device__ __forceinline__ void nv_expand_a(NvStage& st) {
         *reinterpret_cast<h8_t*>(&st.a[row * kNvARow + (((2 * g + 1) ^ (row & 15)) << 4)]) = nv_expand8(c.y, p2, mult);
     }
 }
+template <int TM>
+__device__ __forceinline__ void nv_expand_a(NvStageT<TM, false>&) {}
 
-// Full K loop of one 64 x 256 tile for the MF A fragments (16 rows each) that
+// Full K loop of one TM x 256 tile for the MF A fragments (16 rows each) that
 // hold rows of the problem.  acc[mf][nf]: A rows mf*16 .., B rows of the wave's
 // fragment nf (wave * 32 + nf * 16 ..); D row = A row, D column = B row.
-// Every wave takes part in the copies and barriers.  ACODES: A arrives as
-// NVFP4 codes and scales and is expanded into the stage's fp16 A each step.
-template <int MF, bool ACODES = false>
-__device__ __forceinline__ void nv_tile_mainloop(NvSmem& sm, const NvSrc& S, int nsteps, v4f acc[4][2]) {
+// Every wave takes part in the copies and barriers.  With NS stages the copies
+// of step ks + NS - 1 are issued at step ks; the wait at step ks leaves the
+// copies of the later steps in flight.
+template <int TM, int NS, bool ACODES, int MF>
+__device__ __forceinline__ void nv_tile_mainloop(NvSmemT<TM, NS, ACODES>& sm, const NvSrc& S, int nsteps,
+                                                 v4f acc[4][2]) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int lr = lane & 15, lq = lane >> 4;
-    nv_issue<ACODES>(sm.st[0], S, 0);
+#pragma unroll
+    for (int p = 0; p < NS - 1; ++p)
+        if (p < nsteps) nv_issue<TM, NS, ACODES, MF>(sm.st[p], S, p);
+    int cur = 0;
     for (int ks = 0; ks < nsteps; ++ks) {
-        wait_vm_zero();
+        if (NS == 3 && ks + 1 < nsteps)
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kNvDmaPerStep3) : "memory");   // step ks + 1 may still land
+        else
+            wait_vm_zero();
         __syncthreads();
-        if (ks + 1 < nsteps) nv_issue<ACODES>(sm.st[(ks + 1) & 1], S, ks + 1);
+        const int nxt = cur == 0 ? NS - 1 : cur - 1;    // (ks + NS - 1) % NS
+        if (ks + NS - 1 < nsteps) nv_issue<TM, NS, ACODES, MF>(sm.st[nxt], S, ks + NS - 1);
         if (ACODES) {
-            nv_expand_a(sm.st[ks & 1]);
+            nv_expand_a<TM>(sm.st[cur]);
             __syncthreads();
         }
+        const NvStageT<TM, ACODES>& st = sm.st[cur];
+        cur = cur + 1 == NS ? 0 : cur + 1;
         if (MF == 0) continue;
-        const NvStage& st = sm.st[ks & 1];
 #pragma unroll
         for (int hs = 0; hs < 2; ++hs) {
             // B: the lane's 32 codes (K hs*128 + 32 lq ..) of its row in each fragment
@@ -180,16 +225,17 @@ __device__ __forceinline__ void nv_tile_mainloop(NvSmem& sm, const NvSrc& S, int
     }
 }
 
-template <bool ACODES = false>
-__device__ __forceinline__ void nv_tile_mainloop_rows(NvSmem& sm, const NvSrc& S, int nsteps, v4f acc[4][2],
-                                                      int64_t rows) {
-    const int mf = rows <= 0 ? 0 : (rows >= 64 ? 4 : (int)((rows + 15) >> 4));
+template <int TM, int NS, bool ACODES>
+__device__ __forceinline__ void nv_tile_mainloop_rows(NvSmemT<TM, NS, ACODES>& sm, const NvSrc& S, int nsteps,
+                                                      v4f acc[4][2], int64_t rows) {
+    constexpr int kMaxMf = TM / 16;
+    const int mf = rows <= 0 ? 0 : (rows >= TM ? kMaxMf : (int)((rows + 15) >> 4));
     switch (__builtin_amdgcn_readfirstlane(mf)) {
-        case 4: nv_tile_mainloop<4, ACODES>(sm, S, nsteps, acc); break;
-        case 3: nv_tile_mainloop<3, ACODES>(sm, S, nsteps, acc); break;
-        case 2: nv_tile_mainloop<2, ACODES>(sm, S, nsteps, acc); break;
-        case 1: nv_tile_mainloop<1, ACODES>(sm, S, nsteps, acc); break;
-        default: nv_tile_mainloop<0, ACODES>(sm, S, nsteps, acc); break;
+        case 4: if constexpr (kMaxMf >= 4) nv_tile_mainloop<TM, NS, ACODES, 4>(sm, S, nsteps, acc); break;
+        case 3: if constexpr (kMaxMf >= 3) nv_tile_mainloop<TM, NS, ACODES, 3>(sm, S, nsteps, acc); break;
+        case 2: nv_tile_mainloop<TM, NS, ACODES, 2>(sm, S, nsteps, acc); break;
+        case 1: nv_tile_mainloop<TM, NS, ACODES, 1>(sm, S, nsteps, acc); break;
+        default: nv_tile_mainloop<TM, NS, ACODES, 0>(sm, S, nsteps, acc); break;
     }
 }
 

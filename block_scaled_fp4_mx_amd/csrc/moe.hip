@@ -28,7 +28,8 @@ namespace {
 constexpr int kRouteSlots = 512;    // slots per routing block (bit masks of 16 words per expert)
 constexpr int kMaxExperts = 1024;
 constexpr int kBM = 128;            // routed rows per fallback grouped-GEMM tile
-constexpr int kMinTileRows = 64;    // smallest row tile of any path
+constexpr int kMinTileRows = 32;    // smallest row tile of any path
+constexpr int kNvDecodeTokens = 128;  // NV batches up to this many tokens use the decode tiles
 constexpr int kGuCols = 64;         // intermediate columns (of g and of u) per gate/up tile
 constexpr int kDnCols = 128;        // hidden columns per down tile
 constexpr int kThreads = 256;
@@ -46,8 +47,8 @@ Layout layout(int fmt, int64_t T, int64_t H, int topk, int E, int64_t I) {
     const int64_t S = T * topk;
     const int blk = fmt == FP4_FMT_MX ? 32 : 16;
     L.nblk = (S + kRouteSlots - 1) / kRouteSlots;
-    // row tiles are 64 (NV tiles), 128 (fallback) or 256 (MX tiles) routed rows:
-    // at most ceil(S / 64) + one partial tile per expert
+    // row tiles are 32 or 64 (NV tiles), 128 (fallback) or 256 (MX tiles) routed
+    // rows: at most ceil(S / 32) + one partial tile per expert
     L.max_tiles = (S + kMinTileRows - 1) / kMinTileRows + (E < S ? E : S);
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t at = o; o += a256(bytes); return at; };
@@ -651,8 +652,9 @@ __device__ __forceinline__ int64_t gu_nv_row(int slab_row, int64_t c0, int64_t I
     return (q >= 16 ? I : 0) + c0 + w * 16 + (q & 15);
 }
 
+template <int TM, int NS>
 __global__ __launch_bounds__(kNvThreads, 1) void moe_gate_up_nv_kernel(GemmParams p) {
-    __shared__ __align__(16) NvSmem sm;
+    __shared__ __align__(16) NvSmemT<TM, NS, false> sm;
     const int tile = blockIdx.y;
     if (tile >= *p.ntiles) return;
     const int e = p.tile_e[tile];
@@ -671,24 +673,28 @@ __global__ __launch_bounds__(kNvThreads, 1) void moe_gate_up_nv_kernel(GemmParam
         for (int nf = 0; nf < 2; ++nf) acc[mf][nf] = v4f{0.f, 0.f, 0.f, 0.f};
 
     if (!injected) {
-        NvSrc S;
+        NvSrc S{};
         S.a = reinterpret_cast<const uint8_t*>(p.x16);
         S.b = p.w13c + (int64_t)e * (2 * I) * (H / 2);
         S.s = p.w13s + (int64_t)e * (2 * I) * (H / 16);
         const uint32_t apitch = (uint32_t)(H * 2), bpitch = (uint32_t)(H / 2), spitch = (uint32_t)(H / 16);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int arow = nv_a_row(q);
-            const int64_t pos = min(r0 + arow, rend - 1);
-            S.aoff[q] = (uint32_t)(p.perm[pos] / p.topk) * apitch + nv_a_chunk(arow);
+            if (q < TM / 16) {
+                const int arow = nv_a_row<TM>(q);
+                const int64_t pos = min(r0 + arow, rend - 1);
+                S.aoff[q] = (uint32_t)(p.perm[pos] / p.topk) * apitch + nv_a_chunk(arow);
+            }
             S.boff[q] = (uint32_t)gu_nv_row(mx_code_row(q), c0, I) * bpitch + mx_chunk16();
         }
         S.soff = (uint32_t)gu_nv_row(mx_scale_row(), c0, I) * spitch;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) S.sdw[j] = (uint32_t)gu_nv_row(nv_sdw_row(j), c0, I) * spitch + nv_sdw_col();
         nv_tile_mainloop_rows(sm, S, (int)(H / 256), acc, rend - r0);
     } else {
         // g|u given per slot (debug injection, tensor scales included)
 #pragma unroll
-        for (int mf = 0; mf < 4; ++mf)
+        for (int mf = 0; mf < TM / 16; ++mf)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int64_t pos = r0 + mf * 16 + lq * 4 + r;
@@ -701,9 +707,9 @@ __global__ __launch_bounds__(kNvThreads, 1) void moe_gate_up_nv_kernel(GemmParam
     __syncthreads();   // the h tile reuses the stages
 
     const float gscale = injected ? 1.0f : __fmul_rn(p.act_ts[0], p.w13ts[e]);
-    uint16_t* hsm = reinterpret_cast<uint16_t*>(&sm);      // 64 rows x 128 bf16
+    uint16_t* hsm = reinterpret_cast<uint16_t*>(&sm);      // TM rows x 128 bf16
 #pragma unroll
-    for (int mf = 0; mf < 4; ++mf)
+    for (int mf = 0; mf < TM / 16; ++mf)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int rl = mf * 16 + lq * 4 + r;
@@ -723,11 +729,11 @@ __global__ __launch_bounds__(kNvThreads, 1) void moe_gate_up_nv_kernel(GemmParam
             }
         }
     __syncthreads();
-    // quantize the 64 x 128 h tile: unit = 8 consecutive columns of one row; a
+    // quantize the TM x 128 h tile: unit = 8 consecutive columns of one row; a
     // 16-group spans 2 consecutive lanes
     const double st_h = (double)p.act_ts[1];
 #pragma unroll
-    for (int q = 0; q < (kNvTileM * kNvGuCols / 8) / kNvThreads; ++q) {
+    for (int q = 0; q < (TM * kNvGuCols / 8) / kNvThreads; ++q) {
         const int unit = threadIdx.x + q * kNvThreads;
         const int rl = unit / (kNvGuCols / 8), cu = unit % (kNvGuCols / 8);
         const uint4 v = *reinterpret_cast<const uint4*>(&hsm[rl * kNvGuCols + cu * 8]);
@@ -751,10 +757,11 @@ __global__ __launch_bounds__(kNvThreads, 1) void moe_gate_up_nv_kernel(GemmParam
 
 // down: the fp16 expansion of Q(h) for the tile's rows times w2 rows n0 .. n0 + 255.
 constexpr int kNvYRow = kNvTileN + 4;   // fp32 row pitch of the combine staging tile
-static_assert(kNvTileM * kNvYRow * 4 <= (int)sizeof(NvSmem), "staging tile exceeds the NV tile's LDS");
 
+template <int TM, int NS>
 __global__ __launch_bounds__(kNvThreads, 1) void moe_down_nv_kernel(GemmParams p) {
-    __shared__ __align__(16) NvSmem sm;
+    __shared__ __align__(16) NvSmemT<TM, NS, false> sm;
+    static_assert(TM * kNvYRow * 4 <= (int)sizeof(sm), "staging tile exceeds the NV tile's LDS");
     const int tile = blockIdx.y;
     if (tile >= *p.ntiles) return;
     const int e = p.tile_e[tile];
@@ -765,19 +772,23 @@ __global__ __launch_bounds__(kNvThreads, 1) void moe_down_nv_kernel(GemmParams p
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int lr = lane & 15, lq = lane >> 4;
 
-    NvSrc S;
+    NvSrc S{};
     S.a = reinterpret_cast<const uint8_t*>(p.h16);
     S.b = p.w2c + (int64_t)e * H * (I / 2);
     S.s = p.w2s + (int64_t)e * H * (I / 16);
     const uint32_t apitch = (uint32_t)(I * 2), bpitch = (uint32_t)(I / 2), spitch = (uint32_t)(I / 16);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        const int arow = nv_a_row(q);
-        const int64_t pos = min(r0 + arow, rend - 1);
-        S.aoff[q] = (uint32_t)(p.h16_by_slot ? p.perm[pos] : pos) * apitch + nv_a_chunk(arow);
+        if (q < TM / 16) {
+            const int arow = nv_a_row<TM>(q);
+            const int64_t pos = min(r0 + arow, rend - 1);
+            S.aoff[q] = (uint32_t)(p.h16_by_slot ? p.perm[pos] : pos) * apitch + nv_a_chunk(arow);
+        }
         S.boff[q] = (uint32_t)min(n0 + mx_code_row(q), H - 1) * bpitch + mx_chunk16();
     }
     S.soff = (uint32_t)min(n0 + mx_scale_row(), H - 1) * spitch;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) S.sdw[j] = (uint32_t)min(n0 + nv_sdw_row(j), H - 1) * spitch + nv_sdw_col();
 
     v4f acc[4][2];
 #pragma unroll
@@ -790,7 +801,7 @@ __global__ __launch_bounds__(kNvThreads, 1) void moe_down_nv_kernel(GemmParams p
     const float yscale = __fmul_rn(p.act_ts[1], p.w2ts[e]);
     float* ysm = reinterpret_cast<float*>(&sm);
 #pragma unroll
-    for (int mf = 0; mf < 4; ++mf)
+    for (int mf = 0; mf < TM / 16; ++mf)
 #pragma unroll
         for (int nf = 0; nf < 2; ++nf)
 #pragma unroll
@@ -803,7 +814,7 @@ __global__ __launch_bounds__(kNvThreads, 1) void moe_down_nv_kernel(GemmParams p
                 if (p.dbg.y && pos < rend) p.dbg.y[(int64_t)p.perm[pos] * H + n0 + cl] = y;
             }
     __syncthreads();
-    for (int rr = wave; rr < kNvTileM; rr += kNvThreads / 64) {
+    for (int rr = wave; rr < TM; rr += kNvThreads / 64) {
         const int64_t pos = r0 + rr;
         if (pos >= rend) break;     // rows are in order: the rest of this wave's rows are past the end too
         const int64_t slot = p.perm[pos];
@@ -888,8 +899,9 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t s) {
     // rows per tile), NV with multiples of 256 (64 routed rows per tile)
     const bool tiled = a.fmt == FP4_FMT_MX && H % 512 == 0 && I % 512 == 0;
     const bool nv_tiled = a.fmt == FP4_FMT_NV && H % 256 == 0 && I % 256 == 0;
+    const bool nv_decode = T <= kNvDecodeTokens;       // 32-row, three-stage NV tiles
     route_scan_kernel<<<1, 1024, 0, s>>>(blockbase, L.nblk, E, counts, offsets, tile_e, tile_r, ntiles,
-                                         tiled ? kTileM : (nv_tiled ? kNvTileM : kBM));
+                                         tiled ? kTileM : (nv_tiled ? (nv_decode ? 32 : 64) : kBM));
     route_place_kernel<<<(unsigned)L.nblk, kRouteSlots, (size_t)E * (kRouteSlots / 32) * 4, s>>>(a.ids, S, E, blockbase, perm,
                                                                                   slot_pos);
     if ((err = hipGetLastError()) != hipSuccess || (err = mark(2)) != hipSuccess) return err;
@@ -928,14 +940,16 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t s) {
         expand_nv16_kernel<<<stream_grid(T * H / 16), kThreads, 0, s>>>(xc, xs, T, H, x16);
         const dim3 g_gu((unsigned)(I / kNvGuCols), (unsigned)L.max_tiles);
         const dim3 g_dn((unsigned)(H / kNvTileN), (unsigned)L.max_tiles);
-        moe_gate_up_nv_kernel<<<g_gu, kNvThreads, 0, s>>>(p);
+        if (nv_decode) moe_gate_up_nv_kernel<32, 3><<<g_gu, kNvThreads, 0, s>>>(p);
+        else moe_gate_up_nv_kernel<64, 2><<<g_gu, kNvThreads, 0, s>>>(p);
         if ((err = hipGetLastError()) != hipSuccess || (err = mark(3)) != hipSuccess) return err;
         if (a.dbg.h_codes_in)
             expand_nv16_kernel<<<stream_grid(S * I / 16), kThreads, 0, s>>>(a.dbg.h_codes_in, a.dbg.h_scales_in, S, I,
                                                                              h16);
         else
             expand_nv16_kernel<<<stream_grid(S * I / 16), kThreads, 0, s>>>(hc, hs, S, I, h16);
-        moe_down_nv_kernel<<<g_dn, kNvThreads, 0, s>>>(p);
+        if (nv_decode) moe_down_nv_kernel<32, 3><<<g_dn, kNvThreads, 0, s>>>(p);
+        else moe_down_nv_kernel<64, 2><<<g_dn, kNvThreads, 0, s>>>(p);
         if ((err = hipGetLastError()) != hipSuccess || (err = mark(4)) != hipSuccess) return err;
     } else if (tiled) {
         const dim3 g_gu((unsigned)(I / kGu2Cols), (unsigned)L.max_tiles);

@@ -75,6 +75,16 @@ def test_moe_tiled_nv_segments():
     _all_checks(case, oracle_expect(case, np.arange(case.T), eq))
 
 
+def test_moe_decode_nv_segments():
+    """Batches of at most 128 tokens take the 32-row, three-stage NV tiles:
+    several tiles per expert, ragged last tiles, and K loops of 4 (gate/up)
+    and 3 (down) steps, which exercise the copy waits with two steps in flight."""
+    case, eq = _small_case("nv", 106, 100, 1024, 768, 8, 6)
+    counts = np.bincount(case.ids.ravel(), minlength=8)
+    assert counts.max() > 64 and (counts % 32 != 0).any()
+    _all_checks(case, oracle_expect(case, np.arange(case.T), eq))
+
+
 def test_moe_single_expert_topk1():
     T, H, I, E = 33, 128, 256, 5
     ids = np.full((T, 1), 3, np.int32)
