@@ -12,7 +12,7 @@ are already resident in HBM:
   moe       the MoE layer at hidden 4096 (384 experts, top-6, intermediate
             2048, 8192 tokens, MXFP4 weights and activations), and the NVFP4
             MoE layer at hidden 7168 (intermediate 3072) on a decode batch of
-            64 tokens.
+            64 tokens and on a prefill batch of 16384 tokens.
 The input of every HBM-bound stage rotates through copies whose total exceeds
 the 256 MB last-level cache, so each launch reads HBM, not cache.
 
@@ -220,6 +220,8 @@ def main():
             stages.append(build_moe_h4096(torch, F, W, dev))
         if want is None or "moe_h7168_decode64" in want:
             stages.append(build_moe_decode(torch, F, W, dev))
+        if want is None or "moe_h7168_prefill16384" in want:
+            stages.append(build_moe_prefill(torch, F, W, dev))
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -327,6 +329,12 @@ def main():
         comps["moe_h7168_decode_tokens_per_s"] = round(64 / (m["avg_us"] * 1e-6), 1)
         comps["moe_h7168_decode_weight_GBps"] = m["achieved"]
         comps["moe_h7168_decode_frac_hbm"] = m["frac"]
+    if "moe_h7168_prefill16384" in rooflines:
+        m = rooflines["moe_h7168_prefill16384"]
+        comps["moe_h7168_prefill_tokens_per_s"] = round(16384 / (m["avg_us"] * 1e-6), 1)
+        comps["moe_h7168_prefill_tflops"] = m["achieved"]
+        comps["moe_h7168_prefill_frac_16bit_peak"] = m["frac"]
+        comps["moe_h7168_prefill_frac_fp4_peak"] = round(m["achieved"] / PEAK_FP4_TFLOPS, 4)
     out = {
         "metric": METRIC,
         "value": value,
@@ -343,7 +351,7 @@ def main():
         "config": {"workload": "W4A4 MXFP4 GEMM M=N=K=4096 (bf16 out, fp32 accumulate) for value; per step also "
                                "MX/NV quantize of linear 4096x4096 W and 2048x4096 A, MX->NV remap, MX dequant, "
                                "MoE hidden 4096 (384 experts, top-6, inter 2048, 8192 tokens, MXFP4) and "
-                               "NVFP4 MoE hidden 7168 (inter 3072, 64 decode tokens)",
+                               "NVFP4 MoE hidden 7168 (inter 3072) at 64 decode and 16384 prefill tokens",
                    "accumulate": "fp32", "traffic_source": "profiles/traffic.json" if traffic else None},
         "components": comps,
         "roofline": {k: v for k, v in dom.items() if k in ("bound", "achieved", "peak", "unit", "frac", "traffic")}
@@ -383,10 +391,13 @@ def moe_stage(torch, F, name, fmt, m, E, w13c, w13s, w2c, w2s, w13ts, w2ts, act,
         "down": (bound, flops_dn, "2*H*I flop per routed slot"),
         "combine": ("hbm", S * H * 4 + T * H * 2, "4 B per slot per hidden column in, 2 B per token column out"),
     }
+    nv_tile = "<32, 3>" if T <= 128 else "<64, 2>"      # the launcher's decode / prefill NV tiles
     names = {"quantize_x": "mx_quantize_kernel" if fmt == F.FMT_MX else "nv_quantize_kernel",
              "routing": "route_count_kernel + route_scan_kernel + route_place_kernel",
-             "gate_up": "moe_gate_up_mx256_kernel" if fmt == F.FMT_MX else "moe_gate_up_kernel<1>",
-             "down": "moe_down_mx256_kernel" if fmt == F.FMT_MX else "moe_down_kernel<1>",
+             "gate_up": "moe_gate_up_mx256_kernel" if fmt == F.FMT_MX else
+             f"expand_nv16_kernel (x) + moe_gate_up_nv_kernel{nv_tile}",
+             "down": "moe_down_mx256_kernel" if fmt == F.FMT_MX else
+             f"expand_nv16_kernel (h) + moe_down_nv_kernel{nv_tile}",
              "combine": "combine_kernel"}
     if bound == "hbm":
         # decode: the expert weights dominate the bytes of both GEMMs
@@ -422,10 +433,22 @@ def build_moe_h4096(torch, F, W, dev):
 
 def build_moe_decode(torch, F, W, dev):
     """NVFP4 MoE layer at hidden 7168 on a decode batch of 64 tokens: the
-    active experts' weights stream from HBM.  The activation tensor scales are
-    calibrated: s_x from amax(x), s_h from amax(h) of one calibration call."""
-    m = W.moe_workload(5, 64)
-    T, H, I, E = 64, m.hidden, m.inter, 384
+    active experts' weights stream from HBM."""
+    return build_moe_nv(torch, F, W, dev, 64, "moe_h7168_decode64", "hbm")
+
+
+def build_moe_prefill(torch, F, W, dev):
+    """NVFP4 MoE layer at hidden 7168 on a prefill batch of 16384 tokens: both
+    grouped GEMMs are bound by the fp16 MFMA the exact NV expansion feeds."""
+    return build_moe_nv(torch, F, W, dev, 16384, "moe_h7168_prefill16384", "mfma_bf16")
+
+
+def build_moe_nv(torch, F, W, dev, tokens, name, bound):
+    """NVFP4 MoE layer at hidden 7168 (inter 3072, 384 experts, top-6).  The
+    activation tensor scales are calibrated: s_x from amax(x), s_h from amax(h)
+    of one calibration call."""
+    m = W.moe_workload(5, tokens)
+    T, H, I, E = tokens, m.hidden, m.inter, 384
     active = sorted(set(m.ids.ravel().tolist()))
     w13c = torch.zeros((E, 2 * I, H // 2), dtype=torch.uint8, device=dev)
     w13s = torch.zeros((E, 2 * I, H // 16), dtype=torch.uint8, device=dev)
@@ -454,8 +477,8 @@ def build_moe_decode(torch, F, W, dev):
     act[1] = float(h.float().abs().max()) / 2688.0
     del h
     per_expert = 3 * H * I * (0.5 + 1 / 16)
-    return moe_stage(torch, F, "moe_h7168_decode64", F.FMT_NV, m, E, w13c, w13s, w2c, w2s, w13ts, w2ts, act, out, ws,
-                     len(active) * per_expert, 4.0 * S * H * I, 2.0 * S * H * I, "hbm")
+    return moe_stage(torch, F, name, F.FMT_NV, m, E, w13c, w13s, w2c, w2s, w13ts, w2ts, act, out, ws,
+                     len(active) * per_expert, 4.0 * S * H * I, 2.0 * S * H * I, bound)
 
 
 def cpu_baseline():

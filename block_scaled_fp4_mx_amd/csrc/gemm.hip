@@ -104,9 +104,9 @@ __global__ __launch_bounds__(kTileThreads, 1) void gemm_mx_256_kernel(
     const int64_t m0 = (int64_t)tm * kTileM, n0 = (int64_t)tn * kTileN;
     const int64_t kbytes = k / 2, kblocks = k / 32;
     const int t = threadIdx.x;
-    MxSlabSrc A, B;
-    mx_slab_src(A, ac, as, m0, m, kbytes, kblocks);
-    mx_slab_src(B, bc, bs, n0, n, kbytes, kblocks);
+    MxDenseSrc A, B;
+    mx_dense_src(A, ac, as, m0, m, kbytes, kblocks);
+    mx_dense_src(B, bc, bs, n0, n, kbytes, kblocks);
     v4f acc[kWaveFragsN][8];
 #pragma unroll
     for (int j = 0; j < kWaveFragsN; ++j)

@@ -27,6 +27,7 @@
 // logical chunk, which land on 8 different bank groups (no conflicts measured).
 #pragma once
 
+
 #include "mma_core.h"
 
 namespace fp4 {
@@ -65,8 +66,27 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 struct MxSlabSrc {
     const uint8_t* codes;
     const uint8_t* scales;
-    uint32_t off[4];
+    uint32_t offs[4];
     uint32_t soff;
+    __device__ __forceinline__ uint32_t off(int q) const { return offs[q]; }
+};
+
+// Dense operand whose slab rows are consecutive: the offsets are recomputed
+// at each copy from the row base (a few ALU ops), which keeps eight registers
+// free for the whole K loop.  The empty asm hides the row base's value, so the
+// compiler cannot hoist the eight products out of the loop again.
+struct MxDenseSrc {
+    const uint8_t* codes;
+    const uint8_t* scales;
+    int row0;              // operand row of this lane's code copy q = 0
+    int last;              // last valid operand row
+    uint32_t kbytes, chunk;
+    uint32_t soff;
+    __device__ __forceinline__ uint32_t off(int q) const {
+        int r = row0;
+        asm volatile("" : "+v"(r));
+        return (uint32_t)min(r + q * 8, last) * kbytes + chunk;
+    }
 };
 
 __device__ __forceinline__ int mx_code_row(int q) {
@@ -80,6 +100,17 @@ __device__ __forceinline__ uint32_t mx_chunk16() {
 
 // Dense operand: slab rows r0 .. r0 + 255 of a [rows, kbytes] code matrix,
 // clamped to its last row.
+__device__ __forceinline__ void mx_dense_src(MxDenseSrc& s, const uint8_t* codes, const uint8_t* scales, int64_t r0,
+                                             int64_t rows, int64_t kbytes, int64_t kblocks) {
+    s.codes = codes;
+    s.scales = scales;
+    s.row0 = (int)r0 + mx_code_row(0);
+    s.last = (int)rows - 1;
+    s.kbytes = (uint32_t)kbytes;
+    s.chunk = mx_chunk16();
+    s.soff = (uint32_t)min((int)r0 + mx_scale_row(), (int)rows - 1) * (uint32_t)kblocks;
+}
+
 __device__ __forceinline__ void mx_slab_src(MxSlabSrc& s, const uint8_t* codes, const uint8_t* scales, int64_t r0,
                                             int64_t rows, int64_t kbytes, int64_t kblocks) {
     s.codes = codes;
@@ -87,7 +118,7 @@ __device__ __forceinline__ void mx_slab_src(MxSlabSrc& s, const uint8_t* codes, 
     const int last = (int)rows - 1;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-        s.off[q] = (uint32_t)min((int)r0 + mx_code_row(q), last) * (uint32_t)kbytes + mx_chunk16();
+        s.offs[q] = (uint32_t)min((int)r0 + mx_code_row(q), last) * (uint32_t)kbytes + mx_chunk16();
     s.soff = (uint32_t)min((int)r0 + mx_scale_row(), last) * (uint32_t)kblocks;
 }
 
@@ -108,21 +139,23 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 
 __device__ __forceinline__ void wait_vm_zero() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-__device__ __forceinline__ void mx_issue_codes(MxCodes& st, const MxSlabSrc& A, const MxSlabSrc& B, int ks) {
+template <class SA, class SB>
+__device__ __forceinline__ void mx_issue_codes(MxCodes& st, const SA& A, const SB& B, int ks) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint8_t* ac = A.codes + (int64_t)ks * kRowBytes;
     const uint8_t* bc = B.codes + (int64_t)ks * kRowBytes;
     const uint32_t la = lds_addr(st.a) + wave * 4 * 1024, lb = lds_addr(st.b) + wave * 4 * 1024;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        dma16(ac, A.off[q], la + q * 1024);
-        dma16(bc, B.off[q], lb + q * 1024);
+        dma16(ac, A.off(q), la + q * 1024);
+        dma16(bc, B.off(q), lb + q * 1024);
     }
 }
 
 // Scale bytes of steps 2p and 2p + 1 (blocks 16p .. 16p + 15) of every row:
 // waves 0-3 fetch the A rows, waves 4-7 the B rows.
-__device__ __forceinline__ void mx_issue_scales(MxScales& sc, const MxSlabSrc& A, const MxSlabSrc& B, int p) {
+template <class SA, class SB>
+__device__ __forceinline__ void mx_issue_scales(MxScales& sc, const SA& A, const SB& B, int p) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (wave < 4)
         dma16(A.scales + (int64_t)p * 16, A.soff, lds_addr(sc.a) + wave * 1024);
@@ -170,8 +203,8 @@ __device__ __forceinline__ int scale_at(uint2 w, int s, int lk) {
 // Only the wave's first NF row fragments are computed (the grouped GEMMs pass
 // fewer for a segment's last rows); every wave takes part in the copies and
 // barriers whatever its NF.
-template <int NF>
-__device__ __forceinline__ void mx_tile_mainloop(MxSmem& sm, const MxSlabSrc& A, const MxSlabSrc& B, int64_t kblocks,
+template <int NF, class SA, class SB>
+__device__ __forceinline__ void mx_tile_mainloop(MxSmem& sm, const SA& A, const SB& B, int64_t kblocks,
                                                  v4f acc[kWaveFragsN][8]) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave >> 2, wn = wave & 3, lk = lane >> 4;
@@ -224,8 +257,9 @@ __device__ __forceinline__ void mx_tile_mainloop(MxSmem& sm, const MxSlabSrc& A,
 
 // The K loop for a wave of which only `rows` (from its first row on) are
 // needed: ceil(rows / 16) row fragments, at least 0 and at most 8.
-__device__ __forceinline__ void mx_tile_mainloop_rows(MxSmem& sm, const MxSlabSrc& A, const MxSlabSrc& B,
-                                                      int64_t kblocks, v4f acc[kWaveFragsN][8], int64_t rows) {
+template <class SA, class SB>
+__device__ __forceinline__ void mx_tile_mainloop_rows(MxSmem& sm, const SA& A, const SB& B, int64_t kblocks,
+                                                      v4f acc[kWaveFragsN][8], int64_t rows) {
     const int nf = rows <= 0 ? 0 : (rows >= 128 ? 8 : (int)((rows + 15) >> 4));
     switch (__builtin_amdgcn_readfirstlane(nf)) {
         case 8: mx_tile_mainloop<8>(sm, A, B, kblocks, acc); break;

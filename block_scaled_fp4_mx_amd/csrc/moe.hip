@@ -467,8 +467,8 @@ __global__ __launch_bounds__(kTileThreads, 1) void moe_gate_up_mx256_kernel(Gemm
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int64_t pos = min(r0 + mx_code_row(q), rend - 1);
-            A.off[q] = (uint32_t)(p.perm[pos] / p.topk) * kbytes + ch;
-            B.off[q] = (uint32_t)gu_weight_row(mx_code_row(q), c0, I) * kbytes + ch;
+            A.offs[q] = (uint32_t)(p.perm[pos] / p.topk) * kbytes + ch;
+            B.offs[q] = (uint32_t)gu_weight_row(mx_code_row(q), c0, I) * kbytes + ch;
         }
         const int64_t spos = min(r0 + mx_scale_row(), rend - 1);
         A.soff = (uint32_t)(p.perm[spos] / p.topk) * kblocks;
@@ -565,7 +565,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void moe_down_mx256_kernel(GemmPar
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int64_t pos = min(r0 + mx_code_row(q), rend - 1);
-        A.off[q] = (uint32_t)(inj ? p.perm[pos] : pos) * kbytes + ch;
+        A.offs[q] = (uint32_t)(inj ? p.perm[pos] : pos) * kbytes + ch;
     }
     const int64_t spos = min(r0 + mx_scale_row(), rend - 1);
     A.soff = (uint32_t)(inj ? p.perm[spos] : spos) * kblocks;

@@ -127,3 +127,12 @@ def test_moe_workload5_decode_sampled():
     """NVFP4 MoE at hidden 7168, decode batch of 64 tokens; one token per stage."""
     case, eq, sample = _full_case(5, "nv", sample=(17,))
     _all_checks(case, oracle_expect(case, sample, eq), fill=True)
+
+
+@pytest.mark.timeout(600)
+def test_moe_workload5_prefill_sampled():
+    """NVFP4 MoE at hidden 7168 on a prefill batch of 16384 tokens (98,304
+    routed slots, the 64-row two-stage NV tiles), in the launch the benchmark
+    times: routing checked whole, two tokens checked per stage."""
+    case, eq, sample = _full_case(5, "nv", tokens=16384, sample=(3, 12345))
+    _all_checks(case, oracle_expect(case, sample, eq), fill=True)
