@@ -391,13 +391,14 @@ def moe_stage(torch, F, name, fmt, m, E, w13c, w13s, w2c, w2s, w13ts, w2ts, act,
         "down": (bound, flops_dn, "2*H*I flop per routed slot"),
         "combine": ("hbm", S * H * 4 + T * H * 2, "4 B per slot per hidden column in, 2 B per token column out"),
     }
-    nv_tile = "<32, 3>" if T <= 128 else "<64, 2>"      # the launcher's decode / prefill NV tiles
+    nv_gu, nv_dn = (("moe_gate_up_nv_kernel<32, 3>", "moe_down_nv_kernel<32, 3>") if T <= 128 else
+                    ("moe_gate_up_nvw_kernel", "moe_down_nvw_kernel"))   # the launcher's decode / wide NV tiles
     names = {"quantize_x": "mx_quantize_kernel" if fmt == F.FMT_MX else "nv_quantize_kernel",
              "routing": "route_count_kernel + route_scan_kernel + route_place_kernel",
              "gate_up": "moe_gate_up_mx256_kernel" if fmt == F.FMT_MX else
-             f"expand_nv16_kernel (x) + moe_gate_up_nv_kernel{nv_tile}",
+             f"expand_nv16_kernel (x) + {nv_gu}",
              "down": "moe_down_mx256_kernel" if fmt == F.FMT_MX else
-             f"expand_nv16_kernel (h) + moe_down_nv_kernel{nv_tile}",
+             f"expand_nv16_kernel (h) + {nv_dn}",
              "combine": "combine_kernel"}
     if bound == "hbm":
         # decode: the expert weights dominate the bytes of both GEMMs

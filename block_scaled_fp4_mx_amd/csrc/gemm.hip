@@ -13,14 +13,13 @@
 // significant bits) and uses v_mfma_f32_16x16x32_bf16; the two fp32 tensor
 // scales multiply the fp32 accumulator at the end.
 #include "gemm_mx_tile.h"
-#include "gemm_nv_tile.h"
+#include "gemm_nv_wide.h"
 #include "mma_core.h"
 
 namespace fp4 {
 namespace {
 
 constexpr int kBM = 128, kBN = 128, kThreads = 256;
-constexpr int kNvGemmM = 64;    // A rows per NV GEMM tile
 
 // 16x16 accumulator layout: lane holds rows 4*(lane/16) + r, column lane % 16.
 __device__ __forceinline__ void store_tile(const v4f acc[4][4], void* c, int c_f32, int64_t ldc, int64_t m,
@@ -169,49 +168,54 @@ __global__ __launch_bounds__(kTileThreads, 1) void gemm_mx_256_kernel(
     }
 }
 
-// NV GEMM on 64 x 256 tiles (gemm_nv_tile.h): B expanded to fp16 in
+// NV GEMM on the wide 64 x 512 tiles (gemm_nv_wide.h): B expanded to fp16 in
 // registers, A expanded into LDS each step, fp16 MFMA, tensor scales in the
 // epilogue; C goes through LDS and leaves in whole-row 16-byte pieces.
 __global__ __launch_bounds__(kNvThreads, 1) void gemm_nv_tile_kernel(
     const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as, const float* __restrict__ ats,
     const uint8_t* __restrict__ bc, const uint8_t* __restrict__ bs, const float* __restrict__ bts, int64_t m,
     int64_t n, int64_t k, void* __restrict__ c, int c_f32, int64_t ldc, int tiles_m, int tiles_n) {
-    __shared__ __align__(16) NvSmemT<kNvGemmM, 2, true> sm;
+    __shared__ __align__(16) NwSmem<true> sm;
     int tm, tn;
     tile_coords(tiles_m, tiles_n, tm, tn);
-    const int64_t m0 = (int64_t)tm * kNvGemmM, n0 = (int64_t)tn * kNvTileN;
+    const int64_t m0 = (int64_t)tm * kNwM, n0 = (int64_t)tn * kNwN;
     const uint32_t kb = (uint32_t)(k / 2), kg = (uint32_t)(k / 16);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int lr = lane & 15, lq = lane >> 4;
-    NvSrc S{};
+    NwSrc S{};
     S.ac = ac;
     S.as = as;
     S.b = bc;
     S.s = bs;
-    S.acoff = (uint32_t)min(m0 + wave * 8 + (lane >> 3), m - 1) * kb + (uint32_t)(lane & 7) * 16;
-    S.asoff = (uint32_t)min(m0 + lane, m - 1) * kg;
+    S.acoff = (uint32_t)min(m0 + nw_ac_row(), m - 1) * kb + nw_ac_chunk();
+    S.asoff = (uint32_t)min(m0 + nw_as_row(), m - 1) * kg + nw_s_col();
 #pragma unroll
-    for (int q = 0; q < 4; ++q) S.boff[q] = (uint32_t)min(n0 + mx_code_row(q), n - 1) * kb + mx_chunk16();
-    S.soff = (uint32_t)min(n0 + mx_scale_row(), n - 1) * kg;
-    v4f acc[4][2];
+    for (int q = 0; q < 4; ++q) {
+        const int brow = nw_b_row(q);
+        S.boff[q] = (uint32_t)min(n0 + brow, n - 1) * kb + nw_b_chunk(brow);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) S.soff[j] = (uint32_t)min(n0 + nw_s_row(j), n - 1) * kg + nw_s_col();
+    v4f acc[4][4];
 #pragma unroll
     for (int mf = 0; mf < 4; ++mf)
 #pragma unroll
-        for (int nf = 0; nf < 2; ++nf) acc[mf][nf] = v4f{0.f, 0.f, 0.f, 0.f};
-    nv_tile_mainloop_rows(sm, S, (int)(k / 256), acc, m - m0);
+        for (int nf = 0; nf < 4; ++nf) acc[mf][nf] = v4f{0.f, 0.f, 0.f, 0.f};
+    nw_mainloop_rows(sm, S, (int)(k / kNwK), acc, m - m0);
 
     const float scale = __fmul_rn(*ats, *bts);
     const int esz = c_f32 ? 4 : 2;
-    const int rowb = kNvTileN * esz + 16;            // padded LDS row pitch (bytes)
+    const int rowb = kNwN * esz + 16;                // padded LDS row pitch (bytes)
+    static_assert(kNwM * (kNwN * 4 + 16) <= (int)sizeof(sm), "C staging exceeds the tile's LDS");
     uint8_t* csm = reinterpret_cast<uint8_t*>(&sm);
     __syncthreads();                                 // the stages are free
 #pragma unroll
     for (int mf = 0; mf < 4; ++mf)
 #pragma unroll
-        for (int nf = 0; nf < 2; ++nf)
+        for (int nf = 0; nf < 4; ++nf)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int row = mf * 16 + lq * 4 + r, col = wave * 32 + nf * 16 + lr;
+                const int row = mf * 16 + lq * 4 + r, col = wave * 64 + nf * 16 + lr;
                 const float v = __fmul_rn(acc[mf][nf][r], scale);
                 if (c_f32)
                     *reinterpret_cast<float*>(csm + row * rowb + col * 4) = v;
@@ -219,9 +223,9 @@ __global__ __launch_bounds__(kNvThreads, 1) void gemm_nv_tile_kernel(
                     *reinterpret_cast<uint16_t*>(csm + row * rowb + col * 2) = (uint16_t)f32_to_bf16_rne(v);
             }
     __syncthreads();
-    const int chunks_row = kNvTileN * esz / 16;
+    const int chunks_row = kNwN * esz / 16;
     const bool vec = ((ldc * esz) & 15) == 0;
-    for (int q = threadIdx.x; q < kNvGemmM * chunks_row; q += kNvThreads) {
+    for (int q = threadIdx.x; q < kNwM * chunks_row; q += kNvThreads) {
         const int row = q / chunks_row, ch = q - row * chunks_row;
         const int64_t grow = m0 + row, gcol = n0 + ch * (16 / esz);
         if (grow >= m || gcol >= n) continue;
@@ -262,9 +266,9 @@ hipError_t launch_gemm_nv(const uint8_t* ac, const uint8_t* as, const float* ats
                           const uint8_t* bc, const uint8_t* bs, const float* bts,
                           int64_t m, int64_t n, int64_t k, void* c, int c_f32, int64_t ldc,
                           hipStream_t s) {
-    const int64_t tiles_m = (m + kNvGemmM - 1) / kNvGemmM, tiles_n = (n + kNvTileN - 1) / kNvTileN;
+    const int64_t tiles_m = (m + kNwM - 1) / kNwM, tiles_n = (n + kNwN - 1) / kNwN;
     const bool small_ops = m * (k / 2) < (1ll << 31) && n * (k / 2) < (1ll << 31);
-    if (k % 256 == 0 && k > 0 && small_ops && tiles_m * tiles_n >= 64 && tiles_m * tiles_n < (1ll << 31)) {
+    if (k % kNwK == 0 && k > 0 && small_ops && tiles_m * tiles_n >= 32 && tiles_m * tiles_n < (1ll << 31)) {
         gemm_nv_tile_kernel<<<(unsigned)(tiles_m * tiles_n), kNvThreads, 0, s>>>(
             ac, as, ats, bc, bs, bts, m, n, k, c, c_f32, ldc, (int)tiles_m, (int)tiles_n);
     } else {

@@ -120,24 +120,23 @@ __device__ __forceinline__ void nv_issue(NvStageT<TM, ACODES>& sm, const NvSrc& 
     }
 }
 
-// fp32 scale operand (2^e) and fp16 multiplier pair of an E4M3 group byte g:
-// normal (e_f > 0): s_g = 2^(e_f - 7) (1 + m/8); subnormal: s_g = 2^-9 m; g = 0
-// gives the multiplier 0.
-__device__ __forceinline__ void nv_scale_parts(uint32_t g, float& p2, h2_t& mult) {
-    const uint32_t ef = (g >> 3) & 15u, m = g & 7u;
-    const bool normal = ef != 0u;
-    p2 = __uint_as_float((normal ? ef + 120u : 118u) << 23);
-    const uint16_t mb = normal ? (uint16_t)(0x3C00u | (m << 7)) : __builtin_bit_cast(uint16_t, (_Float16)(float)m);
-    const h2_t mm = __builtin_bit_cast(h2_t, (uint32_t)mb * 0x10001u);
-    mult = mm;
+// Two E4M3 group bytes (bits 15:0 of g2) -> the fp16 pair {s_g0, s_g1}.  Every
+// E4M3 value, subnormals included, is an fp16 normal number, so the conversion
+// (v_cvt_scalef32_pk_f16_fp8 with scale 1) is exact.
+__device__ __forceinline__ h2_t nv_scale_pair(uint32_t g2) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(g2, 1.0f, false);
 }
 
-// Eight codes (one word) of one group -> 8 exact fp16 values code * s_g.
-__device__ __forceinline__ h8_t nv_expand8(uint32_t w, float p2, h2_t mult) {
-    const h2_t a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, p2, 0) * mult;
-    const h2_t b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, p2, 1) * mult;
-    const h2_t c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, p2, 2) * mult;
-    const h2_t d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, p2, 3) * mult;
+// Eight codes (one word) of one group -> 8 exact fp16 values code * s_g.  The
+// codes convert exactly (scale 1); the product of an E2M1 and an E4M3 value has
+// at most 6 significant bits and lies in [2^-10, 2688] (or is zero), so the
+// packed fp16 multiply rounds nothing.
+__device__ __forceinline__ h8_t nv_expand8(uint32_t w, _Float16 s) {
+    const h2_t s2 = {s, s};
+    const h2_t a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2;
+    const h2_t b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s2;
+    const h2_t c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s2;
+    const h2_t d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s2;
     return h8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
@@ -150,11 +149,9 @@ __device__ __forceinline__ void nv_expand_a(NvStageT<TM, true>& st) {
         const int id = (int)threadIdx.x + q * kNvThreads;
         const int row = id >> 4, g = id & 15;
         const uint2 c = *reinterpret_cast<const uint2*>(&st.ac[row * kNvBRow + g * 8]);
-        float p2;
-        h2_t mult;
-        nv_scale_parts(st.as[row * kNvSRow + g], p2, mult);
-        *reinterpret_cast<h8_t*>(&st.a[row * kNvARow + (((2 * g) ^ (row & 15)) << 4)]) = nv_expand8(c.x, p2, mult);
-        *reinterpret_cast<h8_t*>(&st.a[row * kNvARow + (((2 * g + 1) ^ (row & 15)) << 4)]) = nv_expand8(c.y, p2, mult);
+        const _Float16 sg = nv_scale_pair(st.as[row * kNvSRow + g])[0];
+        *reinterpret_cast<h8_t*>(&st.a[row * kNvARow + (((2 * g) ^ (row & 15)) << 4)]) = nv_expand8(c.x, sg);
+        *reinterpret_cast<h8_t*>(&st.a[row * kNvARow + (((2 * g + 1) ^ (row & 15)) << 4)]) = nv_expand8(c.y, sg);
     }
 }
 template <int TM>
@@ -199,14 +196,11 @@ __device__ __forceinline__ void nv_tile_mainloop(NvSmemT<TM, NS, ACODES>& sm, co
                 const int row = wave * 32 + nf * 16 + lr;
                 const uint4 c = *reinterpret_cast<const uint4*>(&st.b[row * kNvBRow + (((hs * 4 + lq) ^ (row & 7)) * 16)]);
                 const uint32_t sg = *reinterpret_cast<const uint16_t*>(&st.s[row * kNvSRow + hs * 8 + lq * 2]);
-                float p0, p1;
-                h2_t m0, m1;
-                nv_scale_parts(sg & 0xFFu, p0, m0);
-                nv_scale_parts(sg >> 8, p1, m1);
-                bx[nf][0] = nv_expand8(c.x, p0, m0);
-                bx[nf][1] = nv_expand8(c.y, p0, m0);
-                bx[nf][2] = nv_expand8(c.z, p1, m1);
-                bx[nf][3] = nv_expand8(c.w, p1, m1);
+                const h2_t sp = nv_scale_pair(sg);
+                bx[nf][0] = nv_expand8(c.x, sp[0]);
+                bx[nf][1] = nv_expand8(c.y, sp[0]);
+                bx[nf][2] = nv_expand8(c.z, sp[1]);
+                bx[nf][3] = nv_expand8(c.w, sp[1]);
             }
             // A: fp16 rows, chunk hs*16 + 4 lq + i of each row
 #pragma unroll

@@ -19,6 +19,7 @@
 // combine of tokens to experts ("DeepSeek-V4" article, section 6.1).
 #include "gemm_mx_tile.h"
 #include "gemm_nv_tile.h"
+#include "gemm_nv_wide.h"
 #include "mma_core.h"
 #include "quant_device.h"
 
@@ -632,10 +633,8 @@ __global__ __launch_bounds__(kThreads) void expand_nv16_kernel(const uint8_t* __
     const int64_t stride = (int64_t)gridDim.x * kThreads;
     for (int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x; u < total; u += stride) {
         const uint2 c = *reinterpret_cast<const uint2*>(codes + u * 8);
-        float p2;
-        h2_t mult;
-        nv_scale_parts(scales[u], p2, mult);
-        const h8_t a = nv_expand8(c.x, p2, mult), b = nv_expand8(c.y, p2, mult);
+        const _Float16 sg = nv_scale_pair(scales[u])[0];
+        const h8_t a = nv_expand8(c.x, sg), b = nv_expand8(c.y, sg);
         uint4* o = reinterpret_cast<uint4*>(out + u * 16);
         o[0] = __builtin_bit_cast(uint4, a);
         o[1] = __builtin_bit_cast(uint4, b);
@@ -825,6 +824,204 @@ __global__ __launch_bounds__(kNvThreads, 1) void moe_down_nv_kernel(GemmParams p
     }
 }
 
+// ---------------------------------------------------------------- wide NV tiles
+// Prefill-sized batches: 64 routed rows x 512 weight rows per tile (the wide
+// NV tile).  gate/up: wave w owns slab rows w*64 .. +63: 32 w1 rows
+// (intermediate columns c0 + w*32 ..) then the 32 w3 rows of the same
+// columns, so fragments 0-1 hold g and fragments 2-3 the matching u.  A tile
+// covers 256 intermediate columns.
+constexpr int kNwGuCols = 256;
+
+__device__ __forceinline__ int64_t gu_nw_row(int slab_row, int64_t c0, int64_t I) {
+    const int w = slab_row >> 6, q = slab_row & 63;
+    return (q >= 32 ? I : 0) + c0 + w * 32 + (q & 31);
+}
+
+__global__ __launch_bounds__(kNvThreads, 1) void moe_gate_up_nvw_kernel(GemmParams p) {
+    __shared__ __align__(16) NwSmem<false> sm;
+    static_assert(kNwM * kNwGuCols * 2 <= (int)sizeof(sm), "h tile exceeds the wide tile's LDS");
+    const int tile = blockIdx.y;
+    if (tile >= *p.ntiles) return;
+    const int e = p.tile_e[tile];
+    const int64_t r0 = p.tile_r[tile];
+    const int64_t rend = p.offsets[e + 1];
+    const int64_t c0 = (int64_t)blockIdx.x * kNwGuCols;
+    const int64_t H = p.H, I = p.I;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lr = lane & 15, lq = lane >> 4;
+    const bool injected = p.dbg.gate_up_in != nullptr;
+
+    v4f acc[4][4];
+#pragma unroll
+    for (int mf = 0; mf < 4; ++mf)
+#pragma unroll
+        for (int nf = 0; nf < 4; ++nf) acc[mf][nf] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    if (!injected) {
+        NwSrc S{};
+        S.a = reinterpret_cast<const uint8_t*>(p.x16);
+        S.b = p.w13c + (int64_t)e * (2 * I) * (H / 2);
+        S.s = p.w13s + (int64_t)e * (2 * I) * (H / 16);
+        const uint32_t apitch = (uint32_t)(H * 2), bpitch = (uint32_t)(H / 2), spitch = (uint32_t)(H / 16);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int arow = nw_a_row(q);
+            const int64_t pos = min(r0 + arow, rend - 1);
+            S.aoff[q] = (uint32_t)(p.perm[pos] / p.topk) * apitch + nw_a_chunk(arow);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int brow = nw_b_row(q);
+            S.boff[q] = (uint32_t)gu_nw_row(brow, c0, I) * bpitch + nw_b_chunk(brow);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) S.soff[j] = (uint32_t)gu_nw_row(nw_s_row(j), c0, I) * spitch + nw_s_col();
+        nw_mainloop_rows(sm, S, (int)(H / kNwK), acc, rend - r0);
+    } else {
+        // g|u given per slot (debug injection, tensor scales included)
+#pragma unroll
+        for (int mf = 0; mf < 4; ++mf)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t pos = r0 + mf * 16 + lq * 4 + r;
+                if (pos >= rend) continue;
+                const float* src = p.dbg.gate_up_in + (int64_t)p.perm[pos] * 2 * I;
+#pragma unroll
+                for (int nf = 0; nf < 2; ++nf) {
+                    acc[mf][nf][r] = src[c0 + wave * 32 + nf * 16 + lr];
+                    acc[mf][nf + 2][r] = src[I + c0 + wave * 32 + nf * 16 + lr];
+                }
+            }
+    }
+    __syncthreads();   // the h tile reuses the stages
+
+    const float gscale = injected ? 1.0f : __fmul_rn(p.act_ts[0], p.w13ts[e]);
+    uint16_t* hsm = reinterpret_cast<uint16_t*>(&sm);      // 64 rows x 256 bf16
+#pragma unroll
+    for (int mf = 0; mf < 4; ++mf)
+#pragma unroll
+        for (int nf = 0; nf < 2; ++nf)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int rl = mf * 16 + lq * 4 + r;
+                const int cl = wave * 32 + nf * 16 + lr;
+                const float g = injected ? acc[mf][nf][r] : __fmul_rn(acc[mf][nf][r], gscale);
+                const float u = injected ? acc[mf][nf + 2][r] : __fmul_rn(acc[mf][nf + 2][r], gscale);
+                const uint32_t hb = f32_to_bf16_rne(silu_mul(g, u));
+                hsm[rl * kNwGuCols + cl] = (uint16_t)hb;
+                const int64_t pos = r0 + rl;
+                if (pos < rend && (p.dbg.gate_up || p.dbg.h_bf16)) {
+                    const int64_t slot = p.perm[pos];
+                    if (p.dbg.gate_up) {
+                        p.dbg.gate_up[slot * 2 * I + c0 + cl] = g;
+                        p.dbg.gate_up[slot * 2 * I + I + c0 + cl] = u;
+                    }
+                    if (p.dbg.h_bf16) static_cast<uint16_t*>(p.dbg.h_bf16)[slot * I + c0 + cl] = (uint16_t)hb;
+                }
+            }
+    __syncthreads();
+    // quantize the 64 x 256 h tile: unit = 8 consecutive columns of one row; a
+    // 16-group spans 2 consecutive lanes
+    const double st_h = (double)p.act_ts[1];
+#pragma unroll
+    for (int q = 0; q < (kNwM * kNwGuCols / 8) / kNvThreads; ++q) {
+        const int unit = threadIdx.x + q * kNvThreads;
+        const int rl = unit / (kNwGuCols / 8), cu = unit % (kNwGuCols / 8);
+        const uint4 v = *reinterpret_cast<const uint4*>(&hsm[rl * kNwGuCols + cu * 8]);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        uint32_t sb;
+        const uint32_t packed = nv_quant8(w, st_h, sb);
+        const int64_t pos = r0 + rl;
+        if (pos < rend) {
+            const int64_t col = c0 + cu * 8;
+            reinterpret_cast<uint32_t*>(p.hc + pos * (I / 2) + col / 2)[0] = packed;
+            const bool lead = (cu & 1) == 0;
+            if (lead) p.hs[pos * (I / 16) + col / 16] = (uint8_t)sb;
+            if (p.dbg.h_codes || p.dbg.h_scales) {
+                const int64_t slot = p.perm[pos];
+                if (p.dbg.h_codes) reinterpret_cast<uint32_t*>(p.dbg.h_codes + slot * (I / 2) + col / 2)[0] = packed;
+                if (p.dbg.h_scales && lead) p.dbg.h_scales[slot * (I / 16) + col / 16] = (uint8_t)sb;
+            }
+        }
+    }
+}
+
+// down: the fp16 expansion of Q(h) for the tile's rows times w2 rows n0 .. n0 + 511
+// (rows past H are clamped and their columns never stored).
+constexpr int kNwYRow = kNwN + 4;   // fp32 row pitch of the combine staging tile
+
+__global__ __launch_bounds__(kNvThreads, 1) void moe_down_nvw_kernel(GemmParams p) {
+    __shared__ __align__(16) NwSmem<false> sm;
+    static_assert(kNwM * kNwYRow * 4 <= (int)sizeof(sm), "staging tile exceeds the wide tile's LDS");
+    const int tile = blockIdx.y;
+    if (tile >= *p.ntiles) return;
+    const int e = p.tile_e[tile];
+    const int64_t r0 = p.tile_r[tile];
+    const int64_t rend = p.offsets[e + 1];
+    const int64_t n0 = (int64_t)blockIdx.x * kNwN;
+    const int64_t H = p.H, I = p.I;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lr = lane & 15, lq = lane >> 4;
+
+    NwSrc S{};
+    S.a = reinterpret_cast<const uint8_t*>(p.h16);
+    S.b = p.w2c + (int64_t)e * H * (I / 2);
+    S.s = p.w2s + (int64_t)e * H * (I / 16);
+    const uint32_t apitch = (uint32_t)(I * 2), bpitch = (uint32_t)(I / 2), spitch = (uint32_t)(I / 16);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int arow = nw_a_row(q);
+        const int64_t pos = min(r0 + arow, rend - 1);
+        S.aoff[q] = (uint32_t)(p.h16_by_slot ? p.perm[pos] : pos) * apitch + nw_a_chunk(arow);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int brow = nw_b_row(q);
+        S.boff[q] = (uint32_t)min(n0 + brow, H - 1) * bpitch + nw_b_chunk(brow);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) S.soff[j] = (uint32_t)min(n0 + nw_s_row(j), H - 1) * spitch + nw_s_col();
+
+    v4f acc[4][4];
+#pragma unroll
+    for (int mf = 0; mf < 4; ++mf)
+#pragma unroll
+        for (int nf = 0; nf < 4; ++nf) acc[mf][nf] = v4f{0.f, 0.f, 0.f, 0.f};
+    nw_mainloop_rows(sm, S, (int)(I / kNwK), acc, rend - r0);
+    __syncthreads();   // the staging tile reuses the stages
+
+    const float yscale = __fmul_rn(p.act_ts[1], p.w2ts[e]);
+    float* ysm = reinterpret_cast<float*>(&sm);
+#pragma unroll
+    for (int mf = 0; mf < 4; ++mf)
+#pragma unroll
+        for (int nf = 0; nf < 4; ++nf)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int rl = mf * 16 + lq * 4 + r;
+                const int cl = wave * 64 + nf * 16 + lr;
+                const float y = __fmul_rn(acc[mf][nf][r], yscale);
+                ysm[rl * kNwYRow + cl] = y;
+                const int64_t pos = r0 + rl;
+                if (p.dbg.y && pos < rend && n0 + cl < H) p.dbg.y[(int64_t)p.perm[pos] * H + n0 + cl] = y;
+            }
+    __syncthreads();
+    for (int rr = wave; rr < kNwM; rr += kNvThreads / 64) {
+        const int64_t pos = r0 + rr;
+        if (pos >= rend) break;     // rows are in order: the rest of this wave's rows are past the end too
+        const int64_t slot = p.perm[pos];
+        const float wgt = p.weights[slot];
+#pragma unroll
+        for (int hh = 0; hh < kNwN / 256; ++hh) {
+            const int col = hh * 256 + lane * 4;
+            if (n0 + col >= H) break;     // H is a multiple of 4: a float4 is wholly in or out
+            const float4 v = *reinterpret_cast<const float4*>(&ysm[rr * kNwYRow + col]);
+            *reinterpret_cast<float4*>(p.ybuf + slot * H + n0 + col) =
+                make_float4(__fmul_rn(wgt, v.x), __fmul_rn(wgt, v.y), __fmul_rn(wgt, v.z), __fmul_rn(wgt, v.w));
+        }
+    }
+}
+
 // out[t] = bf16(sum over j of w * y of slot t*topk + j), summed in fp32 in
 // order j = 0 .. topk-1 over the slots whose expert id is in range.
 __global__ __launch_bounds__(kThreads) void combine_kernel(const float4* __restrict__ ybuf,
@@ -896,7 +1093,8 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t s) {
     // 2. routing metadata
     route_count_kernel<<<(unsigned)L.nblk, kRouteSlots, 0, s>>>(a.ids, S, E, blockbase);
     // LDS-staged tiles: MX with hidden and inter multiples of 512 (256 routed
-    // rows per tile), NV with multiples of 256 (64 routed rows per tile)
+    // rows per tile), NV with multiples of 256 (32 routed rows per tile for
+    // decode batches, 64 for larger ones)
     const bool tiled = a.fmt == FP4_FMT_MX && H % 512 == 0 && I % 512 == 0;
     const bool nv_tiled = a.fmt == FP4_FMT_NV && H % 256 == 0 && I % 256 == 0;
     const bool nv_decode = T <= kNvDecodeTokens;       // 32-row, three-stage NV tiles
@@ -938,18 +1136,21 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t s) {
     // 3. gate/up + SiLU*mul + quantize h; 4. down + weighted combine
     if (nv_tiled) {
         expand_nv16_kernel<<<stream_grid(T * H / 16), kThreads, 0, s>>>(xc, xs, T, H, x16);
-        const dim3 g_gu((unsigned)(I / kNvGuCols), (unsigned)L.max_tiles);
-        const dim3 g_dn((unsigned)(H / kNvTileN), (unsigned)L.max_tiles);
-        if (nv_decode) moe_gate_up_nv_kernel<32, 3><<<g_gu, kNvThreads, 0, s>>>(p);
-        else moe_gate_up_nv_kernel<64, 2><<<g_gu, kNvThreads, 0, s>>>(p);
+        if (nv_decode)
+            moe_gate_up_nv_kernel<32, 3><<<dim3((unsigned)(I / kNvGuCols), (unsigned)L.max_tiles), kNvThreads, 0, s>>>(p);
+        else
+            moe_gate_up_nvw_kernel<<<dim3((unsigned)(I / kNwGuCols), (unsigned)L.max_tiles), kNvThreads, 0, s>>>(p);
         if ((err = hipGetLastError()) != hipSuccess || (err = mark(3)) != hipSuccess) return err;
         if (a.dbg.h_codes_in)
             expand_nv16_kernel<<<stream_grid(S * I / 16), kThreads, 0, s>>>(a.dbg.h_codes_in, a.dbg.h_scales_in, S, I,
                                                                              h16);
         else
             expand_nv16_kernel<<<stream_grid(S * I / 16), kThreads, 0, s>>>(hc, hs, S, I, h16);
-        if (nv_decode) moe_down_nv_kernel<32, 3><<<g_dn, kNvThreads, 0, s>>>(p);
-        else moe_down_nv_kernel<64, 2><<<g_dn, kNvThreads, 0, s>>>(p);
+        if (nv_decode)
+            moe_down_nv_kernel<32, 3><<<dim3((unsigned)(H / kNvTileN), (unsigned)L.max_tiles), kNvThreads, 0, s>>>(p);
+        else
+            moe_down_nvw_kernel<<<dim3((unsigned)((H + kNwN - 1) / kNwN), (unsigned)L.max_tiles), kNvThreads, 0, s>>>(
+                p);
         if ((err = hipGetLastError()) != hipSuccess || (err = mark(4)) != hipSuccess) return err;
     } else if (tiled) {
         const dim3 g_gu((unsigned)(I / kGu2Cols), (unsigned)L.max_tiles);

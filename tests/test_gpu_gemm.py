@@ -130,7 +130,7 @@ def test_gemm_nv_ragged(m, n, k):
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("pad", [0, 4])
 def test_gemm_nv_tiled_ragged_strided(dtype, pad):
-    """K a multiple of 256 and at least 64 tiles: the 64x256 LDS-staged NV tile
+    """K a multiple of 128 and at least 32 tiles: the 64x512 LDS-staged NV tile
     (A expanded to fp16 in LDS, B in registers), ragged M and N, both output
     types and a padded output row pitch."""
     m, n, k = 1000, 1100, 1024
@@ -147,6 +147,13 @@ def test_gemm_nv_tiled_ragged_strided(dtype, pad):
     _assert_within(c, Cref, S)
     if pad:
         assert torch.isnan(buf[:, n:].float()).all()
+
+
+@pytest.mark.parametrize("m,n,k", [(700, 1500, 128), (640, 2048, 384), (2000, 520, 256)])
+def test_gemm_nv_tiled_short_k(m, n, k):
+    """The tiled NV path with one, two and three K steps (the three-stage copy
+    ring before it is full) and N tails of 476 and 8 columns."""
+    _nv_case(W.random_linear(m + n + k, m, n, k, outlier_p=0.01), torch.float32)
 
 
 def test_gemm_nv_4096_sampled():
