@@ -195,11 +195,55 @@ __device__ __forceinline__ int scale_at(uint2 w, int s, int lk) {
     return (int)((s ? w.y : w.x) >> (8 * lk));
 }
 
-// Full K loop of one 256 x 256 tile; acc zeroed by the caller.  The loop runs
-// over half-steps (128 K values), so each accumulator has one MFMA per
-// iteration.  At the start of step ks the copies of step ks have landed (wait +
-// barrier) and those of step ks + 1 (and, when ks + 1 is even, the scales of
-// steps ks + 1 and ks + 2) are issued into the buffers step ks - 1 used.
+// One half-step's fragments and scale operands in registers.
+struct MxFrags {
+    v8i a[8], b[kWaveFragsN];
+    int sa[8], sb[kWaveFragsN];
+};
+
+// Reads half-step S (K values S*128 .. of the step) of the stage `codes` for
+// the wave's first NF row fragments; wsa / wsb hold the step's scale words.
+template <int NF, int S>
+__device__ __forceinline__ void mx_read_half(MxFrags& f, const MxCodes& codes, const MxLdsBase& lb, const uint2* wsa,
+                                             const uint2* wsb, int lk) {
+    const uint8_t* st_a = codes.a + lb.a[S];
+    const uint8_t* st_b = codes.b + lb.b[S];
+#pragma unroll
+    for (int i = 0; i < NF; ++i) {
+        f.a[i] = frag_at(st_a + i * 16 * kRowBytes);
+        f.sa[i] = scale_at(wsa[i], S, lk);
+    }
+#pragma unroll
+    for (int j = 0; j < kWaveFragsN; ++j) {
+        f.b[j] = frag_at(st_b + j * 16 * kRowBytes);
+        f.sb[j] = scale_at(wsb[j], S, lk);
+    }
+}
+
+template <int NF>
+__device__ __forceinline__ void mx_mfma_half(v4f acc[kWaveFragsN][8], const MxFrags& f) {
+#pragma unroll
+    for (int j = 0; j < kWaveFragsN; ++j)
+#pragma unroll
+        for (int i = 0; i < NF; ++i)
+            acc[j][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f.b[j], f.a[i], acc[j][i], 4, 4, 0, f.sb[j], 0,
+                                                                           f.sa[i]);
+}
+
+// Full K loop of one 256 x 256 tile; acc zeroed by the caller.  At the start of
+// step ks the copies of step ks have landed (wait + barrier) and those of step
+// ks + 1 (and, when ks + 1 is even, the scales of steps ks + 1 and ks + 2) are
+// issued into the buffers step ks - 1 used.  Each step is two half-steps of
+// 128 K values: read the half's fragments from LDS, then one MFMA per
+// accumulator.
+//
+// Half of the waves (those whose index has bit 1 set) run half a step behind
+// the others: they hold the fragments of a step's second half across the
+// barrier and multiply them at the start of the next step.  In lock step every
+// wave would read its fragments from LDS right after each barrier while the
+// matrix cores idle; staggered, half the waves read while the other half
+// multiply.  (Of the splits tried, this one measured fastest; the result does
+// not depend on it, since every accumulator still sees its K blocks in order.)
 // Only the wave's first NF row fragments are computed (the grouped GEMMs pass
 // fewer for a segment's last rows); every wave takes part in the copies and
 // barriers whatever its NF.
@@ -208,51 +252,34 @@ __device__ __forceinline__ void mx_tile_mainloop(MxSmem& sm, const SA& A, const 
                                                  v4f acc[kWaveFragsN][8]) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave >> 2, wn = wave & 3, lk = lane >> 4;
+    const bool lag = (__builtin_amdgcn_readfirstlane(wave) & 2) != 0;
     const int nsteps = (int)(kblocks / kStepBlocks);
     const MxLdsBase lb = mx_lds_base(wm, wn, lane);
     mx_issue_codes(sm.codes[0], A, B, 0);
     mx_issue_scales(sm.scales[0], A, B, 0);
     uint2 wsa[8], wsb[kWaveFragsN];
-    for (int hs = 0; hs < 2 * nsteps; ++hs) {
-        const int ks = hs >> 1, s = hs & 1;
-        if (s == 0) {
-            wait_vm_zero();
-            __syncthreads();
-            if (ks + 1 < nsteps) {
-                mx_issue_codes(sm.codes[(ks + 1) & 1], A, B, ks + 1);
-                if (((ks + 1) & 1) == 0) mx_issue_scales(sm.scales[((ks + 1) >> 1) & 1], A, B, (ks + 1) >> 1);
-            }
-            if (NF == 0) continue;
-            const uint8_t* sc_a = sm.scales[(ks >> 1) & 1].a + (ks & 1) * 8;
-            const uint8_t* sc_b = sm.scales[(ks >> 1) & 1].b + (ks & 1) * 8;
-#pragma unroll
-            for (int i = 0; i < NF; ++i) wsa[i] = *reinterpret_cast<const uint2*>(sc_a + lb.sa + i * 16 * kScaleRow);
-#pragma unroll
-            for (int j = 0; j < kWaveFragsN; ++j)
-                wsb[j] = *reinterpret_cast<const uint2*>(sc_b + lb.sb + j * 16 * kScaleRow);
+    MxFrags f;
+    for (int ks = 0; ks < nsteps; ++ks) {
+        wait_vm_zero();
+        __syncthreads();
+        if (ks + 1 < nsteps) {
+            mx_issue_codes(sm.codes[(ks + 1) & 1], A, B, ks + 1);
+            if (((ks + 1) & 1) == 0) mx_issue_scales(sm.scales[((ks + 1) >> 1) & 1], A, B, (ks + 1) >> 1);
         }
         if (NF == 0) continue;
-        const uint8_t* st_a = sm.codes[ks & 1].a + (s ? lb.a[1] : lb.a[0]);
-        const uint8_t* st_b = sm.codes[ks & 1].b + (s ? lb.b[1] : lb.b[0]);
-        v8i a[8], b[kWaveFragsN];
-        int sa[8], sb[kWaveFragsN];
+        if (lag && ks > 0) mx_mfma_half<NF>(acc, f);          // second half of step ks - 1
+        const uint8_t* sc_a = sm.scales[(ks >> 1) & 1].a + (ks & 1) * 8;
+        const uint8_t* sc_b = sm.scales[(ks >> 1) & 1].b + (ks & 1) * 8;
 #pragma unroll
-        for (int i = 0; i < NF; ++i) {
-            a[i] = frag_at(st_a + i * 16 * kRowBytes);
-            sa[i] = scale_at(wsa[i], s, lk);
-        }
+        for (int i = 0; i < NF; ++i) wsa[i] = *reinterpret_cast<const uint2*>(sc_a + lb.sa + i * 16 * kScaleRow);
 #pragma unroll
-        for (int j = 0; j < kWaveFragsN; ++j) {
-            b[j] = frag_at(st_b + j * 16 * kRowBytes);
-            sb[j] = scale_at(wsb[j], s, lk);
-        }
-#pragma unroll
-        for (int j = 0; j < kWaveFragsN; ++j)
-#pragma unroll
-            for (int i = 0; i < NF; ++i)
-                acc[j][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b[j], a[i], acc[j][i], 4, 4, 0, sb[j], 0,
-                                                                               sa[i]);
+        for (int j = 0; j < kWaveFragsN; ++j) wsb[j] = *reinterpret_cast<const uint2*>(sc_b + lb.sb + j * 16 * kScaleRow);
+        mx_read_half<NF, 0>(f, sm.codes[ks & 1], lb, wsa, wsb, lk);
+        mx_mfma_half<NF>(acc, f);
+        mx_read_half<NF, 1>(f, sm.codes[ks & 1], lb, wsa, wsb, lk);
+        if (!lag) mx_mfma_half<NF>(acc, f);
     }
+    if (NF != 0 && lag && nsteps > 0) mx_mfma_half<NF>(acc, f);
 }
 
 // The K loop for a wave of which only `rows` (from its first row on) are
