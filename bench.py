@@ -35,7 +35,7 @@ step time (algorithmic work per launch over its event-measured duration) and
 rocprofv3 FETCH_SIZE / WRITE_SIZE counters recorded in profiles/traffic.json
 (written by profile_counters.sh), scaled by what the same counters read for a
 plain copy of known size; it is null when the kernel sources changed since.
-`cpu_baseline` times the CPU oracle on a bounded sample of the GEMM workload.
+`cpu_baseline` times the CPU oracle on the whole GEMM workload.
 """
 from __future__ import annotations
 
@@ -483,8 +483,10 @@ def build_moe_nv(torch, F, W, dev, tokens, name, bound):
 
 
 def cpu_baseline():
-    """The CPU oracle on a bounded sample of the GEMM workload: 64 rows of A
-    quantized and multiplied by the full quantized W (4096x4096), fp64."""
+    """The CPU oracle on the whole W4A4 GEMM workload (M=N=K=4096): W is
+    MX-quantized beforehand (pre-quantized weights, as in the workload), then
+    the timed part quantizes A and forms the exact fp64 product with its error
+    bound."""
     import workloads as W
     from oracle import gemm as G
     from oracle import quant as Q
@@ -494,17 +496,17 @@ def cpu_baseline():
     except Exception:
         threads = os.cpu_count() or 1
     wl = W.workload3()
-    ab = W.bf16_bits(wl.A)[:64]
+    ab = W.bf16_bits(wl.A)
     wb = W.bf16_bits(wl.W)
-    t0 = time.perf_counter()
-    ea = Q.mx_quantize(ab)
     eb = tuple(np.concatenate(p) for p in zip(*[Q.mx_quantize(wb[i:i + 512]) for i in range(0, 4096, 512)]))
+    t0 = time.perf_counter()
+    ea = tuple(np.concatenate(p) for p in zip(*[Q.mx_quantize(ab[i:i + 512]) for i in range(0, 4096, 512)]))
     G.gemm_ref("mx", *ea, *eb)
     dt = time.perf_counter() - t0
-    flops = 2.0 * 64 * 4096 * 4096
+    flops = 2.0 * 4096 ** 3
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": "64x4096 A rows times the full 4096x4096 W of the 4096^3 GEMM: MX-quantize both "
-                      "(fp64 numpy) and the exact fp64 product with its error bound; "
+            "sample": "the whole 4096^3 W4A4 MXFP4 GEMM: MX-quantize A (fp64 numpy) and the exact fp64 product "
+                      "with its error bound, W pre-quantized; "
                       f"{dt:.1f} s on {os.cpu_count()} host cores"}
 
 

@@ -111,7 +111,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void gemm_mx_256_kernel(
     for (int j = 0; j < kWaveFragsN; ++j)
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[j][i] = v4f{0.f, 0.f, 0.f, 0.f};
-    mx_tile_mainloop<8>(sm, A, B, kblocks, acc);
+    mx_tile_mainloop_rows(sm, A, B, kblocks, acc, m - m0 - (int64_t)(threadIdx.x >> 8) * 128, m - m0);
 
     // Epilogue through LDS: the tile (bf16: all 256 rows; fp32: 128 rows per
     // pass) is written in the accumulator layout, then stored row by row in

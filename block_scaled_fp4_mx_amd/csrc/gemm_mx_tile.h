@@ -139,15 +139,17 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 
 __device__ __forceinline__ void wait_vm_zero() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Only the A slab rows below arows (the rows of the fragments in use) are
+// fetched; B always fills the whole slab.
 template <class SA, class SB>
-__device__ __forceinline__ void mx_issue_codes(MxCodes& st, const SA& A, const SB& B, int ks) {
+__device__ __forceinline__ void mx_issue_codes(MxCodes& st, const SA& A, const SB& B, int ks, int arows) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint8_t* ac = A.codes + (int64_t)ks * kRowBytes;
     const uint8_t* bc = B.codes + (int64_t)ks * kRowBytes;
     const uint32_t la = lds_addr(st.a) + wave * 4 * 1024, lb = lds_addr(st.b) + wave * 4 * 1024;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        dma16(ac, A.off(q), la + q * 1024);
+        if (wave * 32 + q * 8 < arows) dma16(ac, A.off(q), la + q * 1024);
         dma16(bc, B.off(q), lb + q * 1024);
     }
 }
@@ -155,12 +157,14 @@ __device__ __forceinline__ void mx_issue_codes(MxCodes& st, const SA& A, const S
 // Scale bytes of steps 2p and 2p + 1 (blocks 16p .. 16p + 15) of every row:
 // waves 0-3 fetch the A rows, waves 4-7 the B rows.
 template <class SA, class SB>
-__device__ __forceinline__ void mx_issue_scales(MxScales& sc, const SA& A, const SB& B, int p) {
+__device__ __forceinline__ void mx_issue_scales(MxScales& sc, const SA& A, const SB& B, int p, int arows) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (wave < 4)
-        dma16(A.scales + (int64_t)p * 16, A.soff, lds_addr(sc.a) + wave * 1024);
-    else
+    if (wave < 4) {
+        if (wave * 64 < arows)
+            dma16(A.scales + (int64_t)p * 16, A.soff, lds_addr(sc.a) + wave * 1024);
+    } else {
         dma16(B.scales + (int64_t)p * 16, B.soff, lds_addr(sc.b) + (wave - 4) * 1024);
+    }
 }
 
 // Per-lane LDS bases of this wave's fragments (row wm*128 + i*16 + lr has
@@ -249,22 +253,22 @@ __device__ __forceinline__ void mx_mfma_half(v4f acc[kWaveFragsN][8], const MxFr
 // barriers whatever its NF.
 template <int NF, class SA, class SB>
 __device__ __forceinline__ void mx_tile_mainloop(MxSmem& sm, const SA& A, const SB& B, int64_t kblocks,
-                                                 v4f acc[kWaveFragsN][8]) {
+                                                 v4f acc[kWaveFragsN][8], int arows) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave >> 2, wn = wave & 3, lk = lane >> 4;
     const bool lag = (__builtin_amdgcn_readfirstlane(wave) & 2) != 0;
     const int nsteps = (int)(kblocks / kStepBlocks);
     const MxLdsBase lb = mx_lds_base(wm, wn, lane);
-    mx_issue_codes(sm.codes[0], A, B, 0);
-    mx_issue_scales(sm.scales[0], A, B, 0);
+    mx_issue_codes(sm.codes[0], A, B, 0, arows);
+    mx_issue_scales(sm.scales[0], A, B, 0, arows);
     uint2 wsa[8], wsb[kWaveFragsN];
     MxFrags f;
     for (int ks = 0; ks < nsteps; ++ks) {
         wait_vm_zero();
         __syncthreads();
         if (ks + 1 < nsteps) {
-            mx_issue_codes(sm.codes[(ks + 1) & 1], A, B, ks + 1);
-            if (((ks + 1) & 1) == 0) mx_issue_scales(sm.scales[((ks + 1) >> 1) & 1], A, B, (ks + 1) >> 1);
+            mx_issue_codes(sm.codes[(ks + 1) & 1], A, B, ks + 1, arows);
+            if (((ks + 1) & 1) == 0) mx_issue_scales(sm.scales[((ks + 1) >> 1) & 1], A, B, (ks + 1) >> 1, arows);
         }
         if (NF == 0) continue;
         if (lag && ks > 0) mx_mfma_half<NF>(acc, f);          // second half of step ks - 1
@@ -283,21 +287,25 @@ __device__ __forceinline__ void mx_tile_mainloop(MxSmem& sm, const SA& A, const 
 }
 
 // The K loop for a wave of which only `rows` (from its first row on) are
-// needed: ceil(rows / 16) row fragments, at least 0 and at most 8.
+// needed: ceil(rows / 16) row fragments, at least 0 and at most 8.  tile_rows
+// (the rows of the whole tile from its first row on) bounds the A rows fetched.
 template <class SA, class SB>
 __device__ __forceinline__ void mx_tile_mainloop_rows(MxSmem& sm, const SA& A, const SB& B, int64_t kblocks,
-                                                      v4f acc[kWaveFragsN][8], int64_t rows) {
+                                                      v4f acc[kWaveFragsN][8], int64_t rows,
+                                                      int64_t tile_rows) {
+    // A slab rows to fetch: the tile's rows rounded up to whole fragments
+    const int arows = __builtin_amdgcn_readfirstlane((int)min<int64_t>(kTileM, (tile_rows + 15) & ~int64_t(15)));
     const int nf = rows <= 0 ? 0 : (rows >= 128 ? 8 : (int)((rows + 15) >> 4));
     switch (__builtin_amdgcn_readfirstlane(nf)) {
-        case 8: mx_tile_mainloop<8>(sm, A, B, kblocks, acc); break;
-        case 7: mx_tile_mainloop<7>(sm, A, B, kblocks, acc); break;
-        case 6: mx_tile_mainloop<6>(sm, A, B, kblocks, acc); break;
-        case 5: mx_tile_mainloop<5>(sm, A, B, kblocks, acc); break;
-        case 4: mx_tile_mainloop<4>(sm, A, B, kblocks, acc); break;
-        case 3: mx_tile_mainloop<3>(sm, A, B, kblocks, acc); break;
-        case 2: mx_tile_mainloop<2>(sm, A, B, kblocks, acc); break;
-        case 1: mx_tile_mainloop<1>(sm, A, B, kblocks, acc); break;
-        default: mx_tile_mainloop<0>(sm, A, B, kblocks, acc); break;
+        case 8: mx_tile_mainloop<8>(sm, A, B, kblocks, acc, arows); break;
+        case 7: mx_tile_mainloop<7>(sm, A, B, kblocks, acc, arows); break;
+        case 6: mx_tile_mainloop<6>(sm, A, B, kblocks, acc, arows); break;
+        case 5: mx_tile_mainloop<5>(sm, A, B, kblocks, acc, arows); break;
+        case 4: mx_tile_mainloop<4>(sm, A, B, kblocks, acc, arows); break;
+        case 3: mx_tile_mainloop<3>(sm, A, B, kblocks, acc, arows); break;
+        case 2: mx_tile_mainloop<2>(sm, A, B, kblocks, acc, arows); break;
+        case 1: mx_tile_mainloop<1>(sm, A, B, kblocks, acc, arows); break;
+        default: mx_tile_mainloop<0>(sm, A, B, kblocks, acc, arows); break;
     }
 }
 

@@ -474,7 +474,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void moe_gate_up_mx256_kernel(Gemm
         const int64_t spos = min(r0 + mx_scale_row(), rend - 1);
         A.soff = (uint32_t)(p.perm[spos] / p.topk) * kblocks;
         B.soff = (uint32_t)gu_weight_row(mx_scale_row(), c0, I) * kblocks;
-        mx_tile_mainloop_rows(sm, A, B, H / 32, acc, rend - (r0 + wm * 128));
+        mx_tile_mainloop_rows(sm, A, B, H / 32, acc, rend - (r0 + wm * 128), rend - r0);
     } else {
         // g|u given per slot (debug injection): place them in the accumulator layout
 #pragma unroll
@@ -577,7 +577,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void moe_down_mx256_kernel(GemmPar
     for (int j = 0; j < kWaveFragsN; ++j)
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[j][i] = v4f{0.f, 0.f, 0.f, 0.f};
-    mx_tile_mainloop_rows(sm, A, B, I / 32, acc, rend - (r0 + wm * 128));
+    mx_tile_mainloop_rows(sm, A, B, I / 32, acc, rend - (r0 + wm * 128), rend - r0);
 
     if (p.dbg.y) {
 #pragma unroll
