@@ -139,6 +139,12 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 
 __device__ __forceinline__ void wait_vm_zero() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Before the barrier that hands a stage back to the copies: this wave's copies
+// have landed and its LDS reads have returned their data (a wave may hold a
+// half-step's fragments across the barrier, read from the stage the next
+// copies overwrite).
+__device__ __forceinline__ void wait_copies_and_reads() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory"); }
+
 // Only the A slab rows below arows (the rows of the fragments in use) are
 // fetched; B always fills the whole slab.
 template <class SA, class SB>
@@ -264,7 +270,7 @@ __device__ __forceinline__ void mx_tile_mainloop(MxSmem& sm, const SA& A, const 
     uint2 wsa[8], wsb[kWaveFragsN];
     MxFrags f;
     for (int ks = 0; ks < nsteps; ++ks) {
-        wait_vm_zero();
+        wait_copies_and_reads();
         __syncthreads();
         if (ks + 1 < nsteps) {
             mx_issue_codes(sm.codes[(ks + 1) & 1], A, B, ks + 1, arows);

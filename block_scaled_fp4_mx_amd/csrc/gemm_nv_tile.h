@@ -7,9 +7,8 @@
 // inside fp16's normal range for every E4M3 scale) and fed to
 // v_mfma_f32_16x16x32_f16; the tensor scales multiply the fp32 result.  The
 // expansion costs two instructions per pair of codes: v_cvt_scalef32_pk_f16_fp4
-// gives code * 2^e for the power-of-two part of s_g (it multiplies by
-// 2^floor(log2 scale)), and a packed fp16 multiply by the E4M3 mantissa
-// (1 + m/8, or m for a subnormal byte) finishes the exact value.
+// (scale 1) converts the codes, and a packed fp16 multiply by s_g (two group
+// bytes go to fp16 in one v_cvt_scalef32_pk_f16_fp8) finishes the exact value.
 //
 // Stage layout per K step: A TM rows x 512 B (16-byte chunk c of row r at
 // c ^ (r & 15)), B codes 256 rows x 128 B (chunk c of row r at c ^ (r & 7)), B

@@ -14,7 +14,9 @@
 //
 // Stage layout per K step (128 values):
 //   A fp16  64 rows x 256 B, 16-byte chunk c of row r at slot c ^ (r & 15);
-//   B codes 512 rows x 64 B, chunk c of row r at slot c ^ (r & 3);
+//   B codes 512 rows x 64 B, chunk c of row r at slot c ^ nw_swz(r), which
+//           puts any 8 (and any 16) consecutive rows of a fragment read on
+//           different 16-byte bank groups;
 //   B E4M3  512 rows x 8 B, row-major.
 // Every stage arrives by global_load_lds DMA (dwordx4 for codes and fp16,
 // dword for the scale bytes).  With A given as NVFP4 codes (the dense GEMM),
@@ -73,7 +75,8 @@ __device__ __forceinline__ int nw_wave() { return (int)(threadIdx.x >> 6); }
 __device__ __forceinline__ int nw_a_row(int q) { return 8 * nw_wave() + 4 * q + (int)((threadIdx.x & 63) >> 4); }
 __device__ __forceinline__ uint32_t nw_a_chunk(int row) { return ((threadIdx.x & 15u) ^ (uint32_t)(row & 15)) << 4; }
 __device__ __forceinline__ int nw_b_row(int q) { return 64 * nw_wave() + 16 * q + (int)((threadIdx.x & 63) >> 2); }
-__device__ __forceinline__ uint32_t nw_b_chunk(int row) { return ((threadIdx.x & 3u) ^ (uint32_t)(row & 3)) << 4; }
+__device__ __forceinline__ uint32_t nw_swz(int row) { return (uint32_t)((row >> 1) ^ (row >> 3)) & 3u; }
+__device__ __forceinline__ uint32_t nw_b_chunk(int row) { return ((threadIdx.x & 3u) ^ nw_swz(row)) << 4; }
 __device__ __forceinline__ int nw_s_row(int j) { return 64 * nw_wave() + 32 * j + (int)((threadIdx.x & 63) >> 1); }
 __device__ __forceinline__ uint32_t nw_s_col() { return (threadIdx.x & 1u) << 2; }
 __device__ __forceinline__ int nw_ac_row() { return 16 * (nw_wave() & 3) + (int)((threadIdx.x & 63) >> 2); }
@@ -169,7 +172,7 @@ __device__ __forceinline__ void nw_mainloop(NwSmem<ACODES>& sm, const NwSrc& S, 
 #pragma unroll
         for (int nf = 0; nf < 4; ++nf) {
             const int row = wave * 64 + nf * 16 + lr;
-            c[nf] = *reinterpret_cast<const uint4*>(&st.b[row * kNwBRow + ((lq ^ (row & 3)) << 4)]);
+            c[nf] = *reinterpret_cast<const uint4*>(&st.b[row * kNwBRow + ((lq ^ nw_swz(row)) << 4)]);
             sp[nf] = nv_scale_pair(*reinterpret_cast<const uint16_t*>(&st.s[row * kNwSRow + lq * 2]));
         }
 #pragma unroll
