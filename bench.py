@@ -118,6 +118,7 @@ def load_traffic():
 
 
 def main():
+    t_start = time.perf_counter()
     args = parse()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU; multi-GPU runs are not part of it "
@@ -131,6 +132,9 @@ def main():
     dev = "cuda"
     torch.cuda.init()
     stream = torch.cuda.current_stream()
+
+    def progress(msg):
+        print(f"[bench] {msg} ({time.perf_counter() - t_start:.0f} s)", file=sys.stderr, flush=True)
 
     def rot_copies(t, per_copy_bytes):
         n = max(2, int(np.ceil(1.5 * MALL_BYTES / per_copy_bytes)))
@@ -215,13 +219,17 @@ def main():
               "gemm_nv_tile_kernel"),
     ]
     want = set(args.only.split(",")) if args.only else None
+    progress("linear and GEMM inputs ready")
     if not args.no_moe:
         if want is None or "moe_h4096" in want:
             stages.append(build_moe_h4096(torch, F, W, dev))
+            progress("build_moe_h4096 done")
         if want is None or "moe_h7168_decode64" in want:
             stages.append(build_moe_decode(torch, F, W, dev))
+            progress("build_moe_decode done")
         if want is None or "moe_h7168_prefill16384" in want:
             stages.append(build_moe_prefill(torch, F, W, dev))
+            progress("build_moe_prefill done")
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -230,11 +238,13 @@ def main():
     if want is not None:
         stages = [s for s in stages if s.name in want]
 
+    progress(f"{len(stages)} stages built")
     for _ in range(args.warmup):
         for s in stages:
             s.launch()
         st["i"] += 1
     torch.cuda.synchronize()
+    progress("warmup done")
 
     # timed steps: the whole path, back to back, with no markers in between
     torch.cuda.synchronize()
@@ -246,6 +256,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
+    progress("timed steps done")
 
     # per-stage durations: `steps` launches of the stage between two events on
     # its stream, queued behind a spin kernel so the host's launch rate never
@@ -278,6 +289,7 @@ def main():
             s.moe["set_events"]([None] * 6)
             moe_marks[s.name] = evs
 
+    progress("per-stage timing done")
     traffic = load_traffic()
     rooflines = {}
     kernel_rows = []                        # (ms, name, entry) for the dominant-kernel choice
