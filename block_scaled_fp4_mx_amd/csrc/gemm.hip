@@ -20,6 +20,7 @@ namespace fp4 {
 namespace {
 
 constexpr int kBM = 128, kBN = 128, kThreads = 256;
+constexpr int kNvGemmTM = 64;   // A rows per NV GEMM tile (wide tile, three stages, A as codes)
 
 // 16x16 accumulator layout: lane holds rows 4*(lane/16) + r, column lane % 16.
 __device__ __forceinline__ void store_tile(const v4f acc[4][4], void* c, int c_f32, int64_t ldc, int64_t m,
@@ -175,10 +176,10 @@ __global__ __launch_bounds__(kNvThreads, 1) void gemm_nv_tile_kernel(
     const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as, const float* __restrict__ ats,
     const uint8_t* __restrict__ bc, const uint8_t* __restrict__ bs, const float* __restrict__ bts, int64_t m,
     int64_t n, int64_t k, void* __restrict__ c, int c_f32, int64_t ldc, int tiles_m, int tiles_n) {
-    __shared__ __align__(16) NwSmem<true> sm;
+    __shared__ __align__(16) NwSmem<kNvGemmTM, 3, true> sm;
     int tm, tn;
     tile_coords(tiles_m, tiles_n, tm, tn);
-    const int64_t m0 = (int64_t)tm * kNwM, n0 = (int64_t)tn * kNwN;
+    const int64_t m0 = (int64_t)tm * kNvGemmTM, n0 = (int64_t)tn * kNwN;
     const uint32_t kb = (uint32_t)(k / 2), kg = (uint32_t)(k / 16);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int lr = lane & 15, lq = lane >> 4;
@@ -206,7 +207,7 @@ __global__ __launch_bounds__(kNvThreads, 1) void gemm_nv_tile_kernel(
     const float scale = __fmul_rn(*ats, *bts);
     const int esz = c_f32 ? 4 : 2;
     const int rowb = kNwN * esz + 16;                // padded LDS row pitch (bytes)
-    static_assert(kNwM * (kNwN * 4 + 16) <= (int)sizeof(sm), "C staging exceeds the tile's LDS");
+    static_assert(kNvGemmTM * (kNwN * 4 + 16) <= (int)sizeof(sm), "C staging exceeds the tile's LDS");
     uint8_t* csm = reinterpret_cast<uint8_t*>(&sm);
     __syncthreads();                                 // the stages are free
 #pragma unroll
@@ -225,7 +226,7 @@ __global__ __launch_bounds__(kNvThreads, 1) void gemm_nv_tile_kernel(
     __syncthreads();
     const int chunks_row = kNwN * esz / 16;
     const bool vec = ((ldc * esz) & 15) == 0;
-    for (int q = threadIdx.x; q < kNwM * chunks_row; q += kNvThreads) {
+    for (int q = threadIdx.x; q < kNvGemmTM * chunks_row; q += kNvThreads) {
         const int row = q / chunks_row, ch = q - row * chunks_row;
         const int64_t grow = m0 + row, gcol = n0 + ch * (16 / esz);
         if (grow >= m || gcol >= n) continue;
@@ -266,7 +267,7 @@ hipError_t launch_gemm_nv(const uint8_t* ac, const uint8_t* as, const float* ats
                           const uint8_t* bc, const uint8_t* bs, const float* bts,
                           int64_t m, int64_t n, int64_t k, void* c, int c_f32, int64_t ldc,
                           hipStream_t s) {
-    const int64_t tiles_m = (m + kNwM - 1) / kNwM, tiles_n = (n + kNwN - 1) / kNwN;
+    const int64_t tiles_m = (m + kNvGemmTM - 1) / kNvGemmTM, tiles_n = (n + kNwN - 1) / kNwN;
     const bool small_ops = m * (k / 2) < (1ll << 31) && n * (k / 2) < (1ll << 31);
     if (k % kNwK == 0 && k > 0 && small_ops && tiles_m * tiles_n >= 32 && tiles_m * tiles_n < (1ll << 31)) {
         gemm_nv_tile_kernel<<<(unsigned)(tiles_m * tiles_n), kNvThreads, 0, s>>>(

@@ -825,11 +825,13 @@ __global__ __launch_bounds__(kNvThreads, 1) void moe_down_nv_kernel(GemmParams p
 }
 
 // ---------------------------------------------------------------- wide NV tiles
-// Prefill-sized batches: 64 routed rows x 512 weight rows per tile (the wide
-// NV tile).  gate/up: wave w owns slab rows w*64 .. +63: 32 w1 rows
-// (intermediate columns c0 + w*32 ..) then the 32 w3 rows of the same
-// columns, so fragments 0-1 hold g and fragments 2-3 the matching u.  A tile
-// covers 256 intermediate columns.
+// Prefill-sized batches: 128 routed rows x 512 weight rows per tile (the wide
+// NV tile, two stages).  gate/up: wave w owns slab rows w*64 .. +63: 32 w1 rows
+// (intermediate columns c0 + w*32 ..) then the 32 w3 rows of the same columns,
+// so fragments 0-1 hold g and fragments 2-3 the matching u.  A tile covers 256
+// intermediate columns.
+constexpr int kNwMoeM = 128;        // routed rows per wide tile
+constexpr int kNwMoeMf = kNwMoeM / 16;
 constexpr int kNwGuCols = 256;
 
 __device__ __forceinline__ int64_t gu_nw_row(int slab_row, int64_t c0, int64_t I) {
@@ -838,8 +840,8 @@ __device__ __forceinline__ int64_t gu_nw_row(int slab_row, int64_t c0, int64_t I
 }
 
 __global__ __launch_bounds__(kNvThreads, 1) void moe_gate_up_nvw_kernel(GemmParams p) {
-    __shared__ __align__(16) NwSmem<false> sm;
-    static_assert(kNwM * kNwGuCols * 2 <= (int)sizeof(sm), "h tile exceeds the wide tile's LDS");
+    __shared__ __align__(16) NwSmem<kNwMoeM, 2, false> sm;
+    static_assert(kNwMoeM * kNwGuCols * 2 <= (int)sizeof(sm), "h tile exceeds the wide tile's LDS");
     const int tile = blockIdx.y;
     if (tile >= *p.ntiles) return;
     const int e = p.tile_e[tile];
@@ -851,9 +853,9 @@ __global__ __launch_bounds__(kNvThreads, 1) void moe_gate_up_nvw_kernel(GemmPara
     const int lr = lane & 15, lq = lane >> 4;
     const bool injected = p.dbg.gate_up_in != nullptr;
 
-    v4f acc[4][4];
+    v4f acc[kNwMoeMf][4];
 #pragma unroll
-    for (int mf = 0; mf < 4; ++mf)
+    for (int mf = 0; mf < kNwMoeMf; ++mf)
 #pragma unroll
         for (int nf = 0; nf < 4; ++nf) acc[mf][nf] = v4f{0.f, 0.f, 0.f, 0.f};
 
@@ -864,8 +866,8 @@ __global__ __launch_bounds__(kNvThreads, 1) void moe_gate_up_nvw_kernel(GemmPara
         S.s = p.w13s + (int64_t)e * (2 * I) * (H / 16);
         const uint32_t apitch = (uint32_t)(H * 2), bpitch = (uint32_t)(H / 2), spitch = (uint32_t)(H / 16);
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int arow = nw_a_row(q);
+        for (int q = 0; q < kNwMoeM / 32; ++q) {
+            const int arow = nw_a_row<kNwMoeM>(q);
             const int64_t pos = min(r0 + arow, rend - 1);
             S.aoff[q] = (uint32_t)(p.perm[pos] / p.topk) * apitch + nw_a_chunk(arow);
         }
@@ -880,7 +882,7 @@ __global__ __launch_bounds__(kNvThreads, 1) void moe_gate_up_nvw_kernel(GemmPara
     } else {
         // g|u given per slot (debug injection, tensor scales included)
 #pragma unroll
-        for (int mf = 0; mf < 4; ++mf)
+        for (int mf = 0; mf < kNwMoeMf; ++mf)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int64_t pos = r0 + mf * 16 + lq * 4 + r;
@@ -896,9 +898,9 @@ __global__ __launch_bounds__(kNvThreads, 1) void moe_gate_up_nvw_kernel(GemmPara
     __syncthreads();   // the h tile reuses the stages
 
     const float gscale = injected ? 1.0f : __fmul_rn(p.act_ts[0], p.w13ts[e]);
-    uint16_t* hsm = reinterpret_cast<uint16_t*>(&sm);      // 64 rows x 256 bf16
+    uint16_t* hsm = reinterpret_cast<uint16_t*>(&sm);      // 128 rows x 256 bf16
 #pragma unroll
-    for (int mf = 0; mf < 4; ++mf)
+    for (int mf = 0; mf < kNwMoeMf; ++mf)
 #pragma unroll
         for (int nf = 0; nf < 2; ++nf)
 #pragma unroll
@@ -920,39 +922,40 @@ __global__ __launch_bounds__(kNvThreads, 1) void moe_gate_up_nvw_kernel(GemmPara
                 }
             }
     __syncthreads();
-    // quantize the 64 x 256 h tile: unit = 8 consecutive columns of one row; a
+    // quantize the 128 x 256 h tile: unit = 8 consecutive columns of one row; a
     // 16-group spans 2 consecutive lanes
     const double st_h = (double)p.act_ts[1];
-#pragma unroll
-    for (int q = 0; q < (kNwM * kNwGuCols / 8) / kNvThreads; ++q) {
+#pragma unroll 2
+    for (int q = 0; q < (kNwMoeM * kNwGuCols / 8) / kNvThreads; ++q) {
         const int unit = threadIdx.x + q * kNvThreads;
         const int rl = unit / (kNwGuCols / 8), cu = unit % (kNwGuCols / 8);
+        const int64_t pos = r0 + rl;
+        if (pos >= rend) break;      // the rows of later units are further down
         const uint4 v = *reinterpret_cast<const uint4*>(&hsm[rl * kNwGuCols + cu * 8]);
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
         uint32_t sb;
         const uint32_t packed = nv_quant8(w, st_h, sb);
-        const int64_t pos = r0 + rl;
-        if (pos < rend) {
-            const int64_t col = c0 + cu * 8;
-            reinterpret_cast<uint32_t*>(p.hc + pos * (I / 2) + col / 2)[0] = packed;
-            const bool lead = (cu & 1) == 0;
-            if (lead) p.hs[pos * (I / 16) + col / 16] = (uint8_t)sb;
-            if (p.dbg.h_codes || p.dbg.h_scales) {
-                const int64_t slot = p.perm[pos];
-                if (p.dbg.h_codes) reinterpret_cast<uint32_t*>(p.dbg.h_codes + slot * (I / 2) + col / 2)[0] = packed;
-                if (p.dbg.h_scales && lead) p.dbg.h_scales[slot * (I / 16) + col / 16] = (uint8_t)sb;
-            }
+        const int64_t col = c0 + cu * 8;
+        reinterpret_cast<uint32_t*>(p.hc + pos * (I / 2) + col / 2)[0] = packed;
+        const bool lead = (cu & 1) == 0;
+        if (lead) p.hs[pos * (I / 16) + col / 16] = (uint8_t)sb;
+        if (p.dbg.h_codes || p.dbg.h_scales) {
+            const int64_t slot = p.perm[pos];
+            if (p.dbg.h_codes) reinterpret_cast<uint32_t*>(p.dbg.h_codes + slot * (I / 2) + col / 2)[0] = packed;
+            if (p.dbg.h_scales && lead) p.dbg.h_scales[slot * (I / 16) + col / 16] = (uint8_t)sb;
         }
     }
 }
 
 // down: the fp16 expansion of Q(h) for the tile's rows times w2 rows n0 .. n0 + 511
-// (rows past H are clamped and their columns never stored).
+// (rows past H are clamped and their columns never stored).  The fp32 result
+// leaves through LDS in two passes of 64 rows.
 constexpr int kNwYRow = kNwN + 4;   // fp32 row pitch of the combine staging tile
+constexpr int kNwYRows = 64;        // rows per staging pass
 
 __global__ __launch_bounds__(kNvThreads, 1) void moe_down_nvw_kernel(GemmParams p) {
-    __shared__ __align__(16) NwSmem<false> sm;
-    static_assert(kNwM * kNwYRow * 4 <= (int)sizeof(sm), "staging tile exceeds the wide tile's LDS");
+    __shared__ __align__(16) NwSmem<kNwMoeM, 2, false> sm;
+    static_assert(kNwYRows * kNwYRow * 4 <= (int)sizeof(sm), "staging tile exceeds the wide tile's LDS");
     const int tile = blockIdx.y;
     if (tile >= *p.ntiles) return;
     const int e = p.tile_e[tile];
@@ -969,8 +972,8 @@ __global__ __launch_bounds__(kNvThreads, 1) void moe_down_nvw_kernel(GemmParams 
     S.s = p.w2s + (int64_t)e * H * (I / 16);
     const uint32_t apitch = (uint32_t)(I * 2), bpitch = (uint32_t)(I / 2), spitch = (uint32_t)(I / 16);
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int arow = nw_a_row(q);
+    for (int q = 0; q < kNwMoeM / 32; ++q) {
+        const int arow = nw_a_row<kNwMoeM>(q);
         const int64_t pos = min(r0 + arow, rend - 1);
         S.aoff[q] = (uint32_t)(p.h16_by_slot ? p.perm[pos] : pos) * apitch + nw_a_chunk(arow);
     }
@@ -982,42 +985,46 @@ __global__ __launch_bounds__(kNvThreads, 1) void moe_down_nvw_kernel(GemmParams 
 #pragma unroll
     for (int j = 0; j < 2; ++j) S.soff[j] = (uint32_t)min(n0 + nw_s_row(j), H - 1) * spitch + nw_s_col();
 
-    v4f acc[4][4];
+    v4f acc[kNwMoeMf][4];
 #pragma unroll
-    for (int mf = 0; mf < 4; ++mf)
+    for (int mf = 0; mf < kNwMoeMf; ++mf)
 #pragma unroll
         for (int nf = 0; nf < 4; ++nf) acc[mf][nf] = v4f{0.f, 0.f, 0.f, 0.f};
     nw_mainloop_rows(sm, S, (int)(I / kNwK), acc, rend - r0);
-    __syncthreads();   // the staging tile reuses the stages
 
     const float yscale = __fmul_rn(p.act_ts[1], p.w2ts[e]);
     float* ysm = reinterpret_cast<float*>(&sm);
 #pragma unroll
-    for (int mf = 0; mf < 4; ++mf)
+    for (int pass = 0; pass < kNwMoeM / kNwYRows; ++pass) {
+        if (r0 + pass * kNwYRows >= rend) break;          // no rows of the problem in this pass (uniform)
+        __syncthreads();   // the staging tile reuses the stages (or the previous pass)
 #pragma unroll
-        for (int nf = 0; nf < 4; ++nf)
+        for (int mf = 0; mf < kNwYRows / 16; ++mf)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int rl = mf * 16 + lq * 4 + r;
-                const int cl = wave * 64 + nf * 16 + lr;
-                const float y = __fmul_rn(acc[mf][nf][r], yscale);
-                ysm[rl * kNwYRow + cl] = y;
-                const int64_t pos = r0 + rl;
-                if (p.dbg.y && pos < rend && n0 + cl < H) p.dbg.y[(int64_t)p.perm[pos] * H + n0 + cl] = y;
+            for (int nf = 0; nf < 4; ++nf)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int rl = mf * 16 + lq * 4 + r;
+                    const int cl = wave * 64 + nf * 16 + lr;
+                    const float y = __fmul_rn(acc[pass * (kNwYRows / 16) + mf][nf][r], yscale);
+                    ysm[rl * kNwYRow + cl] = y;
+                    const int64_t pos = r0 + pass * kNwYRows + rl;
+                    if (p.dbg.y && pos < rend && n0 + cl < H) p.dbg.y[(int64_t)p.perm[pos] * H + n0 + cl] = y;
+                }
+        __syncthreads();
+        for (int rr = wave; rr < kNwYRows; rr += kNvThreads / 64) {
+            const int64_t pos = r0 + pass * kNwYRows + rr;
+            if (pos >= rend) break;     // rows are in order: the rest of this wave's rows are past the end too
+            const int64_t slot = p.perm[pos];
+            const float wgt = p.weights[slot];
+#pragma unroll
+            for (int hh = 0; hh < kNwN / 256; ++hh) {
+                const int col = hh * 256 + lane * 4;
+                if (n0 + col >= H) break;     // H is a multiple of 4: a float4 is wholly in or out
+                const float4 v = *reinterpret_cast<const float4*>(&ysm[rr * kNwYRow + col]);
+                *reinterpret_cast<float4*>(p.ybuf + slot * H + n0 + col) =
+                    make_float4(__fmul_rn(wgt, v.x), __fmul_rn(wgt, v.y), __fmul_rn(wgt, v.z), __fmul_rn(wgt, v.w));
             }
-    __syncthreads();
-    for (int rr = wave; rr < kNwM; rr += kNvThreads / 64) {
-        const int64_t pos = r0 + rr;
-        if (pos >= rend) break;     // rows are in order: the rest of this wave's rows are past the end too
-        const int64_t slot = p.perm[pos];
-        const float wgt = p.weights[slot];
-#pragma unroll
-        for (int hh = 0; hh < kNwN / 256; ++hh) {
-            const int col = hh * 256 + lane * 4;
-            if (n0 + col >= H) break;     // H is a multiple of 4: a float4 is wholly in or out
-            const float4 v = *reinterpret_cast<const float4*>(&ysm[rr * kNwYRow + col]);
-            *reinterpret_cast<float4*>(p.ybuf + slot * H + n0 + col) =
-                make_float4(__fmul_rn(wgt, v.x), __fmul_rn(wgt, v.y), __fmul_rn(wgt, v.z), __fmul_rn(wgt, v.w));
         }
     }
 }
@@ -1094,12 +1101,12 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t s) {
     route_count_kernel<<<(unsigned)L.nblk, kRouteSlots, 0, s>>>(a.ids, S, E, blockbase);
     // LDS-staged tiles: MX with hidden and inter multiples of 512 (256 routed
     // rows per tile), NV with multiples of 256 (32 routed rows per tile for
-    // decode batches, 64 for larger ones)
+    // decode batches, 128 for larger ones)
     const bool tiled = a.fmt == FP4_FMT_MX && H % 512 == 0 && I % 512 == 0;
     const bool nv_tiled = a.fmt == FP4_FMT_NV && H % 256 == 0 && I % 256 == 0;
     const bool nv_decode = T <= kNvDecodeTokens;       // 32-row, three-stage NV tiles
     route_scan_kernel<<<1, 1024, 0, s>>>(blockbase, L.nblk, E, counts, offsets, tile_e, tile_r, ntiles,
-                                         tiled ? kTileM : (nv_tiled ? (nv_decode ? 32 : 64) : kBM));
+                                         tiled ? kTileM : (nv_tiled ? (nv_decode ? 32 : kNwMoeM) : kBM));
     route_place_kernel<<<(unsigned)L.nblk, kRouteSlots, (size_t)E * (kRouteSlots / 32) * 4, s>>>(a.ids, S, E, blockbase, perm,
                                                                                   slot_pos);
     if ((err = hipGetLastError()) != hipSuccess || (err = mark(2)) != hipSuccess) return err;

@@ -66,12 +66,14 @@ def test_moe_tiled_mx_segments():
 
 
 def test_moe_tiled_nv_segments():
-    """Hidden and intermediate multiples of 256 take the 64-row LDS-staged NV
-    tiles (fp16 expansion of the codes): segments spanning several tiles and
-    ragged last tiles of 1 to 4 row fragments."""
+    """Hidden and intermediate multiples of 256 take the 128-row LDS-staged NV
+    tiles (fp16 expansion of the codes): segments spanning several tiles,
+    ragged last tiles of several row-fragment counts, and last tiles of at most
+    64 rows (whose second staging pass of the down tile is skipped)."""
     case, eq = _small_case("nv", 105, 300, 256, 256, 4, 2)
     counts = np.bincount(case.ids.ravel(), minlength=4)
-    assert counts.max() > 64 and len(set((counts % 64 + 15) // 16)) > 1
+    last = counts % 128
+    assert counts.max() > 128 and len(set((last + 15) // 16)) > 2 and ((last > 0) & (last <= 64)).any()
     _all_checks(case, oracle_expect(case, np.arange(case.T), eq))
 
 
