@@ -5,11 +5,13 @@
 //   2. routing metadata on the device: per-block expert histograms, one scan
 //      block (offsets, per-block bases, row-tile list) and a stable placement
 //      of every slot s = t*topk + j into its expert's segment (perm / slot_pos);
+//      batches of at most 512 slots do all of it in one workgroup;
 //   3. grouped gate/up GEMM over row tiles of each expert's segment, gathering
 //      the quantized X rows through perm; each wave holds g and u for the same
 //      (row, column) positions, so the epilogue forms h = SiLU(g) * u in
 //      registers, rounds it to bf16 and quantizes it (MX or NV) straight from LDS;
-//   4. grouped down GEMM on the quantized h rows, whose epilogue multiplies by
+//   4. grouped down GEMM on the quantized h rows (NV: their exact fp16
+//      expansion, written by the gate/up epilogue), whose epilogue multiplies by
 //      the routing weight and writes the fp32 row of the slot into a
 //      [slots, hidden] buffer;
 //   5. combine: each token's topk rows summed in fp32 in slot order, then
@@ -183,6 +185,63 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int32_t* __restrict__ 
     }
 }
 
+// Batches of at most kRouteSlots slots: counts, offsets, the row-tile list and
+// the stable placement in one workgroup (the same results as the three
+// kernels with a single routing block; one launch instead of three).
+__global__ __launch_bounds__(1024) void route_small_kernel(const int32_t* __restrict__ ids, int64_t S, int E,
+                                                           int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                           int32_t* __restrict__ tile_e, int32_t* __restrict__ tile_r,
+                                                           int32_t* __restrict__ ntiles, int tile_rows,
+                                                           int32_t* __restrict__ perm, int32_t* __restrict__ slot_pos) {
+    constexpr int kWords = kRouteSlots / 32;
+    extern __shared__ uint32_t lds[];                // mask [E][kWords], then count / base [E]
+    uint32_t* mask = lds;
+    int32_t* base = reinterpret_cast<int32_t*>(lds + E * kWords);
+    __shared__ int sh[40];
+    for (int i = threadIdx.x; i < E * kWords; i += 1024) mask[i] = 0u;
+    for (int i = threadIdx.x; i < E; i += 1024) base[i] = 0;
+    __syncthreads();
+    const int s = (int)threadIdx.x;
+    int e = -1;
+    if (s < S) {
+        e = ids[s];
+        if ((unsigned)e < (unsigned)E) {
+            atomicOr(&mask[e * kWords + (s >> 5)], 1u << (s & 31));
+            atomicAdd(&base[e], 1);
+        } else {
+            e = -1;                                  // routes nowhere
+        }
+    }
+    __syncthreads();
+    const int t = (int)threadIdx.x;                  // expert t (E <= 1024)
+    const int c = t < E ? base[t] : 0;
+    const int ntl = (c + tile_rows - 1) / tile_rows;
+    int prow = c, ptile = ntl;
+    block_scan2(prow, ptile, sh);                    // exclusive; totals in sh[32], sh[33]
+    if (t < E) {
+        counts[t] = c;
+        offsets[t] = prow;
+        base[t] = prow;                              // only thread t reads and writes entry t
+        for (int i = 0; i < ntl; ++i) {
+            tile_e[ptile + i] = t;
+            tile_r[ptile + i] = prow + i * tile_rows;
+        }
+    }
+    if (t == 0) {
+        offsets[E] = sh[32];
+        *ntiles = sh[33];
+    }
+    __syncthreads();
+    if (e >= 0) {
+        const int w = s >> 5, bit = s & 31;
+        int rank = __popc(mask[e * kWords + w] & ((1u << bit) - 1u));
+        for (int ww = 0; ww < w; ++ww) rank += __popc(mask[e * kWords + ww]);
+        const int pos = base[e] + rank;
+        perm[pos] = s;
+        slot_pos[s] = pos;
+    }
+}
+
 // Stable placement: the rank of slot s among the earlier slots of its block with
 // the same expert comes from a per-expert bit mask of the block's slots.
 __global__ __launch_bounds__(kRouteSlots) void route_place_kernel(const int32_t* __restrict__ ids, int64_t S, int E,
@@ -221,9 +280,10 @@ struct GemmParams {
     const float *w13ts, *w2ts, *act_ts;
     const int32_t *perm, *offsets, *tile_e, *tile_r, *ntiles;
     const float* weights;              // [S]
-    uint8_t *hc, *hs;                  // quantized h [S, I/2], [S, I/blk] in routed order
+    uint8_t *hc, *hs;                  // MX: quantized h [S, I/2], [S, I/32] in routed order
     float* ybuf;                       // [S, H]: w * y of slot s in row s
-    const uint16_t *x16, *h16;         // NV: fp16 code * s_g of Q(x) [T, H] and Q(h) [S, I]
+    const uint16_t* x16;               // NV: fp16 code * s_g of Q(x) [T, H]
+    uint16_t* h16;                     // NV: fp16 code * s_g of Q(h) [S, I], written by the gate/up tiles
     int h16_by_slot;                   // NV: h16 rows are slots (injected Q(h)), else routed positions
     fp4_moe_debug dbg;
 };
@@ -742,9 +802,9 @@ __global__ __launch_bounds__(kNvThreads, 1) void moe_gate_up_nv_kernel(GemmParam
         const int64_t pos = r0 + rl;
         if (pos < rend) {
             const int64_t col = c0 + cu * 8;
-            reinterpret_cast<uint32_t*>(p.hc + pos * (I / 2) + col / 2)[0] = packed;
+            // the down tiles read Q(h) as its exact fp16 expansion
+            *reinterpret_cast<h8_t*>(p.h16 + pos * I + col) = nv_expand8(packed, nv_scale_pair(sb)[0]);
             const bool lead = (cu & 1) == 0;
-            if (lead) p.hs[pos * (I / 16) + col / 16] = (uint8_t)sb;
             if (p.dbg.h_codes || p.dbg.h_scales) {
                 const int64_t slot = p.perm[pos];
                 if (p.dbg.h_codes) reinterpret_cast<uint32_t*>(p.dbg.h_codes + slot * (I / 2) + col / 2)[0] = packed;
@@ -936,9 +996,9 @@ __global__ __launch_bounds__(kNvThreads, 1) void moe_gate_up_nvw_kernel(GemmPara
         uint32_t sb;
         const uint32_t packed = nv_quant8(w, st_h, sb);
         const int64_t col = c0 + cu * 8;
-        reinterpret_cast<uint32_t*>(p.hc + pos * (I / 2) + col / 2)[0] = packed;
+        // the down tiles read Q(h) as its exact fp16 expansion
+        *reinterpret_cast<h8_t*>(p.h16 + pos * I + col) = nv_expand8(packed, nv_scale_pair(sb)[0]);
         const bool lead = (cu & 1) == 0;
-        if (lead) p.hs[pos * (I / 16) + col / 16] = (uint8_t)sb;
         if (p.dbg.h_codes || p.dbg.h_scales) {
             const int64_t slot = p.perm[pos];
             if (p.dbg.h_codes) reinterpret_cast<uint32_t*>(p.dbg.h_codes + slot * (I / 2) + col / 2)[0] = packed;
@@ -1098,17 +1158,26 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t s) {
                          : launch_quantize_nv(a.x, T, H, H, xc, xs, const_cast<float*>(a.act_ts), true, nullptr, s);
     if (err != hipSuccess || (err = mark(1)) != hipSuccess) return err;
     // 2. routing metadata
-    route_count_kernel<<<(unsigned)L.nblk, kRouteSlots, 0, s>>>(a.ids, S, E, blockbase);
     // LDS-staged tiles: MX with hidden and inter multiples of 512 (256 routed
     // rows per tile), NV with multiples of 256 (32 routed rows per tile for
     // decode batches, 128 for larger ones)
     const bool tiled = a.fmt == FP4_FMT_MX && H % 512 == 0 && I % 512 == 0;
     const bool nv_tiled = a.fmt == FP4_FMT_NV && H % 256 == 0 && I % 256 == 0;
     const bool nv_decode = T <= kNvDecodeTokens;       // 32-row, three-stage NV tiles
-    route_scan_kernel<<<1, 1024, 0, s>>>(blockbase, L.nblk, E, counts, offsets, tile_e, tile_r, ntiles,
-                                         tiled ? kTileM : (nv_tiled ? (nv_decode ? 32 : kNwMoeM) : kBM));
-    route_place_kernel<<<(unsigned)L.nblk, kRouteSlots, (size_t)E * (kRouteSlots / 32) * 4, s>>>(a.ids, S, E, blockbase, perm,
-                                                                                  slot_pos);
+    const int tile_rows = tiled ? kTileM : (nv_tiled ? (nv_decode ? 32 : kNwMoeM) : kBM);
+    // grid rows: at most ceil(S / tile_rows) full tiles plus one partial tile
+    // per active expert (the workgroups past the actual count exit at once)
+    const unsigned grid_tiles = (unsigned)((S + tile_rows - 1) / tile_rows + (E < S ? E : S));
+    const size_t small_lds = (size_t)E * (kRouteSlots / 32 + 1) * 4;
+    if (S <= kRouteSlots && small_lds <= 65536) {
+        route_small_kernel<<<1, 1024, small_lds, s>>>(
+            a.ids, S, E, counts, offsets, tile_e, tile_r, ntiles, tile_rows, perm, slot_pos);
+    } else {
+        route_count_kernel<<<(unsigned)L.nblk, kRouteSlots, 0, s>>>(a.ids, S, E, blockbase);
+        route_scan_kernel<<<1, 1024, 0, s>>>(blockbase, L.nblk, E, counts, offsets, tile_e, tile_r, ntiles, tile_rows);
+        route_place_kernel<<<(unsigned)L.nblk, kRouteSlots, (size_t)E * (kRouteSlots / 32) * 4, s>>>(
+            a.ids, S, E, blockbase, perm, slot_pos);
+    }
     if ((err = hipGetLastError()) != hipSuccess || (err = mark(2)) != hipSuccess) return err;
 
     GemmParams p{};
@@ -1144,31 +1213,29 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t s) {
     if (nv_tiled) {
         expand_nv16_kernel<<<stream_grid(T * H / 16), kThreads, 0, s>>>(xc, xs, T, H, x16);
         if (nv_decode)
-            moe_gate_up_nv_kernel<32, 3><<<dim3((unsigned)(I / kNvGuCols), (unsigned)L.max_tiles), kNvThreads, 0, s>>>(p);
+            moe_gate_up_nv_kernel<32, 3><<<dim3((unsigned)(I / kNvGuCols), grid_tiles), kNvThreads, 0, s>>>(p);
         else
-            moe_gate_up_nvw_kernel<<<dim3((unsigned)(I / kNwGuCols), (unsigned)L.max_tiles), kNvThreads, 0, s>>>(p);
+            moe_gate_up_nvw_kernel<<<dim3((unsigned)(I / kNwGuCols), grid_tiles), kNvThreads, 0, s>>>(p);
         if ((err = hipGetLastError()) != hipSuccess || (err = mark(3)) != hipSuccess) return err;
-        if (a.dbg.h_codes_in)
+        if (a.dbg.h_codes_in)      // injected Q(h), by slot: its expansion replaces the tiles' own
             expand_nv16_kernel<<<stream_grid(S * I / 16), kThreads, 0, s>>>(a.dbg.h_codes_in, a.dbg.h_scales_in, S, I,
                                                                              h16);
-        else
-            expand_nv16_kernel<<<stream_grid(S * I / 16), kThreads, 0, s>>>(hc, hs, S, I, h16);
         if (nv_decode)
-            moe_down_nv_kernel<32, 3><<<dim3((unsigned)(H / kNvTileN), (unsigned)L.max_tiles), kNvThreads, 0, s>>>(p);
+            moe_down_nv_kernel<32, 3><<<dim3((unsigned)(H / kNvTileN), grid_tiles), kNvThreads, 0, s>>>(p);
         else
-            moe_down_nvw_kernel<<<dim3((unsigned)((H + kNwN - 1) / kNwN), (unsigned)L.max_tiles), kNvThreads, 0, s>>>(
+            moe_down_nvw_kernel<<<dim3((unsigned)((H + kNwN - 1) / kNwN), grid_tiles), kNvThreads, 0, s>>>(
                 p);
         if ((err = hipGetLastError()) != hipSuccess || (err = mark(4)) != hipSuccess) return err;
     } else if (tiled) {
-        const dim3 g_gu((unsigned)(I / kGu2Cols), (unsigned)L.max_tiles);
-        const dim3 g_dn((unsigned)(H / kTileN), (unsigned)L.max_tiles);
+        const dim3 g_gu((unsigned)(I / kGu2Cols), grid_tiles);
+        const dim3 g_dn((unsigned)(H / kTileN), grid_tiles);
         moe_gate_up_mx256_kernel<<<g_gu, kTileThreads, 0, s>>>(p);
         if ((err = hipGetLastError()) != hipSuccess || (err = mark(3)) != hipSuccess) return err;
         moe_down_mx256_kernel<<<g_dn, kTileThreads, 0, s>>>(p);
         if ((err = hipGetLastError()) != hipSuccess || (err = mark(4)) != hipSuccess) return err;
     } else {
-        const dim3 g_gu((unsigned)(I / kGuCols), (unsigned)L.max_tiles);
-        const dim3 g_dn((unsigned)(H / kDnCols), (unsigned)L.max_tiles);
+        const dim3 g_gu((unsigned)(I / kGuCols), grid_tiles);
+        const dim3 g_dn((unsigned)(H / kDnCols), grid_tiles);
         if (a.fmt == FP4_FMT_MX) moe_gate_up_kernel<FP4_FMT_MX><<<g_gu, kThreads, 0, s>>>(p);
         else moe_gate_up_kernel<FP4_FMT_NV><<<g_gu, kThreads, 0, s>>>(p);
         if ((err = hipGetLastError()) != hipSuccess || (err = mark(3)) != hipSuccess) return err;
