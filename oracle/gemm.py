@@ -24,9 +24,12 @@ from . import quant as Q
 
 
 def operand_values(fmt: str, codes, scales, s_t=None) -> np.ndarray:
-    """Exact real operand values [R, K] in fp64 (NV without s_t applied)."""
+    """Exact real operand values [R, K] in fp64 (NV without s_t applied);
+    fmt "mx8" is MXFP8 (E4M3 bytes [R, K])."""
     if fmt == "mx":
         return Q.mx_dequant_f64(codes, scales)
+    if fmt == "mx8":
+        return Q.mxfp8_dequant_f64(codes, scales)
     c4 = Q.unpack_nibbles(codes)
     R, K = c4.shape
     sg = F.e4m3_value_f64(scales)
@@ -43,6 +46,35 @@ def gemm_ref(fmt: str, a_codes, a_scales, b_codes, b_scales, a_st=None, b_st=Non
         st = float(np.float32(a_st)) * float(np.float32(b_st))
         C, S = C * st, S * st
     return C, S
+
+
+def gemm_ref_w4a8(a_codes8, a_scales, b_codes, b_scales):
+    """W4A4's FP8-activation variant [V4-QAT s4.3]: C = A_hat . B_hat^T with A
+    MXFP8 [M, K] and B MXFP4 [N, K/2]; returns C_ref and the bound S in fp64.
+    A product of an E4M3 and an E2M1 value has at most 6 significant bits, so
+    each term is exact; the fp64 sum's own rounding (at most K * 2**-53 * S)
+    is far inside the 1e-5 * S tolerance."""
+    A = Q.mxfp8_dequant_f64(a_codes8, a_scales)
+    B = Q.mx_dequant_f64(b_codes, b_scales)
+    return A @ B.T, np.abs(A) @ np.abs(B).T
+
+
+def gemm_exact_fraction_w4a8(a_codes8, a_scales, b_codes, b_scales):
+    """Brute force for tiny W4A8 inputs in Python ``Fraction``s, element by element
+    from the byte fields (independent of the fp64 tables)."""
+    cb = Q.unpack_nibbles(b_codes)
+    M, K = np.asarray(a_codes8).shape
+    N = cb.shape[0]
+    out = [[Fraction(0)] * N for _ in range(M)]
+    for m in range(M):
+        for n in range(N):
+            acc = Fraction(0)
+            for k in range(K):
+                a = F.e4m3_decode(int(a_codes8[m, k])) * F.ue8m0_value(int(a_scales[m, k // Q.MX_BLOCK]))
+                b = F.e2m1_value(int(cb[n, k])) * F.ue8m0_value(int(b_scales[n, k // Q.MX_BLOCK]))
+                acc += a * b
+            out[m][n] = acc
+    return out
 
 
 def gemm_exact_fraction(fmt: str, a_codes, a_scales, b_codes, b_scales, a_st=None, b_st=None):

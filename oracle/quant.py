@@ -33,6 +33,19 @@ MXFP4 weights block by block without loss]:
   E4M3 value for j in [-9, 8], so block b is exact iff E_b >= E_max - 17 or all
   of its codes are zero; other blocks are counted as inexact.
 
+MXFP8 (the activations of the W4A8 GEMM) [V4-QAT s4.3: FP4 weights times
+FP8 activations; FP4-101: weights in FP4, activations kept in FP8; V4-ARCH
+s6.3 and V41-NVFP4 s3: 1x32 blocks with one UE8M0 scale].  The pages do not
+spell out the FP8 block rule; the reading taken mirrors the MX rule with E4M3
+elements: E = floor(log2 amax) - 8 (8 is E4M3's largest exponent, as 2 is
+E2M1's), E = -127 when amax = 0, clamped to [-127, 127]; scale byte E + 127;
+each code = E4M3_RNE(x * 2**-E) on the magnitude, saturating at 448 (bytes
+0x7F/0xFF, the NaN encodings, never occur), sign copied from the input.
+
+FP4 -> FP8 [V4-QAT s4.2, V4-ARCH s6.3: FP4 data dequantize to FP8 without
+loss]: every E2M1 magnitude is an E4M3 value, so an MXFP4 block becomes an
+MXFP8 block with the same scale byte and each code re-encoded exactly.
+
 Dequantize [V41-NVFP4 s2: the accumulator multiplies scales back;
 V4-QAT s4.2 FP4 dequant through the scale]:
   MX: (-1)^s MAG[i] 2**E, exact in fp32 and bf16.
@@ -49,6 +62,7 @@ from . import formats as F
 
 MX_BLOCK = 32
 NV_GROUP = 16
+MX8_EMAX = 8                     # largest E4M3 exponent: 448 = 1.75 * 2**8
 NV_TENSOR_DIV = 6 * 448          # amax_t / (6 * 448): E2M1 max times E4M3 max
 
 
@@ -133,6 +147,83 @@ def mx_dequant_f64(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     e = np.asarray(scales, dtype=np.int64) - 127
     v = code_values_f64(c4).reshape(R, K // MX_BLOCK, MX_BLOCK) * np.ldexp(1.0, e)[..., None]
     return v.reshape(R, K)
+
+
+# ====================================================================== MXFP8
+def mxfp8_block_exact(bits: list[int]) -> tuple[list[int], int]:
+    """One 32-element MXFP8 block from bf16 bit patterns: (E4M3 bytes, scale byte)."""
+    vals = [F.bf16_bits_to_fraction(b) for b in bits]
+    amax = max(abs(v) for v in vals)
+    E = -127 if amax == 0 else F.floor_log2(amax) - MX8_EMAX
+    E = min(max(E, -127), 127)
+    inv = Fraction(2) ** -E
+    codes = [F.e4m3_encode(F.round_e4m3_sat(abs(v) * inv)) | (0x80 if b >> 15 else 0)
+             for b, v in zip(bits, vals)]
+    return codes, E + 127
+
+
+def mxfp8_quantize_exact(xbits: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Scalar-loop MXFP8 quantize of a small [R, K] bf16 array: (E4M3 bytes [R, K],
+    UE8M0 scales [R, K/32])."""
+    R, K = xbits.shape
+    assert K % MX_BLOCK == 0
+    codes = np.zeros((R, K), dtype=np.uint8)
+    scales = np.zeros((R, K // MX_BLOCK), dtype=np.uint8)
+    for r in range(R):
+        for b in range(K // MX_BLOCK):
+            c, sb = mxfp8_block_exact([int(v) for v in xbits[r, b * 32:(b + 1) * 32]])
+            codes[r, b * 32:(b + 1) * 32] = c
+            scales[r, b] = sb
+    return codes, scales
+
+
+def mxfp8_quantize(xbits: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """MXFP8 quantize [R, K] bf16 bits -> (E4M3 bytes [R, K], UE8M0 scales [R, K/32]).
+
+    fp64 is exact: x * 2**-E only shifts a bf16 value's exponent, and the E4M3
+    rounding compares it with exact midpoints of the E4M3 table.
+    """
+    xbits = np.asarray(xbits, dtype=np.uint16)
+    R, K = xbits.shape
+    assert K % MX_BLOCK == 0
+    x = F.bf16_bits_to_f64(xbits).reshape(R, K // MX_BLOCK, MX_BLOCK)
+    amax = np.abs(x).max(axis=-1)
+    E = np.full(amax.shape, -127, dtype=np.int64)
+    nz = amax > 0
+    E[nz] = F.frexp_floor_log2(amax[nz]) - MX8_EMAX
+    E = np.clip(E, -127, 127)
+    v = np.abs(x) * np.ldexp(1.0, -E)[..., None]
+    mag = F.e4m3_rne_sat_f64(v)
+    sign = ((xbits.reshape(R, K // MX_BLOCK, MX_BLOCK) >> 15) & 1).astype(np.uint8)
+    codes = (mag | (sign << 7)).astype(np.uint8)
+    return codes.reshape(R, K), (E + 127).astype(np.uint8)
+
+
+def e4m3_signed_f64(codes: np.ndarray) -> np.ndarray:
+    """Signed fp64 values of E4M3 bytes (no NaN encodings)."""
+    c = np.asarray(codes, dtype=np.uint8)
+    v = F.e4m3_value_f64(c & 0x7F)
+    return np.where(c & 0x80, -v, v)
+
+
+def mxfp8_dequant_f64(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Exact real values of MXFP8 data as fp64 [R, K] (E4M3 value times 2**E)."""
+    c = np.asarray(codes, dtype=np.uint8)
+    R, K = c.shape
+    e = np.asarray(scales, dtype=np.int64) - 127
+    v = e4m3_signed_f64(c).reshape(R, K // MX_BLOCK, MX_BLOCK) * np.ldexp(1.0, e)[..., None]
+    return v.reshape(R, K)
+
+
+# E4M3 byte of each E2M1 magnitude index (0, 0.5, 1, 1.5, 2, 3, 4, 6)
+E2M1_TO_E4M3 = np.array([F.e4m3_encode(F.E2M1_MAG[i]) for i in range(8)], dtype=np.uint8)
+
+
+def mx_to_mxfp8(codes: np.ndarray) -> np.ndarray:
+    """MXFP4 codes [R, K/2] -> E4M3 bytes [R, K] of the same values (the scale
+    bytes carry over unchanged): exact, as E2M1 magnitudes are E4M3 values."""
+    c4 = unpack_nibbles(codes)
+    return (E2M1_TO_E4M3[c4 & 7] | ((c4 & 8) << 4)).astype(np.uint8)
 
 
 # ====================================================================== NV
