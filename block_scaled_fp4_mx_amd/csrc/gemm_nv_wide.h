@@ -192,17 +192,21 @@ __device__ __forceinline__ void nw_mainloop(NwSmem<TM, NS, ACODES>& sm, const Nw
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
+            // the sub-step's A fragment reads go out first and land while B is expanded
+            h8_t a[MF > 0 ? MF : 1];
+#pragma unroll
+            for (int mf = 0; mf < MF; ++mf) {
+                const int row = mf * 16 + lr;
+                a[mf] = *reinterpret_cast<const h8_t*>(&ab[row * kNwARow + (((4 * lq + i) ^ (row & 15)) << 4)]);
+            }
             h8_t bx[4];
 #pragma unroll
             for (int nf = 0; nf < 4; ++nf) bx[nf] = nv_expand8(nw_word(c[nf], i), sp[nf][i >> 1]);
 #pragma unroll
-            for (int mf = 0; mf < MF; ++mf) {
-                const int row = mf * 16 + lr;
-                const h8_t a = *reinterpret_cast<const h8_t*>(&ab[row * kNwARow + (((4 * lq + i) ^ (row & 15)) << 4)]);
+            for (int mf = 0; mf < MF; ++mf)
 #pragma unroll
                 for (int nf = 0; nf < 4; ++nf)
-                    acc[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bx[nf], acc[mf][nf], 0, 0, 0);
-            }
+                    acc[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mf], bx[nf], acc[mf][nf], 0, 0, 0);
         }
     }
 }
