@@ -15,7 +15,7 @@ import torch
 __all__ = [
     "lib", "Fp4Error", "FMT_MX", "FMT_NV", "DT_BF16", "DT_F32",
     "fp4_quantize_mx", "fp4_quantize_nv", "fp4_quantize_nv_workspace_bytes", "fp4_remap_mx_to_nv",
-    "fp4_dequant", "fp4_gemm", "fp4_moe_grouped_gemm", "fp4_moe_workspace_bytes", "MoeDebug",
+    "fp4_dequant", "fp4_gemm", "fp4_quantize_mxfp8", "fp4_mx_to_mxfp8", "fp4_gemm_w4a8", "fp4_moe_grouped_gemm", "fp4_moe_workspace_bytes", "MoeDebug",
     "fp4_abi_version", "LIB_PATH",
 ]
 
@@ -44,6 +44,9 @@ _SIGS = {
     "fp4_remap_mx_to_nv": (_i32, [_vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp]),
     "fp4_dequant": (_i32, [_i32, _vp, _vp, _vp, _i64, _i64, _vp, _i32, _i64, _vp]),
     "fp4_gemm": (_i32, [_i32, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _i32, _i64, _vp]),
+    "fp4_quantize_mxfp8": (_i32, [_vp, _i64, _i64, _i64, _vp, _vp, _vp]),
+    "fp4_mx_to_mxfp8": (_i32, [_vp, _i64, _i64, _vp, _vp]),
+    "fp4_gemm_w4a8": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _i32, _i64, _vp]),
     "fp4_moe_grouped_gemm": (_i32, [_i32, _vp, _i64, _i64, _vp, _vp, _i32, _i32, _i64, _vp, _vp, _vp,
                                      _vp, _vp, _vp, _vp, _vp, _vp, _sz, _c.POINTER(MoeDebug), _vp]),
     "fp4_moe_workspace_bytes": (_sz, [_i32, _i64, _i64, _i32, _i32, _i64]),
@@ -141,6 +144,30 @@ def fp4_gemm(fmt, a_codes, a_scales, b_codes, b_scales, c, a_tensor_scale=None, 
     _check("fp4_gemm", lib.fp4_gemm(fmt, _ptr(a_codes), _ptr(a_scales), _ptr(a_tensor_scale), _ptr(b_codes),
                                     _ptr(b_scales), _ptr(b_tensor_scale), m, n, k, _ptr(c), dt, ldc,
                                     _stream(stream)))
+
+
+def fp4_quantize_mxfp8(x, codes8, scales, rows=None, k=None, ld_x=None, stream=None):
+    rows = x.shape[0] if rows is None else rows
+    k = x.shape[1] if k is None else k
+    ld_x = x.stride(0) if ld_x is None else ld_x
+    _check("fp4_quantize_mxfp8", lib.fp4_quantize_mxfp8(_ptr(x), rows, k, ld_x, _ptr(codes8), _ptr(scales),
+                                                        _stream(stream)))
+
+
+def fp4_mx_to_mxfp8(codes, codes8, rows=None, k=None, stream=None):
+    rows = codes.shape[0] if rows is None else rows
+    k = codes.shape[1] * 2 if k is None else k
+    _check("fp4_mx_to_mxfp8", lib.fp4_mx_to_mxfp8(_ptr(codes), rows, k, _ptr(codes8), _stream(stream)))
+
+
+def fp4_gemm_w4a8(a_codes8, a_scales, b_codes, b_scales, c, m=None, n=None, k=None, ldc=None, stream=None):
+    m = a_codes8.shape[0] if m is None else m
+    n = b_codes.shape[0] if n is None else n
+    k = a_codes8.shape[1] if k is None else k
+    ldc = c.stride(0) if ldc is None else ldc
+    dt = DT_F32 if c.dtype == torch.float32 else DT_BF16
+    _check("fp4_gemm_w4a8", lib.fp4_gemm_w4a8(_ptr(a_codes8), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales), m, n, k,
+                                              _ptr(c), dt, ldc, _stream(stream)))
 
 
 def fp4_moe_workspace_bytes(fmt, tokens, hidden, topk, num_experts, inter) -> int:

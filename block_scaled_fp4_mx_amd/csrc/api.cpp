@@ -181,6 +181,51 @@ int fp4_gemm(fp4_format fmt, const uint8_t* a_codes, const uint8_t* a_scales, co
     return hip_status(e, "fp4_gemm launch");
 }
 
+int fp4_quantize_mxfp8(const void* x_bf16, int64_t rows, int64_t k, int64_t ld_x, uint8_t* codes8, uint8_t* scales,
+                       void* stream) {
+    FP4_REQUIRE(rows >= 0 && k >= 0, FP4_ERR_INVALID, "negative size rows=%lld k=%lld", (long long)rows, (long long)k);
+    FP4_REQUIRE(k % 32 == 0, FP4_ERR_SHAPE, "k=%lld is not a multiple of 32", (long long)k);
+    if (rows == 0 || k == 0) return ok();
+    FP4_PTR(x_bf16);
+    FP4_PTR(codes8);
+    FP4_PTR(scales);
+    if (int e = check_ld(ld_x, k, "ld_x")) return e;
+    return hip_status(fp4::launch_quantize_mxfp8(static_cast<const uint16_t*>(x_bf16), rows, k, ld_x, codes8, scales,
+                                                 static_cast<hipStream_t>(stream)),
+                      "fp4_quantize_mxfp8 launch");
+}
+
+int fp4_mx_to_mxfp8(const uint8_t* codes, int64_t rows, int64_t k, uint8_t* codes8, void* stream) {
+    FP4_REQUIRE(rows >= 0 && k >= 0, FP4_ERR_INVALID, "negative size rows=%lld k=%lld", (long long)rows, (long long)k);
+    FP4_REQUIRE(k % 32 == 0, FP4_ERR_SHAPE, "k=%lld is not a multiple of 32", (long long)k);
+    if (rows == 0 || k == 0) return ok();
+    FP4_PTR(codes);
+    FP4_PTR(codes8);
+    return hip_status(fp4::launch_mx_to_mxfp8(codes, rows, k, codes8, static_cast<hipStream_t>(stream)),
+                      "fp4_mx_to_mxfp8 launch");
+}
+
+int fp4_gemm_w4a8(const uint8_t* a_codes8, const uint8_t* a_scales, const uint8_t* b_codes, const uint8_t* b_scales,
+                  int64_t m, int64_t n, int64_t k, void* c, fp4_dtype c_dtype, int64_t ldc, void* stream) {
+    FP4_REQUIRE(c_dtype == FP4_DT_BF16 || c_dtype == FP4_DT_F32, FP4_ERR_INVALID, "bad dtype %d", (int)c_dtype);
+    FP4_REQUIRE(m >= 0 && n >= 0 && k >= 0, FP4_ERR_INVALID, "negative size m=%lld n=%lld k=%lld", (long long)m,
+                (long long)n, (long long)k);
+    FP4_REQUIRE(k % 32 == 0, FP4_ERR_SHAPE, "k=%lld is not a multiple of 32", (long long)k);
+    FP4_REQUIRE(m < (int64_t)65535 * 128, FP4_ERR_SHAPE, "m=%lld too large", (long long)m);
+    if (m == 0 || n == 0) return ok();
+    FP4_PTR(c);
+    FP4_REQUIRE(ldc >= n, FP4_ERR_INVALID, "ldc (%lld) < n (%lld)", (long long)ldc, (long long)n);
+    if (k > 0) {
+        FP4_PTR(a_codes8);
+        FP4_PTR(a_scales);
+        FP4_PTR(b_codes);
+        FP4_PTR(b_scales);
+    }
+    return hip_status(fp4::launch_gemm_w4a8(a_codes8, a_scales, b_codes, b_scales, m, n, k, c, c_dtype == FP4_DT_F32,
+                                            ldc, static_cast<hipStream_t>(stream)),
+                      "fp4_gemm_w4a8 launch");
+}
+
 size_t fp4_moe_workspace_bytes(fp4_format fmt, int64_t tokens, int64_t hidden, int topk, int num_experts,
                                int64_t inter) {
     if (tokens < 0 || hidden <= 0 || topk < 1 || num_experts < 1 || inter <= 0) return 0;

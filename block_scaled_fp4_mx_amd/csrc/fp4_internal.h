@@ -76,6 +76,9 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // Each returns hipSuccess or the launch error.  Shapes are validated by the caller.
 hipError_t launch_quantize_mx(const uint16_t* x, int64_t rows, int64_t k, int64_t ldx,
                               uint8_t* codes, uint8_t* scales, hipStream_t s);
+hipError_t launch_quantize_mxfp8(const uint16_t* x, int64_t rows, int64_t k, int64_t ldx,
+                                 uint8_t* codes, uint8_t* scales, hipStream_t s);
+hipError_t launch_mx_to_mxfp8(const uint8_t* codes, int64_t rows, int64_t k, uint8_t* codes8, hipStream_t s);
 hipError_t launch_quantize_nv(const uint16_t* x, int64_t rows, int64_t k, int64_t ldx,
                               uint8_t* codes, uint8_t* scales, float* tensor_scale,
                               bool ts_is_input, uint32_t* amax_ws, hipStream_t s);
@@ -91,6 +94,9 @@ hipError_t launch_gemm_nv(const uint8_t* ac, const uint8_t* as, const float* ats
                           const uint8_t* bc, const uint8_t* bs, const float* bts,
                           int64_t m, int64_t n, int64_t k, void* c, int c_f32, int64_t ldc,
                           hipStream_t s);
+
+hipError_t launch_gemm_w4a8(const uint8_t* a8, const uint8_t* as, const uint8_t* bc, const uint8_t* bs,
+                            int64_t m, int64_t n, int64_t k, void* c, int c_f32, int64_t ldc, hipStream_t s);
 
 struct MoeArgs {
     int fmt;

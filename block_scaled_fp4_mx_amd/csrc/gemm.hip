@@ -14,6 +14,7 @@
 // scales multiply the fp32 accumulator at the end.
 #include "gemm_mx_tile.h"
 #include "gemm_nv_wide.h"
+#include "gemm_w4a8_tile.h"
 #include "mma_core.h"
 
 namespace fp4 {
@@ -21,6 +22,7 @@ namespace {
 
 constexpr int kBM = 128, kBN = 128, kThreads = 256;
 constexpr int kNvGemmTM = 64;   // A rows per NV GEMM tile (wide tile, three stages, A as codes)
+constexpr bool kW8Lag = true;   // W4A8 tile: half the waves run half a step behind
 
 // 16x16 accumulator layout: lane holds rows 4*(lane/16) + r, column lane % 16.
 __device__ __forceinline__ void store_tile(const v4f acc[4][4], void* c, int c_f32, int64_t ldc, int64_t m,
@@ -43,7 +45,9 @@ __device__ __forceinline__ void store_tile(const v4f acc[4][4], void* c, int c_f
             }
 }
 
-// Block tile 128x128: four waves in a 2x2 grid, each a 64x64 MMA core.
+// Block tile 128x128: four waves in a 2x2 grid, each a 64x64 MMA core.  FMT is
+// FP4_FMT_MX, FP4_FMT_NV or kFmtW4A8 (MXFP8 A times MXFP4 B).
+constexpr int kFmtW4A8 = 2;
 template <int FMT>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(
     const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as, const float* __restrict__ ats,
@@ -52,13 +56,14 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t m0 = (int64_t)blockIdx.y * kBM + (wave >> 1) * 64;
     const int64_t n0 = (int64_t)blockIdx.x * kBN + (wave & 1) * 64;
-    const int blk = FMT == FP4_FMT_MX ? 32 : 16;
+    const int blk = FMT == FP4_FMT_NV ? 16 : 32;
+    const int64_t a_row_bytes = FMT == kFmtW4A8 ? k : k / 2;
     const int lr = lane & 15;
     const uint8_t *a_rows[4], *a_srow[4], *b_rows[4], *b_srow[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int64_t r = m0 + i * 16 + lr;
-        a_rows[i] = r < m ? ac + r * (k / 2) : nullptr;
+        a_rows[i] = r < m ? ac + r * a_row_bytes : nullptr;
         a_srow[i] = r < m ? as + r * (k / blk) : nullptr;
         const int64_t q = n0 + i * 16 + lr;
         b_rows[i] = q < n ? bc + q * (k / 2) : nullptr;
@@ -69,6 +74,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     float scale = 1.0f;
     if (FMT == FP4_FMT_MX) {
         mma_mx_64x64(acc, a_rows, a_srow, b_rows, b_srow, k, lane);
+    } else if (FMT == kFmtW4A8) {
+        mma_w4a8_64x64(acc, a_rows, a_srow, b_rows, b_srow, k, lane);
     } else {
         mma_nv_64x64(acc, a_rows, a_srow, b_rows, b_srow, k, lane);
         scale = __fmul_rn(*ats, *bts);
@@ -91,6 +98,35 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, i
     const int r = t - group * G * tiles_n;
     tm = group * G + r % rows_in_group;
     tn = r / rows_in_group;
+}
+
+// Stores rows_pass rows of a tile staged in LDS (row r's 16-byte chunk c at
+// chunk c ^ (r & 15), rowb bytes per row) to C rows grow0 .. and columns n0 ..,
+// one 16-byte piece per thread and iteration; pieces past m or n are dropped
+// or written element by element.
+__device__ __forceinline__ void store_rows_from_lds(const uint8_t* csm, int rows_pass, int chunks_row, int rowb,
+                                                    int64_t grow0, int64_t n0, int64_t m, int64_t n, void* c,
+                                                    int c_f32, int64_t ldc, bool vec) {
+    const int esz = c_f32 ? 4 : 2;
+    for (int q = threadIdx.x; q < rows_pass * chunks_row; q += blockDim.x) {
+        const int row = q / chunks_row, ch = q - row * chunks_row;
+        const int64_t grow = grow0 + row;
+        const int64_t gcol = n0 + ch * (16 / esz);
+        if (grow >= m || gcol >= n) continue;
+        const uint4 v = *reinterpret_cast<const uint4*>(csm + row * rowb + ((ch ^ (row & 15)) << 4));
+        uint8_t* dst = static_cast<uint8_t*>(c) + (grow * ldc + gcol) * esz;
+        if (vec && gcol + 16 / esz <= n) {
+            *reinterpret_cast<uint4*>(dst) = v;
+        } else {
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+            for (int e = 0; e < 16 / esz && gcol + e < n; ++e) {
+                if (c_f32)
+                    reinterpret_cast<uint32_t*>(dst)[e] = w[e];
+                else
+                    reinterpret_cast<uint16_t*>(dst)[e] = (uint16_t)(w[e >> 1] >> ((e & 1) * 16));
+            }
+        }
+    }
 }
 
 // MX GEMM on 256 x 256 tiles (LDS-staged, see gemm_mx_tile.h).
@@ -147,25 +183,62 @@ __global__ __launch_bounds__(kTileThreads, 1) void gemm_mx_256_kernel(
                 }
         }
         __syncthreads();
-        for (int q = t; q < rows_pass * chunks_row; q += kTileThreads) {
-            const int row = q / chunks_row, ch = q - row * chunks_row;
-            const int64_t grow = m0 + pass * rows_pass + row;
-            const int64_t gcol = n0 + ch * (16 / esz);
-            if (grow >= m || gcol >= n) continue;
-            const uint4 v = *reinterpret_cast<const uint4*>(csm + row * rowb + ((ch ^ (row & 15)) << 4));
-            uint8_t* dst = static_cast<uint8_t*>(c) + (grow * ldc + gcol) * esz;
-            if (vec && gcol + 16 / esz <= n) {
-                *reinterpret_cast<uint4*>(dst) = v;
-            } else {
-                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-                for (int e = 0; e < 16 / esz && gcol + e < n; ++e) {
+        store_rows_from_lds(csm, rows_pass, chunks_row, rowb, m0 + pass * rows_pass, n0, m, n, c, c_f32, ldc, vec);
+    }
+}
+
+// W4A8 GEMM on 256 x 256 tiles (gemm_w4a8_tile.h): MXFP8 activations (A,
+// [m, k] bytes) times MXFP4 weights (B, [n, k/2]).  Epilogue as in the MX
+// kernel: the accumulators go to LDS in passes of 128 (bf16) or 64 (fp32) rows
+// and leave as whole-row 16-byte pieces.
+template <bool LAG>
+__global__ __launch_bounds__(kW8Threads, 1) void gemm_w4a8_256_kernel(
+    const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as, const uint8_t* __restrict__ bc,
+    const uint8_t* __restrict__ bs, int64_t m, int64_t n, int64_t k, void* __restrict__ c, int c_f32,
+    int64_t ldc, int tiles_m, int tiles_n) {
+    __shared__ __align__(16) W8Smem sm;
+    int tm, tn;
+    tile_coords(tiles_m, tiles_n, tm, tn);
+    const int64_t m0 = (int64_t)tm * kW8TileM, n0 = (int64_t)tn * kW8TileN;
+    W8Src S;
+    w8_src(S, ac, as, bc, bs, m0, n0, m, n, k);
+    v4f acc[kW8FragsN][kW8FragsM];
+#pragma unroll
+    for (int j = 0; j < kW8FragsN; ++j)
+#pragma unroll
+        for (int i = 0; i < kW8FragsM; ++i) acc[j][i] = v4f{0.f, 0.f, 0.f, 0.f};
+    w8_mainloop<LAG>(sm, S, (int)(k / kW8StepK), acc);
+
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6, wm = wave >> 1, wn = wave & 1;
+    const int lr = lane & 15, lk = lane >> 4;
+    const int esz = c_f32 ? 4 : 2;
+    const int rowb = kW8TileN * esz;
+    const int rows_pass = c_f32 ? 64 : 128;
+    static_assert(128 * kW8TileN * 2 <= (int)sizeof(W8Smem), "C staging exceeds the tile's LDS");
+    const int chunks_row = rowb / 16;
+    const bool vec = ((ldc * esz) & 15) == 0;
+    uint8_t* csm = reinterpret_cast<uint8_t*>(&sm);
+    for (int pass = 0; pass < kW8TileM / rows_pass; ++pass) {
+        __syncthreads();
+        if ((wm * 64) / rows_pass == pass) {
+#pragma unroll
+            for (int j = 0; j < kW8FragsN; ++j)
+#pragma unroll
+                for (int i = 0; i < kW8FragsM; ++i) {
+                    const int row = wm * 64 - pass * rows_pass + i * 16 + lr;
+                    const int colb = (wn * 128 + j * 16 + lk * 4) * esz;
+                    uint8_t* dst = csm + row * rowb + ((((colb >> 4) ^ (row & 15)) << 4) | (colb & 15));
+                    const v4f v = acc[j][i];
                     if (c_f32)
-                        reinterpret_cast<uint32_t*>(dst)[e] = w[e];
+                        *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
                     else
-                        reinterpret_cast<uint16_t*>(dst)[e] = (uint16_t)(w[e >> 1] >> ((e & 1) * 16));
+                        *reinterpret_cast<uint2*>(dst) =
+                            make_uint2(f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16),
+                                       f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16));
                 }
-            }
         }
+        __syncthreads();
+        store_rows_from_lds(csm, rows_pass, chunks_row, rowb, m0 + pass * rows_pass, n0, m, n, c, c_f32, ldc, vec);
     }
 }
 
@@ -259,6 +332,20 @@ hipError_t launch_gemm_mx(const uint8_t* ac, const uint8_t* as, const uint8_t* b
     } else {
         dim3 grid((unsigned)((n + kBN - 1) / kBN), (unsigned)((m + kBM - 1) / kBM));
         gemm_kernel<FP4_FMT_MX><<<grid, kThreads, 0, s>>>(ac, as, nullptr, bc, bs, nullptr, m, n, k, c, c_f32, ldc);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_w4a8(const uint8_t* ac, const uint8_t* as, const uint8_t* bc, const uint8_t* bs,
+                            int64_t m, int64_t n, int64_t k, void* c, int c_f32, int64_t ldc, hipStream_t s) {
+    const int64_t tiles_m = (m + kW8TileM - 1) / kW8TileM, tiles_n = (n + kW8TileN - 1) / kW8TileN;
+    const bool small_ops = m * k < (1ll << 31) && n * (k / 2) < (1ll << 31);
+    if (k % 512 == 0 && k > 0 && small_ops && tiles_m * tiles_n >= 64 && tiles_m * tiles_n < (1ll << 31)) {
+        gemm_w4a8_256_kernel<kW8Lag><<<(unsigned)(tiles_m * tiles_n), kW8Threads, 0, s>>>(
+            ac, as, bc, bs, m, n, k, c, c_f32, ldc, (int)tiles_m, (int)tiles_n);
+    } else {
+        dim3 grid((unsigned)((n + kBN - 1) / kBN), (unsigned)((m + kBM - 1) / kBM));
+        gemm_kernel<kFmtW4A8><<<grid, kThreads, 0, s>>>(ac, as, nullptr, bc, bs, nullptr, m, n, k, c, c_f32, ldc);
     }
     return hipGetLastError();
 }

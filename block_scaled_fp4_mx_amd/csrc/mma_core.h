@@ -71,6 +71,56 @@ __device__ __forceinline__ void mma_mx_64x64(v4f acc[4][4], const uint8_t* const
     }
 }
 
+// W4A8 core over k (a multiple of 32; blocks past the end read as zero): B is
+// MXFP4 as above (lane group g: block kb0 + g and its scale); A is MXFP8, whose
+// 8-register operand in the mixed-format MFMA holds, for lane group g, the
+// step's K values 16g .. 16g + 15 in bytes 0-15 and 64 + 16g .. 64 + 16g + 15
+// in bytes 16-31 (measured on gfx950), while the scale operand of lane group g
+// is still block kb0 + g's.  E4M3 (format 0) times E2M1 (format 4).
+__device__ __forceinline__ void mma_w4a8_64x64(v4f acc[4][4], const uint8_t* const a_rows[4],
+                                               const uint8_t* const a_srow[4], const uint8_t* const b_rows[4],
+                                               const uint8_t* const b_srow[4], int64_t k, int lane) {
+    const int64_t kb_total = k / 32;
+    const int lk = lane >> 4;
+    for (int64_t kb0 = 0; kb0 < kb_total; kb0 += 4) {
+        const int64_t kb = kb0 + lk;
+        const bool kin = kb < kb_total;
+        const bool lo_in = kb0 + (lk >> 1) < kb_total, hi_in = kb0 + 2 + (lk >> 1) < kb_total;
+        v8i a[4], b[4];
+        int sa[4], sb[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            uint4 lo = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0);
+            int s = 127;
+            if (a_rows[i]) {
+                const uint8_t* p = a_rows[i] + kb0 * 32 + lk * 16;
+                if (lo_in) lo = *reinterpret_cast<const uint4*>(p);
+                if (hi_in) hi = *reinterpret_cast<const uint4*>(p + 64);
+                if (kin) s = a_srow[i][kb];
+            }
+            a[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            sa[i] = s;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            uint4 v = make_uint4(0, 0, 0, 0);
+            int s = 127;
+            if (kin && b_rows[j]) {
+                v = *reinterpret_cast<const uint4*>(b_rows[j] + kb * 16);
+                s = b_srow[j][kb];
+            }
+            b[j] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+            sb[j] = s;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[i], b[j], acc[i][j], 0, 4, 0, sa[i],
+                                                                               0, sb[j]);
+    }
+}
+
 // Expand 8 codes (one 32-bit word of one 16-group) with group scale s_g to bf16.
 __device__ __forceinline__ bf16x8 expand_nv8(uint32_t codes, float sg) {
     u16x8 r;

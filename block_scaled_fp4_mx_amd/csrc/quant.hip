@@ -1,4 +1,5 @@
-// Block-scaled FP4 quantize / dequantize / MX->NV remap kernels for gfx950.
+// Block-scaled FP4 (and MXFP8 activation) quantize / dequantize / MX->NV remap
+// kernels for gfx950.
 //
 // All four are HBM-streaming kernels: one lane owns 8 consecutive elements
 // (one 16-byte bf16 load, one 4-byte code store), so a wavefront reads 1 KiB of
@@ -56,6 +57,50 @@ __global__ __launch_bounds__(kThreads) void mx_quantize_kernel(
                 if ((threadIdx.x & 3) == 0) scales[u >> 2] = (uint8_t)sbyte;
             }
         }
+    }
+}
+
+// ------------------------------------------------------------------ MXFP8 quantize
+// Same lane mapping as the MX quantizer: lane u owns elements 8u..8u+7 (codes
+// bytes 8u..8u+7, one 8-byte store) and a quad of lanes one 32-element block.
+template <bool kContig>
+__global__ __launch_bounds__(kThreads) void mxfp8_quantize_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t k, int64_t ldx,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+    const int64_t upr = k >> 3;
+    const int64_t total = rows * upr;
+    const int64_t step = (int64_t)gridDim.x * kThreads * kMxUnroll;
+    for (int64_t base = (int64_t)blockIdx.x * kThreads * kMxUnroll + threadIdx.x; base < total; base += step) {
+        uint4 v[kMxUnroll];
+#pragma unroll
+        for (int j = 0; j < kMxUnroll; ++j) {
+            const int64_t u = base + (int64_t)j * kThreads;
+            if (u < total) v[j] = *reinterpret_cast<const uint4*>(x + x_offset<kContig>(u, upr, ldx));
+        }
+#pragma unroll
+        for (int j = 0; j < kMxUnroll; ++j) {
+            const int64_t u = base + (int64_t)j * kThreads;
+            if (u < total) {
+                const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+                uint32_t sbyte;
+                reinterpret_cast<uint2*>(codes)[u] = mxfp8_quant8(w, sbyte);
+                if ((threadIdx.x & 3) == 0) scales[u >> 2] = (uint8_t)sbyte;
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------ MXFP4 -> MXFP8
+// Lane u re-encodes code word u (8 E2M1 codes) into 8 E4M3 bytes; the UE8M0
+// scales carry over unchanged, so the caller keeps using the same scale tensor.
+__global__ __launch_bounds__(kThreads) void mx_to_mxfp8_kernel(const uint32_t* __restrict__ codes, int64_t words,
+                                                              uint2* __restrict__ out) {
+    for (int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x; u < words; u += (int64_t)gridDim.x * kThreads) {
+        const uint32_t w = codes[u];
+        uint32_t o[2] = {0u, 0u};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i >> 2] |= e2m1_to_e4m3((w >> (4 * i)) & 15u) << (8 * (i & 3));
+        out[u] = make_uint2(o[0], o[1]);
     }
 }
 
@@ -306,6 +351,27 @@ hipError_t launch_quantize_mx(const uint16_t* x, int64_t rows, int64_t k, int64_
         mx_quantize_kernel<true><<<g, kThreads, 0, s>>>(x, rows, k, ldx, codes, scales);
     else
         mx_quantize_kernel<false><<<g, kThreads, 0, s>>>(x, rows, k, ldx, codes, scales);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_mxfp8(const uint16_t* x, int64_t rows, int64_t k, int64_t ldx,
+                                 uint8_t* codes, uint8_t* scales, hipStream_t s) {
+    const int64_t units = rows * (k / 8);
+    unsigned g = grid_for(units, kMxUnroll);
+    if (g > kMxMaxBlocks) g = kMxMaxBlocks;
+    if (ldx == k)
+        mxfp8_quantize_kernel<true><<<g, kThreads, 0, s>>>(x, rows, k, ldx, codes, scales);
+    else
+        mxfp8_quantize_kernel<false><<<g, kThreads, 0, s>>>(x, rows, k, ldx, codes, scales);
+    return hipGetLastError();
+}
+
+hipError_t launch_mx_to_mxfp8(const uint8_t* codes, int64_t rows, int64_t k, uint8_t* codes8, hipStream_t s) {
+    const int64_t words = rows * (k / 8);
+    unsigned g = grid_for(words);
+    if (g > kMxMaxBlocks) g = kMxMaxBlocks;
+    mx_to_mxfp8_kernel<<<g, kThreads, 0, s>>>(reinterpret_cast<const uint32_t*>(codes), words,
+                                              reinterpret_cast<uint2*>(codes8));
     return hipGetLastError();
 }
 

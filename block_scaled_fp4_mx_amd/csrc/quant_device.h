@@ -58,6 +58,61 @@ __device__ __forceinline__ uint32_t mx_quant8(const uint32_t w[4], uint32_t& sby
     return p;
 }
 
+// MXFP8 (E4M3 elements, UE8M0 scale per 32) for the W4A8 activations: the
+// block exponent is E = floor(log2 amax) - 8, 8 being E4M3's largest exponent,
+// so the block maximum lands in [256, 512) and saturates at 448 when above it.
+// From the amax's exponent field e: byte = E + 127 = e - 8, clamped at 0.
+__device__ __forceinline__ uint32_t mxfp8_scale_byte(uint32_t amax_bits) {
+    const uint32_t e = amax_bits >> 7;
+    return e > 8u ? e - 8u : 0u;
+}
+
+// E4M3 magnitude byte of an exactly known fp32 value 0 <= v < 512, nearest
+// even, saturating at 448 (byte 0x7E).  Below 2^-6 the grid is the subnormal
+// one, multiples of 2^-9 (v * 512 is exact and rint rounds to even).  From
+// 2^-6 on, rounding v's fp32 pattern to 3 mantissa bits (add half an ulp of
+// the kept bits minus one, plus the kept lsb, then truncate) leaves
+// exponent:mantissa in bits 30:20 with any carry moved into the exponent; the
+// E4M3 byte is that field with the exponent rebiased from 127 to 7.
+__device__ __forceinline__ uint32_t e4m3_byte_f32(float v) {
+    const uint32_t b = __float_as_uint(v);
+    const uint32_t sub = (uint32_t)__builtin_rintf(v * 512.0f);
+    const uint32_t r = (b + 0x7FFFFu + ((b >> 20) & 1u)) >> 20;
+    const uint32_t nrm = min(r - (120u << 3), 0x7Eu);
+    return b < 0x3C800000u ? sub : nrm;
+}
+
+// MXFP8: quantize this lane's 8 elements (a quad of lanes is one block) to 8
+// E4M3 bytes (element i in byte i) and the block's UE8M0 byte.  |x| * 2^-E is
+// exact in fp32 whenever it is at least 2^-10 (a bf16 value times a power of
+// two stays exact down to fp32's subnormal range); smaller ones round to 0
+// either way.  The sign bit of x is copied, so -0 gives 0x80.
+__device__ __forceinline__ uint2 mxfp8_quant8(const uint32_t w[4], uint32_t& sbyte) {
+    uint32_t am = mag_max8(w);
+    am = max(am, quad_swap1(am));
+    am = max(am, quad_swap2(am));
+    sbyte = mxfp8_scale_byte(am);
+    const float inv = __uint_as_float((254u - sbyte) << 23);     // 2^(127 - byte) = 2^-E
+    uint32_t out[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t h = (w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+        const float v = __fmul_rn(__uint_as_float((h & 0x7FFFu) << 16), inv);
+        const uint32_t byte = e4m3_byte_f32(v) | ((h >> 8) & 0x80u);
+        out[i >> 2] |= byte << (8 * (i & 3));
+    }
+    return make_uint2(out[0], out[1]);
+}
+
+// E4M3 byte of an E2M1 code (lossless: E2M1 values are E4M3 values).  From the
+// fields: index e*2 + m with e > 0 is (1 + m/2) 2^(e-1), E4M3 exponent field
+// e + 6 and mantissa m << 2; index 1 is 0.5 = 2^-1 (field 6); index 0 is 0.
+__device__ __forceinline__ uint32_t e2m1_to_e4m3(uint32_t c) {
+    const uint32_t i = c & 7u, e = i >> 1, m = i & 1u;
+    const uint32_t mag = e ? (((e + 6u) << 3) | (m << 2)) : (m ? 48u : 0u);
+    return mag | ((c & 8u) << 4);
+}
+
 // Four fp32 pairs -> 8 E2M1 codes, round to nearest even (scale 1.0 = 2^0).
 __device__ __forceinline__ uint32_t cvt8_f32(const float v[8]) {
     uint32_t p = 0;

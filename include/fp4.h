@@ -149,6 +149,48 @@ int fp4_gemm(fp4_format fmt,
              void* c, fp4_dtype c_dtype, int64_t ldc, void* stream);
 
 /*
+ * W4A8: FP4 weights with FP8 activations ("DeepSeek-V4 FP4 QAT" article,
+ * section 4.3: the recommended deployment pairing; section 4.2: FP4 expands into
+ * FP8 without loss).  Activations use MXFP8: E4M3 elements (OCP FP8 E4M3FN,
+ * largest value 448) with one UE8M0 scale per 32 elements along k, the same
+ * block structure as the MXFP4 weights ("DeepSeek-V4" article, section 6.3;
+ * explainer section 3).
+ *
+ * fp4_quantize_mxfp8: per row and 32-element block, amax = max|x|;
+ *   E = floor(log2 amax) - 8 (8 = E4M3's largest exponent; E = -127 when
+ *   amax = 0), clamped to [-127, 127]; scales = E + 127; code byte = E4M3
+ *   round-to-nearest-even of |x| * 2^-E, saturating at 448 (0x7E), with the
+ *   sign bit of x in bit 7 (so -0.0 gives 0x80).
+ *   x_bf16: [rows, ld_x] bf16; codes8: [rows, k] bytes; scales: [rows, k/32].
+ *   Errors: k % 32 != 0 -> FP4_ERR_SHAPE.  Inputs must be finite.
+ */
+int fp4_quantize_mxfp8(const void* x_bf16, int64_t rows, int64_t k, int64_t ld_x,
+                       uint8_t* codes8, uint8_t* scales, void* stream);
+
+/*
+ * Lossless MXFP4 -> MXFP8 re-encoding (QAT article, section 4.2; explainer,
+ * section 6: E2M1 values are E4M3 values): every E2M1 code becomes the E4M3
+ * byte of the same value (sign kept, -0 -> 0x80); the UE8M0 scales are
+ * unchanged, so the caller pairs codes8 with the MXFP4 tensor's own scales.
+ * codes: [rows, k/2] packed E2M1; codes8: [rows, k] bytes.
+ * Errors: k % 32 != 0 -> FP4_ERR_SHAPE.
+ */
+int fp4_mx_to_mxfp8(const uint8_t* codes, int64_t rows, int64_t k, uint8_t* codes8, void* stream);
+
+/*
+ * W4A8 GEMM: C[m, n] = sum_k A_hat[m, k] * B_hat[n, k] with fp32 accumulation,
+ * A_hat the MXFP8 activations (a_codes8 [m, k] E4M3 bytes, a_scales [m, k/32])
+ * and B_hat the MXFP4 weights (b_codes [n, k/2], b_scales [n, k/32]), both
+ * exactly dequantized.  Mixed-format scaled MFMA (E4M3 x E2M1) with the UE8M0
+ * block scales applied by the matrix core.
+ * c: [m, ldc] of c_dtype.  Errors: k % 32 != 0 -> FP4_ERR_SHAPE.
+ */
+int fp4_gemm_w4a8(const uint8_t* a_codes8, const uint8_t* a_scales,
+                  const uint8_t* b_codes, const uint8_t* b_scales,
+                  int64_t m, int64_t n, int64_t k,
+                  void* c, fp4_dtype c_dtype, int64_t ldc, void* stream);
+
+/*
  * Optional intermediate outputs of fp4_moe_grouped_gemm, for staged testing.
  * Every member may be NULL.  Slot s = t * topk + j (token t, choice j).
  *   x_codes   uint8 [tokens, hidden/2], x_scales [tokens, hidden/32|16]  Q(x)
