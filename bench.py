@@ -7,8 +7,9 @@ are already resident in HBM:
             computed, and for the activation also with a calibrated one), the
             lossless MX->NV remap and an MX dequantize of the weight;
   gemm      the 4096^3 W4A4 MXFP4 GEMM (activations quantized on the fly,
-            weights pre-quantized, fp32 accumulation, bf16 output), and the
-            same product in NVFP4;
+            weights pre-quantized, fp32 accumulation, bf16 output), the same
+            product in NVFP4, and the W4A8 variant (MXFP8 activations quantized
+            on the fly times the MXFP4 weights);
   moe       the MoE layer at hidden 4096 (384 experts, top-6, intermediate
             2048, 8192 tokens, MXFP4 weights and activations), and the NVFP4
             MoE layer at hidden 7168 (intermediate 3072) on a decode batch of
@@ -52,6 +53,7 @@ METRIC = "W4A4 GEMM TFLOPS (% FP4 MFMA peak); quantize GB/s; MoE tokens/s at h=4
 PEAK_HBM_GBS = 8000.0
 PEAK_FP4_TFLOPS = 10100.0
 PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP8_TFLOPS = 5000.0
 MALL_BYTES = 256 << 20
 HERE = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_FILE = os.path.join(HERE, "profiles", "traffic.json")
@@ -99,7 +101,8 @@ def roofline_entry(bound, work, ms, per_unit, kernel, extra=None):
         peak, unit = PEAK_HBM_GBS, "GB/s"
     else:
         ach = work / (ms * 1e-3) / 1e12
-        peak, unit = (PEAK_BF16_TFLOPS, "TFLOP/s") if bound == "mfma_bf16" else (PEAK_FP4_TFLOPS, "TFLOP/s")
+        peak = {"mfma_bf16": PEAK_BF16_TFLOPS, "mfma_fp8": PEAK_FP8_TFLOPS}.get(bound, PEAK_FP4_TFLOPS)
+        unit = "TFLOP/s"
     e = dict(bound="mfma" if bound.startswith("mfma") else bound, achieved=round(ach, 1), peak=peak, unit=unit,
              frac=round(ach / peak, 4), traffic=None, avg_us=round(ms * 1e3, 2), work_per_launch=work,
              per_unit=per_unit, kernel=kernel)
@@ -185,6 +188,8 @@ def main():
 
     A3n, W3n = nv_quantized(A3), nv_quantized(W3)
     del W3
+    A3q8 = (torch.empty((4096, 4096), dtype=torch.uint8, device=dev),
+            torch.empty((4096, 4096 // 32), dtype=torch.uint8, device=dev))
 
     st = {"i": 0}
 
@@ -192,7 +197,7 @@ def main():
         return lst[st["i"] % len(lst)]
 
     M2, M2a = 4096 * 4096, 2048 * 4096
-    MXB, NVB = 2 + 0.5 + 1 / 32, 2 + 0.5 + 1 / 16
+    MXB, NVB, MX8B = 2 + 0.5 + 1 / 32, 2 + 0.5 + 1 / 16, 2 + 1 + 1 / 32
     stages = [
         Stage("quantize_mx_W", lambda: F.fp4_quantize_mx(cur(W2s), *W2mx), "hbm", M2 * MXB,
               "2.53125 B/elem (2 bf16 in, 0.5 codes, 1/32 scale out)", "mx_quantize_kernel"),
@@ -217,6 +222,10 @@ def main():
         Stage("gemm_nv_4096", lambda: F.fp4_gemm(F.FMT_NV, A3n[0], A3n[1], W3n[0], W3n[1], C3, A3n[2], W3n[2]),
               "mfma_bf16", 2.0 * 4096 ** 3, "2*M*N*K flop (fp16 MFMA on the exact expansion; 16-bit peak)",
               "gemm_nv_tile_kernel"),
+        Stage("gemm_quantize_A_mxfp8", lambda: F.fp4_quantize_mxfp8(cur(A3s), *A3q8), "hbm", 4096 * 4096 * MX8B,
+              "3.03125 B/elem (2 bf16 in, 1 E4M3 code, 1/32 scale out)", "mxfp8_quantize_kernel"),
+        Stage("gemm_w4a8_4096", lambda: F.fp4_gemm_w4a8(A3q8[0], A3q8[1], W3q[0], W3q[1], C3), "mfma_fp8",
+              2.0 * 4096 ** 3, "2*M*N*K flop (E4M3 x E2M1 MFMA; FP8 peak)", "gemm_w4a8_256_kernel"),
     ]
     want = set(args.only.split(",")) if args.only else None
     progress("linear and GEMM inputs ready")
@@ -325,11 +334,19 @@ def main():
         if qa:
             comps["gemm_with_onthefly_quantize_tflops"] = round(
                 2.0 * 4096 ** 3 / ((gemm["avg_us"] + qa["avg_us"]) * 1e-6) / 1e12, 1)
+    if "gemm_w4a8_4096" in rooflines:
+        g8 = rooflines["gemm_w4a8_4096"]
+        comps["gemm_w4a8_tflops"] = g8["achieved"]
+        comps["gemm_w4a8_frac_fp8_peak"] = g8["frac"]
+        q8 = rooflines.get("gemm_quantize_A_mxfp8")
+        if q8:
+            comps["gemm_w4a8_with_onthefly_quantize_tflops"] = round(
+                2.0 * 4096 ** 3 / ((g8["avg_us"] + q8["avg_us"]) * 1e-6) / 1e12, 1)
     if "gemm_nv_4096" in rooflines:
         comps["gemm_nv_tflops"] = rooflines["gemm_nv_4096"]["achieved"]
         comps["gemm_nv_frac_16bit_peak"] = rooflines["gemm_nv_4096"]["frac"]
     for n in ("quantize_mx_W", "quantize_mx_A", "quantize_nv_W", "quantize_nv_A", "quantize_nv_A_calibrated",
-              "gemm_quantize_A"):
+              "gemm_quantize_A", "gemm_quantize_A_mxfp8"):
         if n in rooflines:
             comps[n + "_GBps"] = rooflines[n]["achieved"]
     if "moe_h4096" in rooflines:
@@ -362,6 +379,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": "W4A4 MXFP4 GEMM M=N=K=4096 (bf16 out, fp32 accumulate) for value; per step also "
                                "MX/NV quantize of linear 4096x4096 W and 2048x4096 A, MX->NV remap, MX dequant, "
+                               "NVFP4 and W4A8 (MXFP8 x MXFP4) GEMMs at 4096^3, "
                                "MoE hidden 4096 (384 experts, top-6, inter 2048, 8192 tokens, MXFP4) and "
                                "NVFP4 MoE hidden 7168 (inter 3072) at 64 decode and 16384 prefill tokens",
                    "accumulate": "fp32", "traffic_source": "profiles/traffic.json" if traffic else None},
@@ -409,8 +427,7 @@ def moe_stage(torch, F, name, fmt, m, E, w13c, w13s, w2c, w2s, w13ts, w2ts, act,
              "routing": "route_count_kernel + route_scan_kernel + route_place_kernel",
              "gate_up": "moe_gate_up_mx256_kernel" if fmt == F.FMT_MX else
              f"expand_nv16_kernel (x) + {nv_gu}",
-             "down": "moe_down_mx256_kernel" if fmt == F.FMT_MX else
-             f"expand_nv16_kernel (h) + {nv_dn}",
+             "down": "moe_down_mx256_kernel" if fmt == F.FMT_MX else nv_dn,
              "combine": "combine_kernel"}
     if bound == "hbm":
         # decode: the expert weights dominate the bytes of both GEMMs

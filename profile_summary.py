@@ -40,14 +40,15 @@ ROWS = {
     "moe_h4096.combine": ("moe_h4096", [("combine_kernel", None)]),
     "moe_h7168_decode64.gate_up": ("moe_h7168_decode64", [("moe_gate_up_nv_kernel", None),
                                                           ("expand_nv16_kernel", 64 * 7168 // 16)]),
-    "moe_h7168_decode64.down": ("moe_h7168_decode64", [("moe_down_nv_kernel", None),
-                                                       ("expand_nv16_kernel", 384 * 3072 // 16)]),
+    "moe_h7168_decode64.down": ("moe_h7168_decode64", [("moe_down_nv_kernel", None)]),
     "moe_h7168_decode64.combine": ("moe_h7168_decode64", [("combine_kernel", None)]),
     # prefill: both fp16 expansions run at the capped grid, so only the tile kernels are attributed
     "moe_h7168_prefill16384.gate_up": ("moe_h7168_prefill16384", [("moe_gate_up_nvw_kernel", None)]),
     "moe_h7168_prefill16384.down": ("moe_h7168_prefill16384", [("moe_down_nvw_kernel", None)]),
     "moe_h7168_prefill16384.combine": ("moe_h7168_prefill16384", [("combine_kernel", None)]),
     "gemm_nv_4096": ("gemm_nv_4096", [("gemm_nv_tile_kernel", None)]),
+    "gemm_w4a8_4096": ("gemm_w4a8_4096", [("gemm_w4a8_256_kernel", None)]),
+    "gemm_quantize_A_mxfp8": ("gemm_quantize_A_mxfp8", [("mxfp8_quantize_kernel", None)]),
 }
 
 
