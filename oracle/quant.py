@@ -368,3 +368,31 @@ def remap_mx_to_nv_exact(codes: np.ndarray, scales: np.ndarray):
             if not exact and any(int(c) & 7 for c in c4[r, b * 32:(b + 1) * 32]):
                 n_inexact += 1
     return out, np.float32(float(Fraction(2) ** k)), n_inexact
+
+
+# ====================================================================== QAT fake quant and STE
+def fake_quant_fp32(fmt: str, xbits: np.ndarray, s_t: float | None = None) -> np.ndarray:
+    """The QAT fake-quantize node [V4-QAT s2.2: quantize-dequantize inserted in
+    the forward pass]: the dequantized values of the quantized tensor, fp32 as
+    `dequant_fp32` defines them.  NV: s_t computed from the tensor unless given."""
+    if fmt == "mx":
+        codes, scales = mx_quantize(xbits)
+        return dequant_fp32("mx", codes, scales)
+    codes, scales, st = nv_quantize(xbits, s_t)
+    return dequant_fp32("nv", codes, scales, st)
+
+
+def fake_quant_bf16_bits(fmt: str, xbits: np.ndarray, s_t: float | None = None) -> np.ndarray:
+    """Same, rounded to bf16 (RNE of the fp32 value), as `dequant_bf16_bits`."""
+    return F.fp32_to_bf16_bits_rne(fake_quant_fp32(fmt, xbits, s_t))
+
+
+def ste_backward(grad: np.ndarray, master: np.ndarray | None = None) -> np.ndarray:
+    """Straight-through estimator [V4-ARCH s6.3: the gradient of the quantized
+    weight goes unchanged to the fp32 master weight]: the incoming gradient
+    (fp32 or bf16 values given as float arrays), added to the existing fp32
+    master gradient when one is given, one fp32 rounding per element."""
+    g = np.asarray(grad, np.float64)
+    if master is None:
+        return F.f64_to_fp32_rne(g)
+    return F.f64_to_fp32_rne(np.asarray(master, np.float64) + g)    # sum of two fp32 is exact in fp64
