@@ -5,7 +5,10 @@ are already resident in HBM:
   quantize  MX and NV quantization of the 4096x4096 weight and the 2048x4096
             activation of the single-linear workload (NV with the tensor scale
             computed, and for the activation also with a calibrated one), the
-            lossless MX->NV remap and an MX dequantize of the weight;
+            lossless MX->NV remap and an MX dequantize of the weight; the QAT
+            fake-quant node (fused quantize -> dequantize, MX and NV) of the
+            weight and its straight-through backward into fp32 master
+            gradients;
   gemm      the 4096^3 W4A4 MXFP4 GEMM (activations quantized on the fly,
             weights pre-quantized, fp32 accumulation, bf16 output), the same
             product in NVFP4, and the W4A8 variant (MXFP8 activations quantized
@@ -165,6 +168,8 @@ def main():
     rem_ts = torch.zeros(1, dtype=torch.float32, device=dev)
     rem_n = torch.zeros(1, dtype=torch.int32, device=dev)
     deq = torch.empty((4096, 4096), dtype=torch.bfloat16, device=dev)
+    fq_out = torch.empty((4096, 4096), dtype=torch.bfloat16, device=dev)
+    masters = rot_copies(torch.zeros((4096, 4096), dtype=torch.float32, device=dev), 4096 * 4096 * 4)
     W2mx_rot = []
     for i in range(nrot2):
         c, s = qbufs(W2, 32)
@@ -215,6 +220,12 @@ def main():
               "remap_max_kernel + remap_kernel"),
         Stage("dequant_mx_W", lambda: F.fp4_dequant(F.FMT_MX, cur(W2mx_rot)[0], cur(W2mx_rot)[1], None, deq), "hbm",
               M2 * (0.5 + 1 / 32 + 2), "2.53125 B/elem (codes + scale in, bf16 out)", "dequant_kernel"),
+        Stage("fake_quant_mx_W", lambda: F.fp4_fake_quant(F.FMT_MX, cur(W2s), fq_out), "hbm", M2 * 4.0,
+              "4 B/elem (2 bf16 in, 2 bf16 out)", "mx_quantize_kernel<true, 1> (bf16 out)"),
+        Stage("fake_quant_nv_W", lambda: F.fp4_fake_quant(F.FMT_NV, cur(W2s), fq_out, tsW, False, nvws), "hbm",
+              M2 * 4.0, "4 B/elem; the tensor-amax read is not counted", "nv_amax_kernel + nv_quantize_kernel<true, 1> (bf16 out)"),
+        Stage("ste_backward_W", lambda: F.fp4_ste_backward(cur(W2s), cur(masters), accumulate=True), "hbm", M2 * 10.0,
+              "10 B/elem (2 bf16 gradient, 4 fp32 master read, 4 written)", "ste_backward_kernel"),
         Stage("gemm_quantize_A", lambda: F.fp4_quantize_mx(cur(A3s), *A3q), "hbm", 4096 * 4096 * MXB,
               "2.53125 B/elem", "mx_quantize_kernel"),
         Stage("gemm_mx_4096", lambda: F.fp4_gemm(F.FMT_MX, A3q[0], A3q[1], W3q[0], W3q[1], C3), "mfma",
@@ -346,7 +357,7 @@ def main():
         comps["gemm_nv_tflops"] = rooflines["gemm_nv_4096"]["achieved"]
         comps["gemm_nv_frac_16bit_peak"] = rooflines["gemm_nv_4096"]["frac"]
     for n in ("quantize_mx_W", "quantize_mx_A", "quantize_nv_W", "quantize_nv_A", "quantize_nv_A_calibrated",
-              "gemm_quantize_A", "gemm_quantize_A_mxfp8"):
+              "gemm_quantize_A", "gemm_quantize_A_mxfp8", "fake_quant_mx_W", "fake_quant_nv_W", "ste_backward_W"):
         if n in rooflines:
             comps[n + "_GBps"] = rooflines[n]["achieved"]
     if "moe_h4096" in rooflines:
@@ -379,6 +390,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": "W4A4 MXFP4 GEMM M=N=K=4096 (bf16 out, fp32 accumulate) for value; per step also "
                                "MX/NV quantize of linear 4096x4096 W and 2048x4096 A, MX->NV remap, MX dequant, "
+                               "MX/NV fake-quant of W and its STE backward, "
                                "NVFP4 and W4A8 (MXFP8 x MXFP4) GEMMs at 4096^3, "
                                "MoE hidden 4096 (384 experts, top-6, inter 2048, 8192 tokens, MXFP4) and "
                                "NVFP4 MoE hidden 7168 (inter 3072) at 64 decode and 16384 prefill tokens",

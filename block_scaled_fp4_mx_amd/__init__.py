@@ -15,7 +15,8 @@ import torch
 __all__ = [
     "lib", "Fp4Error", "FMT_MX", "FMT_NV", "DT_BF16", "DT_F32",
     "fp4_quantize_mx", "fp4_quantize_nv", "fp4_quantize_nv_workspace_bytes", "fp4_remap_mx_to_nv",
-    "fp4_dequant", "fp4_gemm", "fp4_quantize_mxfp8", "fp4_mx_to_mxfp8", "fp4_gemm_w4a8", "fp4_moe_grouped_gemm", "fp4_moe_workspace_bytes", "MoeDebug",
+    "fp4_dequant", "fp4_gemm", "fp4_quantize_mxfp8", "fp4_mx_to_mxfp8", "fp4_gemm_w4a8", "fp4_fake_quant",
+    "fp4_ste_backward", "fp4_moe_grouped_gemm", "fp4_moe_workspace_bytes", "MoeDebug",
     "fp4_abi_version", "LIB_PATH",
 ]
 
@@ -44,6 +45,8 @@ _SIGS = {
     "fp4_remap_mx_to_nv": (_i32, [_vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp]),
     "fp4_dequant": (_i32, [_i32, _vp, _vp, _vp, _i64, _i64, _vp, _i32, _i64, _vp]),
     "fp4_gemm": (_i32, [_i32, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _i32, _i64, _vp]),
+    "fp4_fake_quant": (_i32, [_i32, _vp, _i64, _i64, _i64, _vp, _i32, _i64, _vp, _i32, _vp, _sz, _vp]),
+    "fp4_ste_backward": (_i32, [_vp, _i32, _i64, _i64, _i64, _vp, _i64, _i32, _vp]),
     "fp4_quantize_mxfp8": (_i32, [_vp, _i64, _i64, _i64, _vp, _vp, _vp]),
     "fp4_mx_to_mxfp8": (_i32, [_vp, _i64, _i64, _vp, _vp]),
     "fp4_gemm_w4a8": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _i32, _i64, _vp]),
@@ -144,6 +147,30 @@ def fp4_gemm(fmt, a_codes, a_scales, b_codes, b_scales, c, a_tensor_scale=None, 
     _check("fp4_gemm", lib.fp4_gemm(fmt, _ptr(a_codes), _ptr(a_scales), _ptr(a_tensor_scale), _ptr(b_codes),
                                     _ptr(b_scales), _ptr(b_tensor_scale), m, n, k, _ptr(c), dt, ldc,
                                     _stream(stream)))
+
+
+def fp4_fake_quant(fmt, x, out, tensor_scale=None, tensor_scale_is_input=False, workspace=None, rows=None, k=None,
+                   ld_x=None, ld_out=None, stream=None):
+    rows = x.shape[0] if rows is None else rows
+    k = x.shape[1] if k is None else k
+    ld_x = x.stride(0) if ld_x is None else ld_x
+    ld_out = out.stride(0) if ld_out is None else ld_out
+    dt = DT_F32 if out.dtype == torch.float32 else DT_BF16
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("fp4_fake_quant", lib.fp4_fake_quant(fmt, _ptr(x), rows, k, ld_x, _ptr(out), dt, ld_out, _ptr(tensor_scale),
+                                                int(bool(tensor_scale_is_input)), _ptr(workspace), wsb,
+                                                _stream(stream)))
+
+
+def fp4_ste_backward(grad, grad_master, accumulate=True, rows=None, k=None, ld_grad=None, ld_master=None,
+                     stream=None):
+    rows = grad.shape[0] if rows is None else rows
+    k = grad.shape[1] if k is None else k
+    ld_grad = grad.stride(0) if ld_grad is None else ld_grad
+    ld_master = grad_master.stride(0) if ld_master is None else ld_master
+    dt = DT_F32 if grad.dtype == torch.float32 else DT_BF16
+    _check("fp4_ste_backward", lib.fp4_ste_backward(_ptr(grad), dt, rows, k, ld_grad, _ptr(grad_master), ld_master,
+                                                    int(bool(accumulate)), _stream(stream)))
 
 
 def fp4_quantize_mxfp8(x, codes8, scales, rows=None, k=None, ld_x=None, stream=None):

@@ -181,6 +181,56 @@ int fp4_gemm(fp4_format fmt, const uint8_t* a_codes, const uint8_t* a_scales, co
     return hip_status(e, "fp4_gemm launch");
 }
 
+int fp4_fake_quant(fp4_format fmt, const void* x_bf16, int64_t rows, int64_t k, int64_t ld_x, void* out,
+                   fp4_dtype out_dtype, int64_t ld_out, float* tensor_scale, int tensor_scale_is_input, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+    FP4_REQUIRE(fmt == FP4_FMT_MX || fmt == FP4_FMT_NV, FP4_ERR_INVALID, "bad format %d", (int)fmt);
+    FP4_REQUIRE(out_dtype == FP4_DT_BF16 || out_dtype == FP4_DT_F32, FP4_ERR_INVALID, "bad dtype %d", (int)out_dtype);
+    FP4_REQUIRE(rows >= 0 && k >= 0, FP4_ERR_INVALID, "negative size rows=%lld k=%lld", (long long)rows, (long long)k);
+    const int blk = fmt == FP4_FMT_MX ? 32 : 16;
+    FP4_REQUIRE(k % blk == 0, FP4_ERR_SHAPE, "k=%lld is not a multiple of %d", (long long)k, blk);
+    if (rows == 0 || k == 0) return ok();
+    FP4_PTR(x_bf16);
+    FP4_PTR(out);
+    if (int e = check_ld(ld_x, k, "ld_x")) return e;
+    if (int e = check_ld(ld_out, k, "ld_out")) return e;
+    {
+        const uintptr_t xb = reinterpret_cast<uintptr_t>(x_bf16), ob = reinterpret_cast<uintptr_t>(out);
+        const uintptr_t xe = xb + (uintptr_t)(((rows - 1) * ld_x + k) * 2);
+        const uintptr_t oe = ob + (uintptr_t)(((rows - 1) * ld_out + k) * (out_dtype == FP4_DT_F32 ? 4 : 2));
+        const bool overlap = xb < oe && ob < xe;
+        const bool in_place = xb == ob && ld_x == ld_out && out_dtype == FP4_DT_BF16;
+        FP4_REQUIRE(!overlap || in_place, FP4_ERR_INVALID, "out overlaps x without being x itself");
+    }
+    if (fmt == FP4_FMT_NV) {
+        FP4_SCALAR_PTR(tensor_scale);
+        if (!tensor_scale_is_input) {
+            FP4_REQUIRE(workspace != nullptr && workspace_bytes >= nv_ws_bytes(), FP4_ERR_WORKSPACE,
+                        "workspace needs %zu bytes, got %zu", nv_ws_bytes(), workspace ? workspace_bytes : (size_t)0);
+            FP4_REQUIRE(aligned16(workspace), FP4_ERR_ALIGN, "workspace is not 16-byte aligned");
+        }
+    }
+    return hip_status(fp4::launch_fake_quant(fmt, static_cast<const uint16_t*>(x_bf16), rows, k, ld_x, out,
+                                             out_dtype == FP4_DT_F32, ld_out, tensor_scale, tensor_scale_is_input != 0,
+                                             static_cast<uint32_t*>(workspace), static_cast<hipStream_t>(stream)),
+                      "fp4_fake_quant launch");
+}
+
+int fp4_ste_backward(const void* grad, fp4_dtype grad_dtype, int64_t rows, int64_t k, int64_t ld_grad,
+                     float* grad_master, int64_t ld_master, int accumulate, void* stream) {
+    FP4_REQUIRE(grad_dtype == FP4_DT_BF16 || grad_dtype == FP4_DT_F32, FP4_ERR_INVALID, "bad dtype %d", (int)grad_dtype);
+    FP4_REQUIRE(rows >= 0 && k >= 0, FP4_ERR_INVALID, "negative size rows=%lld k=%lld", (long long)rows, (long long)k);
+    FP4_REQUIRE(k % 8 == 0, FP4_ERR_SHAPE, "k=%lld is not a multiple of 8", (long long)k);
+    if (rows == 0 || k == 0) return ok();
+    FP4_PTR(grad);
+    FP4_PTR(grad_master);
+    if (int e = check_ld(ld_grad, k, "ld_grad")) return e;
+    if (int e = check_ld(ld_master, k, "ld_master")) return e;
+    return hip_status(fp4::launch_ste_backward(grad, grad_dtype == FP4_DT_F32, rows, k, ld_grad, grad_master, ld_master,
+                                               accumulate, static_cast<hipStream_t>(stream)),
+                      "fp4_ste_backward launch");
+}
+
 int fp4_quantize_mxfp8(const void* x_bf16, int64_t rows, int64_t k, int64_t ld_x, uint8_t* codes8, uint8_t* scales,
                        void* stream) {
     FP4_REQUIRE(rows >= 0 && k >= 0, FP4_ERR_INVALID, "negative size rows=%lld k=%lld", (long long)rows, (long long)k);

@@ -82,6 +82,11 @@ hipError_t launch_mx_to_mxfp8(const uint8_t* codes, int64_t rows, int64_t k, uin
 hipError_t launch_quantize_nv(const uint16_t* x, int64_t rows, int64_t k, int64_t ldx,
                               uint8_t* codes, uint8_t* scales, float* tensor_scale,
                               bool ts_is_input, uint32_t* amax_ws, hipStream_t s);
+hipError_t launch_fake_quant(int fmt, const uint16_t* x, int64_t rows, int64_t k, int64_t ldx, void* out,
+                             int out_f32, int64_t ld_out, float* tensor_scale, bool ts_is_input, uint32_t* amax_ws,
+                             hipStream_t s);
+hipError_t launch_ste_backward(const void* g, int g_f32, int64_t rows, int64_t k, int64_t ldg, float* gm, int64_t ldm,
+                               int accumulate, hipStream_t s);
 hipError_t launch_remap(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t k,
                         uint8_t* scales_nv, float* tensor_scale, int32_t* n_inexact, hipStream_t s);
 hipError_t launch_dequant(int fmt, const uint8_t* codes, const uint8_t* scales, const float* ts,

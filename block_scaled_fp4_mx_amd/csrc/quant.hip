@@ -29,13 +29,69 @@ __device__ __forceinline__ int64_t x_offset(int64_t u, int64_t upr, int64_t ldx)
     return r * ldx + (u - r * upr) * 8;
 }
 
+// Output of the fused quantize -> dequantize (fake-quant) mode of the quantize
+// kernels: kOutCodes writes codes and scales; kOutBf16 / kOutF32 write the
+// dequantized values instead (row pitch ld_out elements).
+constexpr int kOutCodes = 0, kOutBf16 = 1, kOutF32 = 2;
+
+// Element offset of unit u (n consecutive elements; upr units per row).
+template <bool kContig>
+__device__ __forceinline__ int64_t unit_offset(int64_t u, int64_t upr, int64_t n, int64_t ld) {
+    if (kContig) return u * n;
+    const int64_t r = u / upr;
+    return r * ld + (u - r * upr) * n;
+}
+
+// Stores n (8 or 16) fp32 values as bf16 (RNE) or fp32.
+template <int kOut, int n>
+__device__ __forceinline__ void store_values(void* out, int64_t o, const float* f) {
+    if (kOut == kOutF32) {
+        float4* p = reinterpret_cast<float4*>(static_cast<float*>(out) + o);
+#pragma unroll
+        for (int i = 0; i < n / 4; ++i) p[i] = make_float4(f[4 * i], f[4 * i + 1], f[4 * i + 2], f[4 * i + 3]);
+    } else {
+        uint4* p = reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + o);
+#pragma unroll
+        for (int i = 0; i < n / 8; ++i) {
+            uint4 q;
+            q.x = f32_to_bf16_rne(f[8 * i + 0]) | (f32_to_bf16_rne(f[8 * i + 1]) << 16);
+            q.y = f32_to_bf16_rne(f[8 * i + 2]) | (f32_to_bf16_rne(f[8 * i + 3]) << 16);
+            q.z = f32_to_bf16_rne(f[8 * i + 4]) | (f32_to_bf16_rne(f[8 * i + 5]) << 16);
+            q.w = f32_to_bf16_rne(f[8 * i + 6]) | (f32_to_bf16_rne(f[8 * i + 7]) << 16);
+            p[i] = q;
+        }
+    }
+}
+
+// Dequantized values of 8 packed codes with scale sc (and, for NV, tensor scale
+// st): MAG * sc is exact (at most 6 significant bits); NV rounds once more by
+// the multiply with st, as the dequantizer does.
+template <bool kNV>
+__device__ __forceinline__ void dequant8(uint32_t c, float sc, float st, float* f) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t code = (c >> (4 * i)) & 0xFu;
+        float val = __fmul_rn(e2m1_mag(code & 7u), sc);
+        if (kNV) val = __fmul_rn(val, st);
+        f[i] = (code & 8u) ? -val : val;
+    }
+}
+
+// 2^(b - 127) for a UE8M0 byte; b == 0 is the fp32 subnormal 2^-127.
+__device__ __forceinline__ float ue8m0_value(uint32_t b) {
+    return b ? __uint_as_float(b << 23) : __uint_as_float(0x00400000u);
+}
+
 // ------------------------------------------------------------------ MX quantize
 // Lane u owns elements 8u..8u+7 of the row-major [rows, k] input (codes word u,
-// scale byte u/4).  Each lane issues kMxUnroll loads before converting.
-template <bool kContig>
+// scale byte u/4).  Each lane issues kMxUnroll loads before converting.  With
+// kOut != kOutCodes the lane writes its 8 dequantized values to out instead
+// (fake-quant); kContig then also means ld_out == k.  x and out may be the same
+// buffer: every lane reads its elements before it writes them.
+template <bool kContig, int kOut = kOutCodes>
 __global__ __launch_bounds__(kThreads) void mx_quantize_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t k, int64_t ldx,
-    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, void* out = nullptr, int64_t ld_out = 0) {
     const int64_t upr = k >> 3;
     const int64_t total = rows * upr;
     const int64_t step = (int64_t)gridDim.x * kThreads * kMxUnroll;
@@ -53,8 +109,14 @@ __global__ __launch_bounds__(kThreads) void mx_quantize_kernel(
                 const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
                 uint32_t sbyte;
                 const uint32_t packed = mx_quant8(w, sbyte);
-                reinterpret_cast<uint32_t*>(codes)[u] = packed;
-                if ((threadIdx.x & 3) == 0) scales[u >> 2] = (uint8_t)sbyte;
+                if (kOut == kOutCodes) {
+                    reinterpret_cast<uint32_t*>(codes)[u] = packed;
+                    if ((threadIdx.x & 3) == 0) scales[u >> 2] = (uint8_t)sbyte;
+                } else {
+                    float f[8];
+                    dequant8<false>(packed, ue8m0_value(sbyte), 1.0f, f);
+                    store_values<kOut, 8>(out, unit_offset<kContig>(u, upr, 8, ld_out), f);
+                }
             }
         }
     }
@@ -161,11 +223,16 @@ __device__ __forceinline__ void nv_load16(const uint16_t* __restrict__ x, int64_
 // rows): 8 code bytes and one scale byte each.  The loads of the next two
 // groups are in flight while one is converted.  npart > 0: s_t comes from the
 // pass-1 partial maxima (and is stored by workgroup 0); npart == 0: s_t is read
-// from *ts.
-template <bool kContig>
+// from *ts.  With kOut != kOutCodes the lane writes its 16 dequantized values
+// (fp32 RNE(MAG * s_g * s_t), or that rounded to bf16) instead of codes and
+// scales; kContig then also means ld_out == k.  x and out may be the same
+// buffer: a group's loads are issued before its values are stored, and the
+// groups in flight are the lane's own.
+template <bool kContig, int kOut = kOutCodes>
 __global__ __launch_bounds__(kThreads) void nv_quantize_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t k, int64_t ldx, uint8_t* __restrict__ codes,
-    uint8_t* __restrict__ scales, float* __restrict__ ts, const uint32_t* __restrict__ part, int npart) {
+    uint8_t* __restrict__ scales, float* __restrict__ ts, const uint32_t* __restrict__ part, int npart,
+    void* out = nullptr, int64_t ld_out = 0) {
     __shared__ NvRecip rtab[128];
     __shared__ uint32_t red[kThreads / 64];
     __shared__ float st_sh;
@@ -220,8 +287,16 @@ __global__ __launch_bounds__(kThreads) void nv_quantize_kernel(
                 if (un < total) nv_load16<kContig>(x, un, gpr, ldx, va[j], vb[j]);
                 const uint32_t sg = nv_group_scale(amax16_bits(w), inv6st32, inv6st, fast);
                 const uint2 c = nv_codes16(w, sg, st, rtab[sg]);
-                *reinterpret_cast<uint2*>(codes + uj * 8) = c;
-                scales[uj] = (uint8_t)sg;
+                if (kOut == kOutCodes) {
+                    *reinterpret_cast<uint2*>(codes + uj * 8) = c;
+                    scales[uj] = (uint8_t)sg;
+                } else {
+                    float f[16];
+                    const float sc = e4m3_value(sg), st32 = st_sh;
+                    dequant8<true>(c.x, sc, st32, f);
+                    dequant8<true>(c.y, sc, st32, f + 8);
+                    store_values<kOut, 16>(out, unit_offset<kContig>(uj, gpr, 16, ld_out), f);
+                }
             }
         }
     }
@@ -273,6 +348,43 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(
             q.w = f32_to_bf16_rne(f[6]) | (f32_to_bf16_rne(f[7]) << 16);
             *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + o) = q;
         }
+    }
+}
+
+// ------------------------------------------------------------------ STE backward
+// Straight-through gradient of the fake-quant node into fp32 master-weight
+// gradients: g_master = (accumulate ? g_master : 0) + g, one fp32 add (RNE) per
+// element.  Lane u owns 8 consecutive elements of a row.
+template <bool kGradF32>
+__global__ __launch_bounds__(kThreads) void ste_backward_kernel(const void* __restrict__ g, int64_t rows, int64_t k,
+                                                               int64_t ldg, float* __restrict__ gm, int64_t ldm,
+                                                               int accumulate) {
+    const int64_t upr = k >> 3;
+    const int64_t total = rows * upr;
+    for (int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x; u < total; u += (int64_t)gridDim.x * kThreads) {
+        const int64_t r = u / upr, c = (u - r * upr) * 8;
+        float gv[8];
+        if (kGradF32) {
+            const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(g) + r * ldg + c);
+            const float4 a = p[0], b = p[1];
+            gv[0] = a.x; gv[1] = a.y; gv[2] = a.z; gv[3] = a.w; gv[4] = b.x; gv[5] = b.y; gv[6] = b.z; gv[7] = b.w;
+        } else {
+            const uint4 q = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(g) + r * ldg + c);
+            const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                gv[2 * i] = bf16_lo(w[i]);
+                gv[2 * i + 1] = bf16_hi(w[i]);
+            }
+        }
+        float4* m = reinterpret_cast<float4*>(gm + r * ldm + c);
+        float4 m0 = make_float4(0.f, 0.f, 0.f, 0.f), m1 = m0;
+        if (accumulate) {
+            m0 = m[0];
+            m1 = m[1];
+        }
+        m[0] = make_float4(__fadd_rn(m0.x, gv[0]), __fadd_rn(m0.y, gv[1]), __fadd_rn(m0.z, gv[2]), __fadd_rn(m0.w, gv[3]));
+        m[1] = make_float4(__fadd_rn(m1.x, gv[4]), __fadd_rn(m1.y, gv[5]), __fadd_rn(m1.z, gv[6]), __fadd_rn(m1.w, gv[7]));
     }
 }
 
@@ -375,26 +487,68 @@ hipError_t launch_mx_to_mxfp8(const uint8_t* codes, int64_t rows, int64_t k, uin
     return hipGetLastError();
 }
 
+// Pass 1 of an NV quantize with a computed tensor scale; returns the number of
+// partial maxima written.
+static int launch_nv_amax(const uint16_t* x, int64_t rows, int64_t k, int64_t ldx, uint32_t* amax_ws, hipStream_t s) {
+    unsigned g = grid_for(rows * (k / 8), kUnroll);
+    if (g > (unsigned)kNvAmaxBlocks) g = kNvAmaxBlocks;
+    if (ldx == k)
+        nv_amax_kernel<true><<<g, kThreads, 0, s>>>(x, rows, k, ldx, amax_ws);
+    else
+        nv_amax_kernel<false><<<g, kThreads, 0, s>>>(x, rows, k, ldx, amax_ws);
+    return (int)g;
+}
+
 hipError_t launch_quantize_nv(const uint16_t* x, int64_t rows, int64_t k, int64_t ldx,
                               uint8_t* codes, uint8_t* scales, float* ts, bool ts_is_input,
                               uint32_t* amax_ws, hipStream_t s) {
     const bool contig = ldx == k;
-    int npart = 0;
-    if (!ts_is_input) {
-        unsigned g = grid_for(rows * (k / 8), kUnroll);
-        if (g > (unsigned)kNvAmaxBlocks) g = kNvAmaxBlocks;
-        npart = (int)g;
-        if (contig)
-            nv_amax_kernel<true><<<g, kThreads, 0, s>>>(x, rows, k, ldx, amax_ws);
-        else
-            nv_amax_kernel<false><<<g, kThreads, 0, s>>>(x, rows, k, ldx, amax_ws);
-    }
+    const int npart = ts_is_input ? 0 : launch_nv_amax(x, rows, k, ldx, amax_ws, s);
     unsigned gq = grid_for(rows * (k / 16));
     if (gq > kNvMaxBlocks) gq = kNvMaxBlocks;
     if (contig)
         nv_quantize_kernel<true><<<gq, kThreads, 0, s>>>(x, rows, k, ldx, codes, scales, ts, amax_ws, npart);
     else
         nv_quantize_kernel<false><<<gq, kThreads, 0, s>>>(x, rows, k, ldx, codes, scales, ts, amax_ws, npart);
+    return hipGetLastError();
+}
+
+hipError_t launch_fake_quant(int fmt, const uint16_t* x, int64_t rows, int64_t k, int64_t ldx, void* out,
+                             int out_f32, int64_t ld_out, float* tensor_scale, bool ts_is_input, uint32_t* amax_ws,
+                             hipStream_t s) {
+    const bool contig = ldx == k && ld_out == k;
+    if (fmt == FP4_FMT_MX) {
+        unsigned g = grid_for(rows * (k / 8), kMxUnroll);
+        if (g > kMxMaxBlocks) g = kMxMaxBlocks;
+#define FQ_MX(C, O) mx_quantize_kernel<C, O><<<g, kThreads, 0, s>>>(x, rows, k, ldx, nullptr, nullptr, out, ld_out)
+        if (contig)
+            out_f32 ? FQ_MX(true, kOutF32) : FQ_MX(true, kOutBf16);
+        else
+            out_f32 ? FQ_MX(false, kOutF32) : FQ_MX(false, kOutBf16);
+#undef FQ_MX
+        return hipGetLastError();
+    }
+    const int npart = ts_is_input ? 0 : launch_nv_amax(x, rows, k, ldx, amax_ws, s);
+    unsigned g = grid_for(rows * (k / 16));
+    if (g > kNvMaxBlocks) g = kNvMaxBlocks;
+#define FQ_NV(C, O) \
+    nv_quantize_kernel<C, O><<<g, kThreads, 0, s>>>(x, rows, k, ldx, nullptr, nullptr, tensor_scale, amax_ws, npart, out, ld_out)
+    if (contig)
+        out_f32 ? FQ_NV(true, kOutF32) : FQ_NV(true, kOutBf16);
+    else
+        out_f32 ? FQ_NV(false, kOutF32) : FQ_NV(false, kOutBf16);
+#undef FQ_NV
+    return hipGetLastError();
+}
+
+hipError_t launch_ste_backward(const void* g, int g_f32, int64_t rows, int64_t k, int64_t ldg, float* gm, int64_t ldm,
+                               int accumulate, hipStream_t s) {
+    unsigned gr = grid_for(rows * (k / 8));
+    if (gr > kMxMaxBlocks) gr = kMxMaxBlocks;
+    if (g_f32)
+        ste_backward_kernel<true><<<gr, kThreads, 0, s>>>(g, rows, k, ldg, gm, ldm, accumulate);
+    else
+        ste_backward_kernel<false><<<gr, kThreads, 0, s>>>(g, rows, k, ldg, gm, ldm, accumulate);
     return hipGetLastError();
 }
 

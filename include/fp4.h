@@ -149,6 +149,39 @@ int fp4_gemm(fp4_format fmt,
              void* c, fp4_dtype c_dtype, int64_t ldc, void* stream);
 
 /*
+ * Fake quantization for quantization-aware training ("DeepSeek-V4 FP4 QAT"
+ * article, section 2.2: quantize-dequantize nodes on the expert weights in the
+ * training forward pass): out = dequant(quantize(x)) in one pass over x, equal
+ * element for element to fp4_quantize_mx / fp4_quantize_nv followed by
+ * fp4_dequant (same rounding rules, same tensor-scale handling), with no codes
+ * or scales materialized.
+ *   NV: as fp4_quantize_nv, s_t is computed (and written to *tensor_scale; the
+ *   workspace is then required) unless tensor_scale_is_input != 0.  MX:
+ *   tensor_scale and the workspace are ignored (may be NULL).
+ * x_bf16: [rows, ld_x] bf16; out: [rows, ld_out] of out_dtype.  out may be x
+ * itself (in place: same pointer, ld_out == ld_x, bf16 output); any other
+ * overlap of x and out is FP4_ERR_INVALID.
+ * Errors: k % 32 (MX) or k % 16 (NV) != 0 -> FP4_ERR_SHAPE; NV workspace too
+ * small -> FP4_ERR_WORKSPACE.  Inputs must be finite.
+ */
+int fp4_fake_quant(fp4_format fmt, const void* x_bf16, int64_t rows, int64_t k, int64_t ld_x,
+                   void* out, fp4_dtype out_dtype, int64_t ld_out,
+                   float* tensor_scale, int tensor_scale_is_input,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Straight-through-estimator backward of the fake-quant node ("DeepSeek-V4"
+ * architecture article, section 6.3: the gradient of the quantized weight is
+ * handed unchanged to the fp32 master weight):
+ *   grad_master[r, c] = (accumulate ? grad_master[r, c] : 0) + grad[r, c],
+ * one fp32 addition (round to nearest even) per element.
+ * grad: [rows, ld_grad] of grad_dtype (bf16 or fp32); grad_master: fp32
+ * [rows, ld_master].  Errors: k % 8 != 0 -> FP4_ERR_SHAPE.
+ */
+int fp4_ste_backward(const void* grad, fp4_dtype grad_dtype, int64_t rows, int64_t k, int64_t ld_grad,
+                     float* grad_master, int64_t ld_master, int accumulate, void* stream);
+
+/*
  * W4A8: FP4 weights with FP8 activations ("DeepSeek-V4 FP4 QAT" article,
  * section 4.3: the recommended deployment pairing; section 4.2: FP4 expands into
  * FP8 without loss).  Activations use MXFP8: E4M3 elements (OCP FP8 E4M3FN,

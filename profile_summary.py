@@ -49,6 +49,8 @@ ROWS = {
     "gemm_nv_4096": ("gemm_nv_4096", [("gemm_nv_tile_kernel", None)]),
     "gemm_w4a8_4096": ("gemm_w4a8_4096", [("gemm_w4a8_256_kernel", None)]),
     "gemm_quantize_A_mxfp8": ("gemm_quantize_A_mxfp8", [("mxfp8_quantize_kernel", None)]),
+    "fake_quant_mx_W": ("fake_quant_mx_W", [("mx_quantize_kernel<true, 1>", None)]),
+    "ste_backward_W": ("ste_backward_W", [("ste_backward_kernel", None)]),
 }
 
 
