@@ -396,3 +396,18 @@ def ste_backward(grad: np.ndarray, master: np.ndarray | None = None) -> np.ndarr
     if master is None:
         return F.f64_to_fp32_rne(g)
     return F.f64_to_fp32_rne(np.asarray(master, np.float64) + g)    # sum of two fp32 is exact in fp64
+
+
+# ====================================================================== MXFP4 KV cache
+def kv_append_mx(cache_codes: np.ndarray, cache_scales: np.ndarray, xbits: np.ndarray, slots) -> tuple:
+    """The MXFP4 KV cache [V4-QAT s3.3: new tokens' vectors are quantized as they
+    join the cache]: each row of x (one token, d values) is MX-quantized on its
+    own and stored at cache row slots[t]; slots outside [0, capacity) are
+    padding and skipped.  Returns updated copies of (codes, scales)."""
+    codes, scales = cache_codes.copy(), cache_scales.copy()
+    cap = codes.shape[0]
+    qc, qs = mx_quantize(xbits)
+    for t, s in enumerate(np.asarray(slots).tolist()):
+        if 0 <= s < cap:
+            codes[s], scales[s] = qc[t], qs[t]
+    return codes, scales
