@@ -9,6 +9,9 @@ are already resident in HBM:
             fake-quant node (fused quantize -> dequantize, MX and NV) of the
             weight and its straight-through backward into fp32 master
             gradients;
+  kv        MXFP4 KV-cache append of a 16384-token prefill (d = 512) into
+            scattered cache slots, and indexer-style FP4 QK scores of 64
+            queries against 32768 cached keys (fp32 scores);
   gemm      the 4096^3 W4A4 MXFP4 GEMM (activations quantized on the fly,
             weights pre-quantized, fp32 accumulation, bf16 output), the same
             product in NVFP4, and the W4A8 variant (MXFP8 activations quantized
@@ -193,6 +196,26 @@ def main():
 
     A3n, W3n = nv_quantized(A3), nv_quantized(W3)
     del W3
+    # KV cache: prefill append (16384 tokens, d 512) into a permuted slot order,
+    # and scores of 64 query latents against 32768 cached keys
+    KV_T, KV_D, KV_N, KV_Q = 16384, 512, 32768, 64
+    kv_x = rot_copies(W.to_bf16(np.random.default_rng(7).standard_normal((KV_T, KV_D))).to(dev), KV_T * KV_D * 2)
+    kv_slots = torch.from_numpy(np.random.default_rng(8).permutation(KV_N)[:KV_T].astype(np.int32)).to(dev)
+    kv_cc = torch.empty((KV_N, KV_D // 2), dtype=torch.uint8, device=dev)
+    kv_cs = torch.empty((KV_N, KV_D // 32), dtype=torch.uint8, device=dev)
+    keys = W.to_bf16(np.random.default_rng(9).standard_normal((KV_N, KV_D))).to(dev)
+    F.fp4_kv_append_mx(keys, torch.arange(KV_N, dtype=torch.int32, device=dev), kv_cc, kv_cs)
+    n_kv = max(2, int(np.ceil(1.5 * MALL_BYTES / (KV_N * (KV_D // 2 + KV_D // 32)))))
+    kv_caches = [(kv_cc.clone(), kv_cs.clone()) for _ in range(n_kv)]     # contiguous codes, scales
+    kv_q = qbufs(W.to_bf16(np.random.default_rng(10).standard_normal((KV_Q, KV_D))).to(dev), 32)
+    F.fp4_quantize_mx(W.to_bf16(np.random.default_rng(10).standard_normal((KV_Q, KV_D))).to(dev), *kv_q)
+    kv_scores = torch.empty((KV_Q, KV_N), dtype=torch.float32, device=dev)
+    del keys
+
+    def kv_score():
+        cc, cs = cur(kv_caches)
+        F.fp4_gemm(F.FMT_MX, kv_q[0], kv_q[1], cc, cs, kv_scores)
+
     A3q8 = (torch.empty((4096, 4096), dtype=torch.uint8, device=dev),
             torch.empty((4096, 4096 // 32), dtype=torch.uint8, device=dev))
 
@@ -226,6 +249,12 @@ def main():
               M2 * 4.0, "4 B/elem; the tensor-amax read is not counted", "nv_amax_kernel + nv_quantize_kernel<true, 1> (bf16 out)"),
         Stage("ste_backward_W", lambda: F.fp4_ste_backward(cur(W2s), cur(masters), accumulate=True), "hbm", M2 * 10.0,
               "10 B/elem (2 bf16 gradient, 4 fp32 master read, 4 written)", "ste_backward_kernel"),
+        Stage("kv_append_prefill16384", lambda: F.fp4_kv_append_mx(cur(kv_x), kv_slots, kv_cc, kv_cs), "hbm",
+              KV_T * KV_D * MXB + KV_T * 4, "2.53125 B/elem + 4 B slot id per token",
+              "mx_quantize_kernel<true, 3>"),
+        Stage("indexer_scores_64x32768", kv_score, "hbm",
+              KV_N * KV_D * (0.5 + 1 / 32) + KV_Q * KV_D * (0.5 + 1 / 32) + KV_Q * KV_N * 4,
+              "cached key codes + scales (0.53125 B/elem) + query codes + fp32 scores out", "gemm_mx_256_kernel"),
         Stage("gemm_quantize_A", lambda: F.fp4_quantize_mx(cur(A3s), *A3q), "hbm", 4096 * 4096 * MXB,
               "2.53125 B/elem", "mx_quantize_kernel"),
         Stage("gemm_mx_4096", lambda: F.fp4_gemm(F.FMT_MX, A3q[0], A3q[1], W3q[0], W3q[1], C3), "mfma",
@@ -357,7 +386,8 @@ def main():
         comps["gemm_nv_tflops"] = rooflines["gemm_nv_4096"]["achieved"]
         comps["gemm_nv_frac_16bit_peak"] = rooflines["gemm_nv_4096"]["frac"]
     for n in ("quantize_mx_W", "quantize_mx_A", "quantize_nv_W", "quantize_nv_A", "quantize_nv_A_calibrated",
-              "gemm_quantize_A", "gemm_quantize_A_mxfp8", "fake_quant_mx_W", "fake_quant_nv_W", "ste_backward_W"):
+              "gemm_quantize_A", "gemm_quantize_A_mxfp8", "fake_quant_mx_W", "fake_quant_nv_W", "ste_backward_W",
+              "kv_append_prefill16384", "indexer_scores_64x32768"):
         if n in rooflines:
             comps[n + "_GBps"] = rooflines[n]["achieved"]
     if "moe_h4096" in rooflines:
@@ -390,7 +420,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": "W4A4 MXFP4 GEMM M=N=K=4096 (bf16 out, fp32 accumulate) for value; per step also "
                                "MX/NV quantize of linear 4096x4096 W and 2048x4096 A, MX->NV remap, MX dequant, "
-                               "MX/NV fake-quant of W and its STE backward, "
+                               "MX/NV fake-quant of W and its STE backward, MXFP4 KV-cache append (16384 x 512) "
+                               "and FP4 indexer scores (64 x 32768 x 512), "
                                "NVFP4 and W4A8 (MXFP8 x MXFP4) GEMMs at 4096^3, "
                                "MoE hidden 4096 (384 experts, top-6, inter 2048, 8192 tokens, MXFP4) and "
                                "NVFP4 MoE hidden 7168 (inter 3072) at 64 decode and 16384 prefill tokens",

@@ -16,7 +16,7 @@ __all__ = [
     "lib", "Fp4Error", "FMT_MX", "FMT_NV", "DT_BF16", "DT_F32",
     "fp4_quantize_mx", "fp4_quantize_nv", "fp4_quantize_nv_workspace_bytes", "fp4_remap_mx_to_nv",
     "fp4_dequant", "fp4_gemm", "fp4_quantize_mxfp8", "fp4_mx_to_mxfp8", "fp4_gemm_w4a8", "fp4_fake_quant",
-    "fp4_ste_backward", "fp4_moe_grouped_gemm", "fp4_moe_workspace_bytes", "MoeDebug",
+    "fp4_ste_backward", "fp4_kv_append_mx", "fp4_moe_grouped_gemm", "fp4_moe_workspace_bytes", "MoeDebug",
     "fp4_abi_version", "LIB_PATH",
 ]
 
@@ -45,6 +45,7 @@ _SIGS = {
     "fp4_remap_mx_to_nv": (_i32, [_vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp]),
     "fp4_dequant": (_i32, [_i32, _vp, _vp, _vp, _i64, _i64, _vp, _i32, _i64, _vp]),
     "fp4_gemm": (_i32, [_i32, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _i32, _i64, _vp]),
+    "fp4_kv_append_mx": (_i32, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _i64, _vp]),
     "fp4_fake_quant": (_i32, [_i32, _vp, _i64, _i64, _i64, _vp, _i32, _i64, _vp, _i32, _vp, _sz, _vp]),
     "fp4_ste_backward": (_i32, [_vp, _i32, _i64, _i64, _i64, _vp, _i64, _i32, _vp]),
     "fp4_quantize_mxfp8": (_i32, [_vp, _i64, _i64, _i64, _vp, _vp, _vp]),
@@ -147,6 +148,14 @@ def fp4_gemm(fmt, a_codes, a_scales, b_codes, b_scales, c, a_tensor_scale=None, 
     _check("fp4_gemm", lib.fp4_gemm(fmt, _ptr(a_codes), _ptr(a_scales), _ptr(a_tensor_scale), _ptr(b_codes),
                                     _ptr(b_scales), _ptr(b_tensor_scale), m, n, k, _ptr(c), dt, ldc,
                                     _stream(stream)))
+
+
+def fp4_kv_append_mx(x, slots, cache_codes, cache_scales, tokens=None, d=None, ld_x=None, stream=None):
+    tokens = x.shape[0] if tokens is None else tokens
+    d = x.shape[1] if d is None else d
+    ld_x = x.stride(0) if ld_x is None else ld_x
+    _check("fp4_kv_append_mx", lib.fp4_kv_append_mx(_ptr(x), tokens, d, ld_x, _ptr(slots), _ptr(cache_codes),
+                                                    _ptr(cache_scales), cache_codes.shape[0], _stream(stream)))
 
 
 def fp4_fake_quant(fmt, x, out, tensor_scale=None, tensor_scale_is_input=False, workspace=None, rows=None, k=None,

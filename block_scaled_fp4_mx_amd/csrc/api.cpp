@@ -181,6 +181,22 @@ int fp4_gemm(fp4_format fmt, const uint8_t* a_codes, const uint8_t* a_scales, co
     return hip_status(e, "fp4_gemm launch");
 }
 
+int fp4_kv_append_mx(const void* x_bf16, int64_t tokens, int64_t d, int64_t ld_x, const int32_t* slots,
+                     uint8_t* cache_codes, uint8_t* cache_scales, int64_t capacity, void* stream) {
+    FP4_REQUIRE(tokens >= 0 && d >= 0 && capacity >= 0, FP4_ERR_INVALID, "negative size tokens=%lld d=%lld capacity=%lld",
+                (long long)tokens, (long long)d, (long long)capacity);
+    FP4_REQUIRE(d % 32 == 0, FP4_ERR_SHAPE, "d=%lld is not a multiple of 32", (long long)d);
+    if (tokens == 0 || d == 0 || capacity == 0) return ok();
+    FP4_PTR(x_bf16);
+    FP4_SCALAR_PTR(slots);
+    FP4_PTR(cache_codes);
+    FP4_PTR(cache_scales);
+    if (int e = check_ld(ld_x, d, "ld_x")) return e;
+    return hip_status(fp4::launch_kv_append(static_cast<const uint16_t*>(x_bf16), tokens, d, ld_x, slots, cache_codes,
+                                            cache_scales, capacity, static_cast<hipStream_t>(stream)),
+                      "fp4_kv_append_mx launch");
+}
+
 int fp4_fake_quant(fp4_format fmt, const void* x_bf16, int64_t rows, int64_t k, int64_t ld_x, void* out,
                    fp4_dtype out_dtype, int64_t ld_out, float* tensor_scale, int tensor_scale_is_input, void* workspace,
                    size_t workspace_bytes, void* stream) {

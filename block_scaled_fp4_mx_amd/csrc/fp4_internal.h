@@ -82,6 +82,8 @@ hipError_t launch_mx_to_mxfp8(const uint8_t* codes, int64_t rows, int64_t k, uin
 hipError_t launch_quantize_nv(const uint16_t* x, int64_t rows, int64_t k, int64_t ldx,
                               uint8_t* codes, uint8_t* scales, float* tensor_scale,
                               bool ts_is_input, uint32_t* amax_ws, hipStream_t s);
+hipError_t launch_kv_append(const uint16_t* x, int64_t tokens, int64_t d, int64_t ldx, const int32_t* slots,
+                            uint8_t* codes, uint8_t* scales, int64_t capacity, hipStream_t s);
 hipError_t launch_fake_quant(int fmt, const uint16_t* x, int64_t rows, int64_t k, int64_t ldx, void* out,
                              int out_f32, int64_t ld_out, float* tensor_scale, bool ts_is_input, uint32_t* amax_ws,
                              hipStream_t s);

@@ -33,6 +33,7 @@ __device__ __forceinline__ int64_t x_offset(int64_t u, int64_t upr, int64_t ldx)
 // kernels: kOutCodes writes codes and scales; kOutBf16 / kOutF32 write the
 // dequantized values instead (row pitch ld_out elements).
 constexpr int kOutCodes = 0, kOutBf16 = 1, kOutF32 = 2;
+constexpr int kOutSlots = 3;   // codes and scales of row r go to row slots[r] (skipped if outside [0, capacity))
 
 // Element offset of unit u (n consecutive elements; upr units per row).
 template <bool kContig>
@@ -91,7 +92,8 @@ __device__ __forceinline__ float ue8m0_value(uint32_t b) {
 template <bool kContig, int kOut = kOutCodes>
 __global__ __launch_bounds__(kThreads) void mx_quantize_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t k, int64_t ldx,
-    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, void* out = nullptr, int64_t ld_out = 0) {
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, void* out = nullptr, int64_t ld_out = 0,
+    const int32_t* __restrict__ slots = nullptr, int64_t capacity = 0) {
     const int64_t upr = k >> 3;
     const int64_t total = rows * upr;
     const int64_t step = (int64_t)gridDim.x * kThreads * kMxUnroll;
@@ -112,6 +114,14 @@ __global__ __launch_bounds__(kThreads) void mx_quantize_kernel(
                 if (kOut == kOutCodes) {
                     reinterpret_cast<uint32_t*>(codes)[u] = packed;
                     if ((threadIdx.x & 3) == 0) scales[u >> 2] = (uint8_t)sbyte;
+                } else if (kOut == kOutSlots) {
+                    const int64_t r = u / upr;
+                    const int64_t slot = slots[r];
+                    if (slot >= 0 && slot < capacity) {
+                        const int64_t v = slot * upr + (u - r * upr);
+                        reinterpret_cast<uint32_t*>(codes)[v] = packed;
+                        if ((threadIdx.x & 3) == 0) scales[v >> 2] = (uint8_t)sbyte;
+                    }
                 } else {
                     float f[8];
                     dequant8<false>(packed, ue8m0_value(sbyte), 1.0f, f);
@@ -510,6 +520,19 @@ hipError_t launch_quantize_nv(const uint16_t* x, int64_t rows, int64_t k, int64_
         nv_quantize_kernel<true><<<gq, kThreads, 0, s>>>(x, rows, k, ldx, codes, scales, ts, amax_ws, npart);
     else
         nv_quantize_kernel<false><<<gq, kThreads, 0, s>>>(x, rows, k, ldx, codes, scales, ts, amax_ws, npart);
+    return hipGetLastError();
+}
+
+hipError_t launch_kv_append(const uint16_t* x, int64_t tokens, int64_t d, int64_t ldx, const int32_t* slots,
+                            uint8_t* codes, uint8_t* scales, int64_t capacity, hipStream_t s) {
+    unsigned g = grid_for(tokens * (d / 8), kMxUnroll);
+    if (g > kMxMaxBlocks) g = kMxMaxBlocks;
+    if (ldx == d)
+        mx_quantize_kernel<true, kOutSlots><<<g, kThreads, 0, s>>>(x, tokens, d, ldx, codes, scales, nullptr, 0, slots,
+                                                                   capacity);
+    else
+        mx_quantize_kernel<false, kOutSlots><<<g, kThreads, 0, s>>>(x, tokens, d, ldx, codes, scales, nullptr, 0, slots,
+                                                                    capacity);
     return hipGetLastError();
 }
 

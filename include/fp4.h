@@ -149,6 +149,25 @@ int fp4_gemm(fp4_format fmt,
              void* c, fp4_dtype c_dtype, int64_t ldc, void* stream);
 
 /*
+ * MXFP4 KV-cache append ("DeepSeek-V4 FP4 QAT" article, section 3.3: the KV
+ * cache is kept in MXFP4 and each new token's vector is quantized as it joins
+ * the cache; the FP4 QK scores of the attention indexer are then fp4_gemm of
+ * the MXFP4 queries against the cache rows, the "DeepSeek-V4" architecture
+ * article, section 3, lightning indexer).  Each cache row is one token's vector
+ * of d values in the MXFP4 layout above (32-element blocks along d, each with
+ * its own UE8M0 byte), so a row's scales never depend on other tokens.
+ *   For t in [0, tokens): if 0 <= slots[t] < capacity, row t of x is quantized
+ *   exactly as fp4_quantize_mx does and written to cache row slots[t]; tokens
+ *   whose slot is outside that range (padding) are skipped.  The in-range slots
+ *   must be distinct.
+ * x_bf16: [tokens, ld_x] bf16; slots: int32 [tokens] (device); cache_codes:
+ * [capacity, d/2]; cache_scales: [capacity, d/32].
+ * Errors: d % 32 != 0 -> FP4_ERR_SHAPE.  Inputs must be finite.
+ */
+int fp4_kv_append_mx(const void* x_bf16, int64_t tokens, int64_t d, int64_t ld_x, const int32_t* slots,
+                     uint8_t* cache_codes, uint8_t* cache_scales, int64_t capacity, void* stream);
+
+/*
  * Fake quantization for quantization-aware training ("DeepSeek-V4 FP4 QAT"
  * article, section 2.2: quantize-dequantize nodes on the expert weights in the
  * training forward pass): out = dequant(quantize(x)) in one pass over x, equal
