@@ -254,7 +254,8 @@ def main():
               "mx_quantize_kernel<true, 3>"),
         Stage("indexer_scores_64x32768", kv_score, "hbm",
               KV_N * KV_D * (0.5 + 1 / 32) + KV_Q * KV_D * (0.5 + 1 / 32) + KV_Q * KV_N * 4,
-              "cached key codes + scales (0.53125 B/elem) + query codes + fp32 scores out", "gemm_mx_256_kernel"),
+              "cached key codes + scales (0.53125 B/elem) + query codes + fp32 scores out",
+              "gemm_mx_skinny_kernel<4, 1>"),
         Stage("gemm_quantize_A", lambda: F.fp4_quantize_mx(cur(A3s), *A3q), "hbm", 4096 * 4096 * MXB,
               "2.53125 B/elem", "mx_quantize_kernel"),
         Stage("gemm_mx_4096", lambda: F.fp4_gemm(F.FMT_MX, A3q[0], A3q[1], W3q[0], W3q[1], C3), "mfma",

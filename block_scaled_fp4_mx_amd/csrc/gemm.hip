@@ -23,6 +23,8 @@ namespace {
 constexpr int kBM = 128, kBN = 128, kThreads = 256;
 constexpr int kNvGemmTM = 64;   // A rows per NV GEMM tile (wide tile, three stages, A as codes)
 constexpr bool kW8Lag = true;   // W4A8 tile: half the waves run half a step behind
+constexpr int64_t kSkinnyMinN = 4096;   // B rows from which few-row A products use the streaming kernel
+constexpr int kSkinnyKF = 1;            // 16-row B fragments per wave in the streaming kernel
 
 // 16x16 accumulator layout: lane holds rows 4*(lane/16) + r, column lane % 16.
 __device__ __forceinline__ void store_tile(const v4f acc[4][4], void* c, int c_f32, int64_t ldc, int64_t m,
@@ -81,6 +83,121 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
         scale = __fmul_rn(*ats, *bts);
     }
     store_tile(acc, c, c_f32, ldc, m, n, m0, n0, lane, scale);
+}
+
+// MX GEMM for few A rows (m <= 64) and many B rows, e.g. indexer scores of a
+// handful of queries against a long key cache: the work is streaming B once.
+// A workgroup owns 64 B rows (4 waves x one 16-row fragment) and all A rows
+// (NQ fragments of 16).  K runs in chunks of 512 values: the workgroup stages
+// the chunk of A (codes and scales) in LDS once, and each wave reads its A
+// fragments from there, so A crosses L2 once per workgroup rather than once
+// per wave; the wave's B chunks and scales come straight from global memory,
+// issued before the A staging so their latency overlaps it.  Per 128-value
+// step a lane carries one 16-byte B chunk and its scale byte, and issues NQ
+// scaled MFMAs with the B fragment first, so its accumulator values are 4
+// consecutive B rows (output columns) of one A row: one 16-byte (fp32) or
+// 8-byte (bf16) store each.  Rows past m or n are clamped for the loads and
+// never stored.  LDS: A row r's 16-byte chunk c at chunk c ^ (r & 15), so the
+// 16 rows a fragment read touches sit in 16 different bank groups.
+constexpr int kSkChunkK = 512;                      // K values staged per chunk
+constexpr int kSkRowB = kSkChunkK / 2;              // code bytes per staged A row
+template <int NQ, int KF>
+__global__ __launch_bounds__(256) void gemm_mx_skinny_kernel(
+    const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as, const uint8_t* __restrict__ bc,
+    const uint8_t* __restrict__ bs, int64_t m, int64_t n, int64_t k, void* __restrict__ c, int c_f32, int64_t ldc) {
+    __shared__ __align__(16) uint8_t a_lds[NQ * 16 * kSkRowB];
+    __shared__ __align__(16) uint8_t as_lds[NQ * 16 * 16];
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int lr = lane & 15, lk = lane >> 4;
+    const int64_t kb = k / 2, kbl = k / 32;
+    const int64_t n0 = (int64_t)blockIdx.x * (64 * KF) + wave * (16 * KF);
+    const uint8_t* bp[KF];
+    const uint8_t* bsp[KF];
+#pragma unroll
+    for (int f = 0; f < KF; ++f) {
+        const int64_t brow = min(n0 + f * 16 + lr, n - 1);
+        bp[f] = bc + brow * kb + lk * 16;
+        bsp[f] = bs + brow * kbl + lk;
+    }
+    v4f acc[KF][NQ];
+#pragma unroll
+    for (int f = 0; f < KF; ++f)
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) acc[f][i] = v4f{0.f, 0.f, 0.f, 0.f};
+    const int nsteps = (int)(k / 128);
+    for (int s0 = 0; s0 < nsteps; s0 += 4) {
+        const int ns = min(4, nsteps - s0);            // steps in this chunk
+        uint4 bv[KF][4];
+        int sb[KF][4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (q < ns) {
+#pragma unroll
+                for (int f = 0; f < KF; ++f) {
+                    bv[f][q] = *reinterpret_cast<const uint4*>(bp[f] + (s0 + q) * 64);
+                    sb[f][q] = bsp[f][(s0 + q) * 4];
+                }
+            }
+        __syncthreads();                                // the previous chunk's A reads are done
+        // stage A: NQ*16 rows x (ns*64) code bytes and ns*4 scale bytes
+        const int cpr = ns * 4;                         // 16-byte code chunks per row in this chunk
+        for (int e = t; e < NQ * 16 * cpr; e += 256) {
+            const int r = e / cpr, ch = e - r * cpr;
+            const int64_t arow = min((int64_t)r, m - 1);
+            const uint4 v = *reinterpret_cast<const uint4*>(ac + arow * kb + (int64_t)s0 * 64 + ch * 16);
+            *reinterpret_cast<uint4*>(a_lds + r * kSkRowB + ((ch ^ (r & 15)) << 4)) = v;
+        }
+        for (int e = t; e < NQ * 16 * cpr; e += 256) {
+            const int r = e / cpr, b = e - r * cpr;    // scale byte b of the chunk (cpr = ns*4 blocks)
+            const int64_t arow = min((int64_t)r, m - 1);
+            as_lds[r * 16 + b] = as[arow * kbl + (int64_t)s0 * 4 + b];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (q >= ns) break;
+#pragma unroll
+            for (int i = 0; i < NQ; ++i) {
+                const int r = i * 16 + lr, ch = q * 4 + lk;
+                const uint4 av = *reinterpret_cast<const uint4*>(a_lds + r * kSkRowB + ((ch ^ (r & 15)) << 4));
+                const int sa = as_lds[r * 16 + q * 4 + lk];
+                const v8i af = v8i{(int)av.x, (int)av.y, (int)av.z, (int)av.w, 0, 0, 0, 0};
+#pragma unroll
+                for (int f = 0; f < KF; ++f)
+                    acc[f][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        v8i{(int)bv[f][q].x, (int)bv[f][q].y, (int)bv[f][q].z, (int)bv[f][q].w, 0, 0, 0, 0}, af,
+                        acc[f][i], 4, 4, 0, sb[f][q], 0, sa);
+            }
+        }
+    }
+    const int esz = c_f32 ? 4 : 2;
+#pragma unroll
+    for (int f = 0; f < KF; ++f) {
+        const int64_t col = n0 + f * 16 + lk * 4;
+        const bool vec = ((ldc * esz) & (c_f32 ? 15 : 7)) == 0 && col + 4 <= n;
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+            const int64_t row = i * 16 + lr;
+            if (row >= m || col >= n) continue;
+            const v4f v = acc[f][i];
+            if (c_f32) {
+                float* dst = static_cast<float*>(c) + row * ldc + col;
+                if (vec) {
+                    *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+                } else {
+                    for (int e = 0; e < 4 && col + e < n; ++e) dst[e] = v[e];
+                }
+            } else {
+                uint16_t* dst = static_cast<uint16_t*>(c) + row * ldc + col;
+                if (vec) {
+                    *reinterpret_cast<uint2*>(dst) = make_uint2(f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16),
+                                                                f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16));
+                } else {
+                    for (int e = 0; e < 4 && col + e < n; ++e) dst[e] = (uint16_t)f32_to_bf16_rne(v[e]);
+                }
+            }
+        }
+    }
 }
 
 // Tile order: consecutive workgroups go to different XCDs (round robin), so
@@ -326,7 +443,16 @@ hipError_t launch_gemm_mx(const uint8_t* ac, const uint8_t* as, const uint8_t* b
                           hipStream_t s) {
     const int64_t tiles_m = (m + kTileM - 1) / kTileM, tiles_n = (n + kTileN - 1) / kTileN;
     const bool small_ops = m * (k / 2) < (1ll << 31) && n * (k / 2) < (1ll << 31);
-    if (k % 512 == 0 && k > 0 && small_ops && tiles_m * tiles_n >= 64 && tiles_m * tiles_n < (1ll << 31)) {
+    if (m <= 64 && n >= kSkinnyMinN && k % 128 == 0 && k > 0 && (n + 63) / 64 < (1ll << 31)) {
+        constexpr int KF = kSkinnyKF;
+        const unsigned grid = (unsigned)((n + 64 * KF - 1) / (64 * KF));
+        switch ((int)((m + 15) / 16)) {
+#define SKINNY(NQ) \
+    case NQ: gemm_mx_skinny_kernel<NQ, KF><<<grid, 256, 0, s>>>(ac, as, bc, bs, m, n, k, c, c_f32, ldc); break;
+            SKINNY(1) SKINNY(2) SKINNY(3) SKINNY(4)
+#undef SKINNY
+        }
+    } else if (k % 512 == 0 && k > 0 && small_ops && tiles_m * tiles_n >= 64 && tiles_m * tiles_n < (1ll << 31)) {
         gemm_mx_256_kernel<<<(unsigned)(tiles_m * tiles_n), kTileThreads, 0, s>>>(ac, as, bc, bs, m, n, k, c, c_f32, ldc,
                                                                          (int)tiles_m, (int)tiles_n);
     } else {

@@ -17,7 +17,7 @@ timeout -k 10 900 rocprofv3 --kernel-trace --stats --output-format csv -d "$OUT/
     python3 "$R/bench.py" --steps 5 --warmup 1 --no-cpu-baseline > "$OUT/trace.log" 2>&1
 
 for grp in copy_256MiB gemm_mx_4096 gemm_nv_4096 gemm_w4a8_4096 gemm_quantize_A_mxfp8 quantize_mx_W quantize_nv_W \
-           fake_quant_mx_W ste_backward_W \
+           fake_quant_mx_W ste_backward_W indexer_scores_64x32768 \
            moe_h4096 moe_h7168_decode64 moe_h7168_prefill16384; do
     for ctr in FETCH_SIZE WRITE_SIZE; do
         echo "counter $ctr on $grp"

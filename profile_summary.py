@@ -51,6 +51,7 @@ ROWS = {
     "gemm_quantize_A_mxfp8": ("gemm_quantize_A_mxfp8", [("mxfp8_quantize_kernel", None)]),
     "fake_quant_mx_W": ("fake_quant_mx_W", [("mx_quantize_kernel<true, 1>", None)]),
     "ste_backward_W": ("ste_backward_W", [("ste_backward_kernel", None)]),
+    "indexer_scores_64x32768": ("indexer_scores_64x32768", [("gemm_mx_skinny_kernel", None)]),
 }
 
 

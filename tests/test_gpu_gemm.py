@@ -175,3 +175,24 @@ def test_gemm_nv_4096_sampled():
     ea2 = chunked(Q.nv_quantize, ab, s_t=sa)
     Cref2, S2 = G.gemm_ref("nv", ea2[0], ea2[1], eb[0][cols], eb[1][cols], sa, sb)
     _assert_within(c[:, cols], Cref2, S2)
+
+
+@pytest.mark.parametrize("m,n,k,dtype,pad", [(1, 4096, 128, torch.float32, 0), (5, 4097, 384, torch.float32, 3),
+                                             (64, 8200, 512, torch.bfloat16, 0), (100, 5000, 256, torch.bfloat16, 5),
+                                             (128, 4160, 1024, torch.float32, 0), (33, 6000, 7168, torch.float32, 0)])
+def test_gemm_mx_skinny_streaming(m, n, k, dtype, pad):
+    """At most 128 A rows and at least 4096 B rows (k % 128 == 0): the
+    streaming kernel (one pass over B), ragged m and n, both output types and
+    an output pitch that forces the element-wise stores."""
+    wl = W.random_linear(m * 7 + n + k, m, n, k, outlier_p=0.01)
+    ab, wb = W.bf16_bits(wl.A), W.bf16_bits(wl.W)
+    a = quantize_mx(dev_bf16(ab))
+    b = quantize_mx(dev_bf16(wb))
+    buf = torch.full((m, n + pad), float("nan"), dtype=dtype, device=DEV)
+    c = buf[:, :n]
+    F.fp4_gemm(F.FMT_MX, a[0], a[1], b[0], b[1], c)
+    torch.cuda.synchronize()
+    Cref, S = G.gemm_ref("mx", *Q.mx_quantize(ab), *chunked(Q.mx_quantize, wb))
+    _assert_within(c, Cref, S)
+    if pad:
+        assert torch.isnan(buf[:, n:].float()).all()
