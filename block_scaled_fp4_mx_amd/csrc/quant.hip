@@ -313,50 +313,39 @@ __global__ __launch_bounds__(kThreads) void nv_quantize_kernel(
 }
 
 // ------------------------------------------------------------------ dequant
+// Lane unit u = elements 8u .. 8u + 7 of the row-major input (one code word,
+// one 16-byte bf16 store, so a store instruction writes 1 KiB contiguously).
+// The grid is capped and every lane keeps kDqUnroll units' loads in flight
+// before converting, so the small code and scale loads overlap their latency.
+constexpr int kDqUnroll = 4;
+constexpr unsigned kDqMaxBlocks = 2048;
 template <bool kNV, bool kF32, bool kContig>
 __global__ __launch_bounds__(kThreads) void dequant_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
     const float* __restrict__ ts, int64_t rows, int64_t k, void* __restrict__ out, int64_t ld) {
     const int64_t upr = k >> 3;
     const int64_t total = rows * upr;
-    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    const int64_t step = (int64_t)gridDim.x * kThreads * kDqUnroll;
     const float st = kNV ? *ts : 1.0f;
-    for (int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x; u < total; u += stride) {
-        const uint32_t c = reinterpret_cast<const uint32_t*>(codes)[u];
-        float sc;
-        if (kNV) {
-            sc = e4m3_value(scales[u >> 1]);
-        } else {
-            const uint32_t sb = scales[u >> 2];
-            // 2^(sb - 127); sb == 0 is the fp32 subnormal 2^-127
-            sc = sb ? __uint_as_float(sb << 23) : __uint_as_float(0x00400000u);
-        }
-        float f[8];
+    for (int64_t base = (int64_t)blockIdx.x * kThreads * kDqUnroll + threadIdx.x; base < total; base += step) {
+        uint32_t c[kDqUnroll], sb[kDqUnroll];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t code = (c >> (4 * i)) & 0xFu;
-            float val = __fmul_rn(e2m1_mag(code & 7u), sc);   // exact (<= 6 significant bits)
-            if (kNV) val = __fmul_rn(val, st);                 // the single rounding
-            f[i] = (code & 8u) ? -val : val;
+        for (int j = 0; j < kDqUnroll; ++j) {
+            const int64_t u = base + (int64_t)j * kThreads;
+            if (u < total) {
+                c[j] = reinterpret_cast<const uint32_t*>(codes)[u];
+                sb[j] = scales[kNV ? (u >> 1) : (u >> 2)];
+            }
         }
-        int64_t o;
-        if (kContig) {
-            o = u * 8;
-        } else {
-            const int64_t r = u / upr;
-            o = r * ld + (u - r * upr) * 8;
-        }
-        if (kF32) {
-            float4* p = reinterpret_cast<float4*>(static_cast<float*>(out) + o);
-            p[0] = make_float4(f[0], f[1], f[2], f[3]);
-            p[1] = make_float4(f[4], f[5], f[6], f[7]);
-        } else {
-            uint4 q;
-            q.x = f32_to_bf16_rne(f[0]) | (f32_to_bf16_rne(f[1]) << 16);
-            q.y = f32_to_bf16_rne(f[2]) | (f32_to_bf16_rne(f[3]) << 16);
-            q.z = f32_to_bf16_rne(f[4]) | (f32_to_bf16_rne(f[5]) << 16);
-            q.w = f32_to_bf16_rne(f[6]) | (f32_to_bf16_rne(f[7]) << 16);
-            *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + o) = q;
+#pragma unroll
+        for (int j = 0; j < kDqUnroll; ++j) {
+            const int64_t u = base + (int64_t)j * kThreads;
+            if (u < total) {
+                const float sc = kNV ? e4m3_value(sb[j]) : ue8m0_value(sb[j]);
+                float f[8];
+                dequant8<kNV>(c[j], sc, st, f);
+                store_values<kF32 ? kOutF32 : kOutBf16, 8>(out, unit_offset<kContig>(u, upr, 8, ld), f);
+            }
         }
     }
 }
@@ -410,15 +399,16 @@ __global__ __launch_bounds__(kRemapMaxThreads) void remap_max_kernel(const uint8
     uint32_t m = 0;
     const int64_t n16 = nb >> 4;
     const uint4* s16 = reinterpret_cast<const uint4*>(s);
-    for (int64_t i = threadIdx.x; i < n16; i += 4 * kRemapMaxThreads) {
-        uint4 v[4];
+    constexpr int kDepth = 4;           // 16-byte loads in flight per thread (deeper measured no faster)
+    for (int64_t i = threadIdx.x; i < n16; i += kDepth * kRemapMaxThreads) {
+        uint4 v[kDepth];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < kDepth; ++j) {
             const int64_t q = i + (int64_t)j * kRemapMaxThreads;
             v[j] = q < n16 ? s16[q] : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < kDepth; ++j) {
             const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
 #pragma unroll
             for (int t = 0; t < 4; ++t)
@@ -586,7 +576,8 @@ hipError_t launch_remap(const uint8_t* codes, const uint8_t* scales, int64_t row
 hipError_t launch_dequant(int fmt, const uint8_t* codes, const uint8_t* scales, const float* ts,
                           int64_t rows, int64_t k, void* out, int out_f32, int64_t ld, hipStream_t s) {
     const int64_t units = rows * (k / 8);
-    const unsigned g = grid_for(units);
+    unsigned g = grid_for(units, kDqUnroll);
+    if (g > kDqMaxBlocks) g = kDqMaxBlocks;
     const bool c = ld == k;
     const bool nv = fmt == FP4_FMT_NV;
 #define FP4_DQ(NV, F32, C) dequant_kernel<NV, F32, C><<<g, kThreads, 0, s>>>(codes, scales, ts, rows, k, out, ld)
