@@ -124,3 +124,46 @@ def test_moe_rejections_and_workspace(F):
     assert call(ws_ptr=None) == WORKSPACE
     assert call(fmt=1) == INVALID                   # NV needs tensor scales
     assert call(tokens=0, ws_ptr=None, ws_bytes=0) == OK
+
+
+def test_w4a8_rejections(F):
+    q = F.lib.fp4_quantize_mxfp8
+    assert q(FAKE, 4, 48, 48, FAKE, FAKE, None) == SHAPE            # k % 32
+    assert q(MISALIGNED, 4, 32, 32, FAKE, FAKE, None) == ALIGN
+    assert q(FAKE, 4, 32, 16, FAKE, FAKE, None) == INVALID          # ld_x < k
+    assert q(None, 0, 32, 32, None, None, None) == OK
+    r = F.lib.fp4_mx_to_mxfp8
+    assert r(FAKE, 4, 40, FAKE, None) == SHAPE
+    assert r(None, 4, 32, FAKE, None) == INVALID
+    assert r(None, 0, 32, None, None) == OK
+    g = F.lib.fp4_gemm_w4a8
+    assert g(FAKE, FAKE, FAKE, FAKE, 8, 8, 48, FAKE, 0, 8, None) == SHAPE
+    assert g(FAKE, FAKE, FAKE, FAKE, 8, 8, 64, FAKE, 5, 8, None) == INVALID      # dtype
+    assert g(FAKE, FAKE, FAKE, FAKE, 8, 8, 64, FAKE, 0, 4, None) == INVALID      # ldc < n
+    assert g(FAKE, FAKE, MISALIGNED, FAKE, 8, 8, 64, FAKE, 0, 8, None) == ALIGN
+    assert g(None, None, None, None, 0, 8, 64, None, 0, 8, None) == OK
+
+
+def test_fake_quant_ste_and_kv_rejections(F):
+    fq = F.lib.fp4_fake_quant
+    assert fq(0, FAKE, 4, 48, 48, FAKE + 4096, 0, 48, None, 0, None, 0, None) == SHAPE     # MX k % 32
+    assert fq(1, FAKE, 4, 40, 40, FAKE + 4096, 0, 40, FAKE, 1, None, 0, None) == SHAPE     # NV k % 16
+    assert fq(3, FAKE, 4, 32, 32, FAKE + 4096, 0, 32, None, 0, None, 0, None) == INVALID   # format
+    assert fq(1, FAKE, 4, 32, 32, FAKE + 4096, 0, 32, FAKE, 0, None, 0, None) == WORKSPACE  # computed s_t
+    assert fq(1, FAKE, 4, 32, 32, FAKE + 4096, 0, 32, None, 1, None, 0, None) == INVALID   # NV needs s_t
+    # out overlapping x without being x (same buffer shifted by 16 bytes)
+    assert fq(0, FAKE, 4, 32, 32, FAKE + 16, 0, 32, None, 0, None, 0, None) == INVALID
+    assert b"overlaps" in F.lib.fp4_last_error()
+    assert fq(0, FAKE, 4, 32, 32, FAKE, 1, 32, None, 0, None, 0, None) == INVALID          # in place needs bf16
+    assert fq(0, None, 0, 32, 32, None, 0, 32, None, 0, None, 0, None) == OK
+    st = F.lib.fp4_ste_backward
+    assert st(FAKE, 0, 4, 12, 16, FAKE, 16, 1, None) == SHAPE       # k % 8
+    assert st(FAKE, 7, 4, 16, 16, FAKE, 16, 1, None) == INVALID     # dtype
+    assert st(FAKE, 0, 4, 16, 16, FAKE, 12, 1, None) == INVALID     # ld_master < k
+    assert st(None, 0, 0, 16, 16, None, 16, 1, None) == OK
+    kv = F.lib.fp4_kv_append_mx
+    assert kv(FAKE, 4, 48, 48, FAKE, FAKE, FAKE, 16, None) == SHAPE
+    assert kv(FAKE, 4, 32, 32, None, FAKE, FAKE, 16, None) == INVALID      # slots
+    assert kv(FAKE, 4, 32, 32, FAKE + 2, FAKE, FAKE, 16, None) == ALIGN    # slots need 4-byte alignment
+    assert kv(FAKE, 4, 32, 32, FAKE, FAKE, FAKE, -1, None) == INVALID
+    assert kv(None, 0, 32, 32, None, None, None, 16, None) == OK
