@@ -21,7 +21,7 @@ namespace fp4 {
 namespace {
 
 constexpr int kBM = 128, kBN = 128, kThreads = 256;
-constexpr int kNvGemmTM = 64;   // A rows per NV GEMM tile (wide tile, three stages, A as codes)
+constexpr int kNvGemmTM = 128;  // A rows per NV GEMM tile (wide tile, two stages, A as codes)
 constexpr bool kW8Lag = true;   // W4A8 tile: half the waves run half a step behind
 constexpr int64_t kSkinnyMinN = 4096;   // B rows from which few-row A products use the streaming kernel
 constexpr int kSkinnyKF = 1;            // 16-row B fragments per wave in the streaming kernel
@@ -366,7 +366,7 @@ __global__ __launch_bounds__(kNvThreads, 1) void gemm_nv_tile_kernel(
     const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as, const float* __restrict__ ats,
     const uint8_t* __restrict__ bc, const uint8_t* __restrict__ bs, const float* __restrict__ bts, int64_t m,
     int64_t n, int64_t k, void* __restrict__ c, int c_f32, int64_t ldc, int tiles_m, int tiles_n) {
-    __shared__ __align__(16) NwSmem<kNvGemmTM, 3, true> sm;
+    __shared__ __align__(16) NwSmem<kNvGemmTM, 2, true> sm;
     int tm, tn;
     tile_coords(tiles_m, tiles_n, tm, tn);
     const int64_t m0 = (int64_t)tm * kNvGemmTM, n0 = (int64_t)tn * kNwN;
@@ -378,8 +378,8 @@ __global__ __launch_bounds__(kNvThreads, 1) void gemm_nv_tile_kernel(
     S.as = as;
     S.b = bc;
     S.s = bs;
-    S.acoff = (uint32_t)min(m0 + nw_ac_row(), m - 1) * kb + nw_ac_chunk();
-    S.asoff = (uint32_t)min(m0 + nw_as_row(), m - 1) * kg + nw_s_col();
+    S.acoff = (uint32_t)min(m0 + nw_ac_row<kNvGemmTM>(), m - 1) * kb + nw_ac_chunk();
+    S.asoff = (uint32_t)min(m0 + nw_as_row<kNvGemmTM>(), m - 1) * kg + nw_s_col();
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int brow = nw_b_row(q);
@@ -387,55 +387,63 @@ __global__ __launch_bounds__(kNvThreads, 1) void gemm_nv_tile_kernel(
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) S.soff[j] = (uint32_t)min(n0 + nw_s_row(j), n - 1) * kg + nw_s_col();
-    v4f acc[4][4];
+    constexpr int kMf = kNvGemmTM / 16;
+    v4f acc[kMf][4];
 #pragma unroll
-    for (int mf = 0; mf < 4; ++mf)
+    for (int mf = 0; mf < kMf; ++mf)
 #pragma unroll
         for (int nf = 0; nf < 4; ++nf) acc[mf][nf] = v4f{0.f, 0.f, 0.f, 0.f};
     nw_mainloop_rows(sm, S, (int)(k / kNwK), acc, m - m0);
 
+    // Epilogue through LDS in four passes of 32 rows (unrolled, so each pass
+    // reads only its own accumulator fragments): the pass's accumulators are
+    // written in the output layout, then its rows leave as whole-row 16-byte
+    // pieces.
     const float scale = __fmul_rn(*ats, *bts);
     const int esz = c_f32 ? 4 : 2;
     const int rowb = kNwN * esz + 16;                // padded LDS row pitch (bytes)
-    static_assert(kNvGemmTM * (kNwN * 4 + 16) <= (int)sizeof(sm), "C staging exceeds the tile's LDS");
-    uint8_t* csm = reinterpret_cast<uint8_t*>(&sm);
-    __syncthreads();                                 // the stages are free
-#pragma unroll
-    for (int mf = 0; mf < 4; ++mf)
-#pragma unroll
-        for (int nf = 0; nf < 4; ++nf)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = mf * 16 + lq * 4 + r, col = wave * 64 + nf * 16 + lr;
-                const float v = __fmul_rn(acc[mf][nf][r], scale);
-                if (c_f32)
-                    *reinterpret_cast<float*>(csm + row * rowb + col * 4) = v;
-                else
-                    *reinterpret_cast<uint16_t*>(csm + row * rowb + col * 2) = (uint16_t)f32_to_bf16_rne(v);
-            }
-    __syncthreads();
+    constexpr int kRowsPass = 32;
+    static_assert(kRowsPass * (kNwN * 4 + 16) <= (int)sizeof(sm), "C staging exceeds the tile's LDS");
     const int chunks_row = kNwN * esz / 16;
     const bool vec = ((ldc * esz) & 15) == 0;
-    for (int q = threadIdx.x; q < kNvGemmTM * chunks_row; q += kNvThreads) {
-        const int row = q / chunks_row, ch = q - row * chunks_row;
-        const int64_t grow = m0 + row, gcol = n0 + ch * (16 / esz);
-        if (grow >= m || gcol >= n) continue;
-        const uint4 v = *reinterpret_cast<const uint4*>(csm + row * rowb + ch * 16);
-        uint8_t* dst = static_cast<uint8_t*>(c) + (grow * ldc + gcol) * esz;
-        if (vec && gcol + 16 / esz <= n) {
-            *reinterpret_cast<uint4*>(dst) = v;
-        } else {
-            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-            for (int e = 0; e < 16 / esz && gcol + e < n; ++e) {
-                if (c_f32)
-                    reinterpret_cast<uint32_t*>(dst)[e] = w[e];
-                else
-                    reinterpret_cast<uint16_t*>(dst)[e] = (uint16_t)(w[e >> 1] >> ((e & 1) * 16));
+    uint8_t* csm = reinterpret_cast<uint8_t*>(&sm);
+#pragma unroll
+    for (int pass = 0; pass < kNvGemmTM / kRowsPass; ++pass) {
+        __syncthreads();                             // the stages (or the previous pass) are free
+#pragma unroll
+        for (int mf = pass * (kRowsPass / 16); mf < (pass + 1) * (kRowsPass / 16); ++mf)
+#pragma unroll
+            for (int nf = 0; nf < 4; ++nf)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = mf * 16 + lq * 4 + r - pass * kRowsPass, col = wave * 64 + nf * 16 + lr;
+                    const float v = __fmul_rn(acc[mf][nf][r], scale);
+                    if (c_f32)
+                        *reinterpret_cast<float*>(csm + row * rowb + col * 4) = v;
+                    else
+                        *reinterpret_cast<uint16_t*>(csm + row * rowb + col * 2) = (uint16_t)f32_to_bf16_rne(v);
+                }
+        __syncthreads();
+        for (int q = threadIdx.x; q < kRowsPass * chunks_row; q += kNvThreads) {
+            const int row = q / chunks_row, ch = q - row * chunks_row;
+            const int64_t grow = m0 + pass * kRowsPass + row, gcol = n0 + ch * (16 / esz);
+            if (grow >= m || gcol >= n) continue;
+            const uint4 v = *reinterpret_cast<const uint4*>(csm + row * rowb + ch * 16);
+            uint8_t* dst = static_cast<uint8_t*>(c) + (grow * ldc + gcol) * esz;
+            if (vec && gcol + 16 / esz <= n) {
+                *reinterpret_cast<uint4*>(dst) = v;
+            } else {
+                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+                for (int e = 0; e < 16 / esz && gcol + e < n; ++e) {
+                    if (c_f32)
+                        reinterpret_cast<uint32_t*>(dst)[e] = w[e];
+                    else
+                        reinterpret_cast<uint16_t*>(dst)[e] = (uint16_t)(w[e >> 1] >> ((e & 1) * 16));
+                }
             }
         }
     }
 }
-
 }  // namespace
 
 hipError_t launch_gemm_mx(const uint8_t* ac, const uint8_t* as, const uint8_t* bc, const uint8_t* bs,
@@ -482,7 +490,7 @@ hipError_t launch_gemm_nv(const uint8_t* ac, const uint8_t* as, const float* ats
                           hipStream_t s) {
     const int64_t tiles_m = (m + kNvGemmTM - 1) / kNvGemmTM, tiles_n = (n + kNwN - 1) / kNwN;
     const bool small_ops = m * (k / 2) < (1ll << 31) && n * (k / 2) < (1ll << 31);
-    if (k % kNwK == 0 && k > 0 && small_ops && tiles_m * tiles_n >= 32 && tiles_m * tiles_n < (1ll << 31)) {
+    if (k % kNwK == 0 && k > 0 && small_ops && tiles_m * tiles_n >= 16 && tiles_m * tiles_n < (1ll << 31)) {
         gemm_nv_tile_kernel<<<(unsigned)(tiles_m * tiles_n), kNvThreads, 0, s>>>(
             ac, as, ats, bc, bs, bts, m, n, k, c, c_f32, ldc, (int)tiles_m, (int)tiles_n);
     } else {

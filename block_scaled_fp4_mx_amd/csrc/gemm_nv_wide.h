@@ -51,7 +51,7 @@ struct NwStage {
 };
 template <int TM, int NS, bool ACODES>
 struct NwSmem {
-    static_assert((TM == 64 && NS == 3) || (TM == 128 && NS == 2 && !ACODES), "supported wide-tile configurations");
+    static_assert((TM == 64 && NS == 3) || (TM == 128 && NS == 2), "supported wide-tile configurations");
     NwStage<TM, ACODES> st[NS];
     uint8_t a16[ACODES ? TM * kNwARow : 16];        // expanded A of the current step
 };
@@ -87,21 +87,33 @@ __device__ __forceinline__ uint32_t nw_swz(int row) { return (uint32_t)((row >> 
 __device__ __forceinline__ uint32_t nw_b_chunk(int row) { return ((threadIdx.x & 3u) ^ nw_swz(row)) << 4; }
 __device__ __forceinline__ int nw_s_row(int j) { return 64 * nw_wave() + 32 * j + (int)((threadIdx.x & 63) >> 1); }
 __device__ __forceinline__ uint32_t nw_s_col() { return (threadIdx.x & 1u) << 2; }
-__device__ __forceinline__ int nw_ac_row() { return 16 * (nw_wave() & 3) + (int)((threadIdx.x & 63) >> 2); }
+// A given as codes: TM = 64 copies its codes with waves 0-3 (16 rows each) and
+// its scales with waves 4-5 (32 rows each); TM = 128 with all 8 waves and waves
+// 4-7.
+template <int TM>
+__device__ __forceinline__ int nw_ac_row() {
+    return 16 * (TM == 64 ? (nw_wave() & 3) : nw_wave()) + (int)((threadIdx.x & 63) >> 2);
+}
 __device__ __forceinline__ uint32_t nw_ac_chunk() { return (threadIdx.x & 3u) << 4; }
-__device__ __forceinline__ int nw_as_row() { return 32 * (nw_wave() & 1) + (int)((threadIdx.x & 63) >> 1); }
+template <int TM>
+__device__ __forceinline__ int nw_as_row() {
+    return 32 * (TM == 64 ? (nw_wave() & 1) : (nw_wave() & 3)) + (int)((threadIdx.x & 63) >> 1);
+}
 
 // Copies of K step ks into one stage.  Every wave issues the same copies each
-// step (TM/32 + 6; with A as codes 7 for waves 0-5 and 6 for waves 6-7): the
-// three-stage waits count on it.
+// step (TM/32 + 6; with A as codes and TM = 64, 7 for waves 0-5 and 6 for waves
+// 6-7): the three-stage waits count on it.
 template <int TM, bool ACODES>
 __device__ __forceinline__ void nw_issue(NwStage<TM, ACODES>& st, const NwSrc& S, int ks) {
     const int wave = __builtin_amdgcn_readfirstlane(nw_wave());
-    if constexpr (ACODES) {
+    if constexpr (ACODES && TM == 64) {
         if (wave < 4)
             dma16(S.ac + (int64_t)ks * kNwBRow, S.acoff, lds_addr(st.ac) + wave * 1024);
         else if (wave < 6)
             dma4(S.as + (int64_t)ks * kNwSRow, S.asoff, lds_addr(st.as) + (wave - 4) * 256);
+    } else if constexpr (ACODES) {
+        dma16(S.ac + (int64_t)ks * kNwBRow, S.acoff, lds_addr(st.ac) + wave * 1024);
+        if (wave >= 4) dma4(S.as + (int64_t)ks * kNwSRow, S.asoff, lds_addr(st.as) + (wave - 4) * 256);
     } else {
         const uint8_t* a = S.a + (int64_t)ks * kNwARow;
         const uint32_t la = lds_addr(st.a) + wave * (TM / 32) * 1024;
@@ -133,14 +145,19 @@ __device__ __forceinline__ void nw_wait_current() {
     }
 }
 
-// A given as codes: one 16-group per thread (64 rows x 8 groups) expanded to
-// fp16 into the shared A buffer, in the swizzled layout the fragment reads use.
-__device__ __forceinline__ void nw_expand_a(const NwStage<64, true>& st, uint8_t* a16) {
-    const int row = (int)(threadIdx.x >> 3), g = (int)(threadIdx.x & 7);
-    const uint2 c = *reinterpret_cast<const uint2*>(&st.ac[row * kNwBRow + g * 8]);
-    const _Float16 sg = nv_scale_pair(st.as[row * kNwSRow + g])[0];
-    *reinterpret_cast<h8_t*>(&a16[row * kNwARow + (((2 * g) ^ (row & 15)) << 4)]) = nv_expand8(c.x, sg);
-    *reinterpret_cast<h8_t*>(&a16[row * kNwARow + (((2 * g + 1) ^ (row & 15)) << 4)]) = nv_expand8(c.y, sg);
+// A given as codes: each thread expands one 16-group per 64 rows (TM x 8
+// groups) to fp16 into the shared A buffer, in the swizzled layout the
+// fragment reads use.
+template <int TM>
+__device__ __forceinline__ void nw_expand_a(const NwStage<TM, true>& st, uint8_t* a16) {
+#pragma unroll
+    for (int h = 0; h < TM / 64; ++h) {
+        const int row = h * 64 + (int)(threadIdx.x >> 3), g = (int)(threadIdx.x & 7);
+        const uint2 c = *reinterpret_cast<const uint2*>(&st.ac[row * kNwBRow + g * 8]);
+        const _Float16 sg = nv_scale_pair(st.as[row * kNwSRow + g])[0];
+        *reinterpret_cast<h8_t*>(&a16[row * kNwARow + (((2 * g) ^ (row & 15)) << 4)]) = nv_expand8(c.x, sg);
+        *reinterpret_cast<h8_t*>(&a16[row * kNwARow + (((2 * g + 1) ^ (row & 15)) << 4)]) = nv_expand8(c.y, sg);
+    }
 }
 
 __device__ __forceinline__ uint32_t nw_word(const uint4& c, int i) {
@@ -176,7 +193,7 @@ __device__ __forceinline__ void nw_mainloop(NwSmem<TM, NS, ACODES>& sm, const Nw
         const NwStage<TM, ACODES>& st = sm.st[cur];
         cur = cur + 1 == NS ? 0 : cur + 1;
         if constexpr (ACODES) {
-            nw_expand_a(st, sm.a16);
+            nw_expand_a<TM>(st, sm.a16);
             __syncthreads();
         }
         if (MF == 0) continue;
