@@ -470,7 +470,7 @@ def moe_stage(torch, F, name, fmt, m, E, w13c, w13s, w2c, w2s, w13ts, w2ts, act,
     names = {"quantize_x": "mx_quantize_kernel" if fmt == F.FMT_MX else "nv_quantize_kernel",
              "routing": "route_count_kernel + route_scan_kernel + route_place_kernel",
              "gate_up": "moe_gate_up_mx256_kernel" if fmt == F.FMT_MX else
-             f"expand_nv16_kernel (x) + {nv_gu}",
+             (f"expand_nv16_kernel (x) + {nv_gu}" if T <= 128 else nv_gu),
              "down": "moe_down_mx256_kernel" if fmt == F.FMT_MX else nv_dn,
              "combine": "combine_kernel"}
     if bound == "hbm":

@@ -21,7 +21,6 @@ namespace fp4 {
 namespace {
 
 constexpr int kBM = 128, kBN = 128, kThreads = 256;
-constexpr int kNvGemmTM = 128;  // A rows per NV GEMM tile (wide tile, two stages, A as codes)
 constexpr bool kW8Lag = true;   // W4A8 tile: half the waves run half a step behind
 constexpr int64_t kSkinnyMinN = 4096;   // B rows from which few-row A products use the streaming kernel
 constexpr int kSkinnyKF = 1;            // 16-row B fragments per wave in the streaming kernel
@@ -359,17 +358,17 @@ __global__ __launch_bounds__(kW8Threads, 1) void gemm_w4a8_256_kernel(
     }
 }
 
-// NV GEMM on the wide 64 x 512 tiles (gemm_nv_wide.h): B expanded to fp16 in
-// registers, A expanded into LDS each step, fp16 MFMA, tensor scales in the
-// epilogue; C goes through LDS and leaves in whole-row 16-byte pieces.
+// NV GEMM on the wide 128 x 512 tiles (gemm_nv_wide.h): B expanded to fp16 in
+// registers, A expanded into LDS one step ahead, fp16 MFMA, tensor scales in
+// the epilogue; C goes through LDS and leaves in whole-row 16-byte pieces.
 __global__ __launch_bounds__(kNvThreads, 1) void gemm_nv_tile_kernel(
     const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as, const float* __restrict__ ats,
     const uint8_t* __restrict__ bc, const uint8_t* __restrict__ bs, const float* __restrict__ bts, int64_t m,
     int64_t n, int64_t k, void* __restrict__ c, int c_f32, int64_t ldc, int tiles_m, int tiles_n) {
-    __shared__ __align__(16) NwSmem<kNvGemmTM, 2, true> sm;
+    __shared__ __align__(16) NwSmem sm;
     int tm, tn;
     tile_coords(tiles_m, tiles_n, tm, tn);
-    const int64_t m0 = (int64_t)tm * kNvGemmTM, n0 = (int64_t)tn * kNwN;
+    const int64_t m0 = (int64_t)tm * kNwM, n0 = (int64_t)tn * kNwN;
     const uint32_t kb = (uint32_t)(k / 2), kg = (uint32_t)(k / 16);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int lr = lane & 15, lq = lane >> 4;
@@ -378,8 +377,8 @@ __global__ __launch_bounds__(kNvThreads, 1) void gemm_nv_tile_kernel(
     S.as = as;
     S.b = bc;
     S.s = bs;
-    S.acoff = (uint32_t)min(m0 + nw_ac_row<kNvGemmTM>(), m - 1) * kb + nw_ac_chunk();
-    S.asoff = (uint32_t)min(m0 + nw_as_row<kNvGemmTM>(), m - 1) * kg + nw_s_col();
+    S.acoff = (uint32_t)min(m0 + nw_ac_row(), m - 1) * kb + nw_ac_chunk();
+    S.asoff = (uint32_t)min(m0 + nw_as_row(), m - 1) * kg + nw_s_col();
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int brow = nw_b_row(q);
@@ -387,10 +386,9 @@ __global__ __launch_bounds__(kNvThreads, 1) void gemm_nv_tile_kernel(
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) S.soff[j] = (uint32_t)min(n0 + nw_s_row(j), n - 1) * kg + nw_s_col();
-    constexpr int kMf = kNvGemmTM / 16;
-    v4f acc[kMf][4];
+    v4f acc[kNwMf][4];
 #pragma unroll
-    for (int mf = 0; mf < kMf; ++mf)
+    for (int mf = 0; mf < kNwMf; ++mf)
 #pragma unroll
         for (int nf = 0; nf < 4; ++nf) acc[mf][nf] = v4f{0.f, 0.f, 0.f, 0.f};
     nw_mainloop_rows(sm, S, (int)(k / kNwK), acc, m - m0);
@@ -408,7 +406,7 @@ __global__ __launch_bounds__(kNvThreads, 1) void gemm_nv_tile_kernel(
     const bool vec = ((ldc * esz) & 15) == 0;
     uint8_t* csm = reinterpret_cast<uint8_t*>(&sm);
 #pragma unroll
-    for (int pass = 0; pass < kNvGemmTM / kRowsPass; ++pass) {
+    for (int pass = 0; pass < kNwM / kRowsPass; ++pass) {
         __syncthreads();                             // the stages (or the previous pass) are free
 #pragma unroll
         for (int mf = pass * (kRowsPass / 16); mf < (pass + 1) * (kRowsPass / 16); ++mf)
@@ -488,7 +486,7 @@ hipError_t launch_gemm_nv(const uint8_t* ac, const uint8_t* as, const float* ats
                           const uint8_t* bc, const uint8_t* bs, const float* bts,
                           int64_t m, int64_t n, int64_t k, void* c, int c_f32, int64_t ldc,
                           hipStream_t s) {
-    const int64_t tiles_m = (m + kNvGemmTM - 1) / kNvGemmTM, tiles_n = (n + kNwN - 1) / kNwN;
+    const int64_t tiles_m = (m + kNwM - 1) / kNwM, tiles_n = (n + kNwN - 1) / kNwN;
     const bool small_ops = m * (k / 2) < (1ll << 31) && n * (k / 2) < (1ll << 31);
     if (k % kNwK == 0 && k > 0 && small_ops && tiles_m * tiles_n >= 16 && tiles_m * tiles_n < (1ll << 31)) {
         gemm_nv_tile_kernel<<<(unsigned)(tiles_m * tiles_n), kNvThreads, 0, s>>>(

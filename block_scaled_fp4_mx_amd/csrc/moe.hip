@@ -42,6 +42,7 @@ inline size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
     size_t xc, xs, counts, offsets, blockbase, perm, slot_pos, tile_e, tile_r, ntiles, hc, hs, ybuf, x16, h16, total;
+    bool x16_h16;                      // the fp16 expansions are allocated
     int64_t nblk, max_tiles;
 };
 
@@ -68,7 +69,8 @@ Layout layout(int fmt, int64_t T, int64_t H, int topk, int E, int64_t I) {
     L.hc = take((size_t)S * I / 2);
     L.hs = take((size_t)S * I / blk);
     L.ybuf = take((size_t)S * H * 4);
-    if (fmt == FP4_FMT_NV) {            // fp16 expansions of Q(x) and Q(h) for the NV tiles
+    L.x16_h16 = fmt == FP4_FMT_NV && T <= kNvDecodeTokens;
+    if (L.x16_h16) {                   // fp16 expansions of Q(x) and Q(h) for the decode NV tiles
         L.x16 = take((size_t)T * H * 2);
         L.h16 = take((size_t)S * I * 2);
     }
@@ -280,11 +282,11 @@ struct GemmParams {
     const float *w13ts, *w2ts, *act_ts;
     const int32_t *perm, *offsets, *tile_e, *tile_r, *ntiles;
     const float* weights;              // [S]
-    uint8_t *hc, *hs;                  // MX: quantized h [S, I/2], [S, I/32] in routed order
+    uint8_t *hc, *hs;                  // quantized h [S, I/2], [S, I/blk] in routed order (MX; NV wide tiles)
     float* ybuf;                       // [S, H]: w * y of slot s in row s
-    const uint16_t* x16;               // NV: fp16 code * s_g of Q(x) [T, H]
-    uint16_t* h16;                     // NV: fp16 code * s_g of Q(h) [S, I], written by the gate/up tiles
-    int h16_by_slot;                   // NV: h16 rows are slots (injected Q(h)), else routed positions
+    const uint16_t* x16;               // NV decode tiles: fp16 code * s_g of Q(x) [T, H]
+    uint16_t* h16;                     // NV decode tiles: fp16 code * s_g of Q(h) [S, I], written by gate/up
+    int h16_by_slot;                   // NV decode tiles: h16 rows are slots (injected Q(h)), else routed positions
     fp4_moe_debug dbg;
 };
 
@@ -886,12 +888,11 @@ __global__ __launch_bounds__(kNvThreads, 1) void moe_down_nv_kernel(GemmParams p
 
 // ---------------------------------------------------------------- wide NV tiles
 // Prefill-sized batches: 128 routed rows x 512 weight rows per tile (the wide
-// NV tile, two stages).  gate/up: wave w owns slab rows w*64 .. +63: 32 w1 rows
-// (intermediate columns c0 + w*32 ..) then the 32 w3 rows of the same columns,
-// so fragments 0-1 hold g and fragments 2-3 the matching u.  A tile covers 256
-// intermediate columns.
-constexpr int kNwMoeM = 128;        // routed rows per wide tile
-constexpr int kNwMoeMf = kNwMoeM / 16;
+// NV tile), both operands NVFP4 codes: gate/up gathers the rows of Q(x) of the
+// tile's slots, down reads Q(h) as gate/up wrote it.  gate/up: wave w owns slab
+// rows w*64 .. +63: 32 w1 rows (intermediate columns c0 + w*32 ..) then the 32
+// w3 rows of the same columns, so fragments 0-1 hold g and fragments 2-3 the
+// matching u.  A tile covers 256 intermediate columns.
 constexpr int kNwGuCols = 256;
 
 __device__ __forceinline__ int64_t gu_nw_row(int slab_row, int64_t c0, int64_t I) {
@@ -900,8 +901,8 @@ __device__ __forceinline__ int64_t gu_nw_row(int slab_row, int64_t c0, int64_t I
 }
 
 __global__ __launch_bounds__(kNvThreads, 1) void moe_gate_up_nvw_kernel(GemmParams p) {
-    __shared__ __align__(16) NwSmem<kNwMoeM, 2, false> sm;
-    static_assert(kNwMoeM * kNwGuCols * 2 <= (int)sizeof(sm), "h tile exceeds the wide tile's LDS");
+    __shared__ __align__(16) NwSmem sm;
+    static_assert(kNwM * kNwGuCols * 2 <= (int)sizeof(sm), "h tile exceeds the wide tile's LDS");
     const int tile = blockIdx.y;
     if (tile >= *p.ntiles) return;
     const int e = p.tile_e[tile];
@@ -913,24 +914,24 @@ __global__ __launch_bounds__(kNvThreads, 1) void moe_gate_up_nvw_kernel(GemmPara
     const int lr = lane & 15, lq = lane >> 4;
     const bool injected = p.dbg.gate_up_in != nullptr;
 
-    v4f acc[kNwMoeMf][4];
+    v4f acc[kNwMf][4];
 #pragma unroll
-    for (int mf = 0; mf < kNwMoeMf; ++mf)
+    for (int mf = 0; mf < kNwMf; ++mf)
 #pragma unroll
         for (int nf = 0; nf < 4; ++nf) acc[mf][nf] = v4f{0.f, 0.f, 0.f, 0.f};
 
     if (!injected) {
         NwSrc S{};
-        S.a = reinterpret_cast<const uint8_t*>(p.x16);
+        S.ac = p.xc;
+        S.as = p.xs;
         S.b = p.w13c + (int64_t)e * (2 * I) * (H / 2);
         S.s = p.w13s + (int64_t)e * (2 * I) * (H / 16);
-        const uint32_t apitch = (uint32_t)(H * 2), bpitch = (uint32_t)(H / 2), spitch = (uint32_t)(H / 16);
-#pragma unroll
-        for (int q = 0; q < kNwMoeM / 32; ++q) {
-            const int arow = nw_a_row<kNwMoeM>(q);
-            const int64_t pos = min(r0 + arow, rend - 1);
-            S.aoff[q] = (uint32_t)(p.perm[pos] / p.topk) * apitch + nw_a_chunk(arow);
-        }
+        const uint32_t bpitch = (uint32_t)(H / 2), spitch = (uint32_t)(H / 16);
+        // A rows: the tokens of the tile's slots (rows past the segment repeat its last)
+        const int64_t ctok = p.perm[min(r0 + nw_ac_row(), rend - 1)] / p.topk;
+        const int64_t stok = p.perm[min(r0 + nw_as_row(), rend - 1)] / p.topk;
+        S.acoff = (uint32_t)ctok * bpitch + nw_ac_chunk();
+        S.asoff = (uint32_t)stok * spitch + nw_s_col();
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int brow = nw_b_row(q);
@@ -942,7 +943,7 @@ __global__ __launch_bounds__(kNvThreads, 1) void moe_gate_up_nvw_kernel(GemmPara
     } else {
         // g|u given per slot (debug injection, tensor scales included)
 #pragma unroll
-        for (int mf = 0; mf < kNwMoeMf; ++mf)
+        for (int mf = 0; mf < kNwMf; ++mf)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int64_t pos = r0 + mf * 16 + lq * 4 + r;
@@ -960,7 +961,7 @@ __global__ __launch_bounds__(kNvThreads, 1) void moe_gate_up_nvw_kernel(GemmPara
     const float gscale = injected ? 1.0f : __fmul_rn(p.act_ts[0], p.w13ts[e]);
     uint16_t* hsm = reinterpret_cast<uint16_t*>(&sm);      // 128 rows x 256 bf16
 #pragma unroll
-    for (int mf = 0; mf < kNwMoeMf; ++mf)
+    for (int mf = 0; mf < kNwMf; ++mf)
 #pragma unroll
         for (int nf = 0; nf < 2; ++nf)
 #pragma unroll
@@ -986,7 +987,7 @@ __global__ __launch_bounds__(kNvThreads, 1) void moe_gate_up_nvw_kernel(GemmPara
     // 16-group spans 2 consecutive lanes
     const double st_h = (double)p.act_ts[1];
 #pragma unroll 2
-    for (int q = 0; q < (kNwMoeM * kNwGuCols / 8) / kNvThreads; ++q) {
+    for (int q = 0; q < (kNwM * kNwGuCols / 8) / kNvThreads; ++q) {
         const int unit = threadIdx.x + q * kNvThreads;
         const int rl = unit / (kNwGuCols / 8), cu = unit % (kNwGuCols / 8);
         const int64_t pos = r0 + rl;
@@ -996,9 +997,10 @@ __global__ __launch_bounds__(kNvThreads, 1) void moe_gate_up_nvw_kernel(GemmPara
         uint32_t sb;
         const uint32_t packed = nv_quant8(w, st_h, sb);
         const int64_t col = c0 + cu * 8;
-        // the down tiles read Q(h) as its exact fp16 expansion
-        *reinterpret_cast<h8_t*>(p.h16 + pos * I + col) = nv_expand8(packed, nv_scale_pair(sb)[0]);
         const bool lead = (cu & 1) == 0;
+        // Q(h) in routed order, as the down tiles read it
+        reinterpret_cast<uint32_t*>(p.hc + pos * (I / 2) + col / 2)[0] = packed;
+        if (lead) p.hs[pos * (I / 16) + col / 16] = (uint8_t)sb;
         if (p.dbg.h_codes || p.dbg.h_scales) {
             const int64_t slot = p.perm[pos];
             if (p.dbg.h_codes) reinterpret_cast<uint32_t*>(p.dbg.h_codes + slot * (I / 2) + col / 2)[0] = packed;
@@ -1014,7 +1016,7 @@ constexpr int kNwYRow = kNwN + 4;   // fp32 row pitch of the combine staging til
 constexpr int kNwYRows = 64;        // rows per staging pass
 
 __global__ __launch_bounds__(kNvThreads, 1) void moe_down_nvw_kernel(GemmParams p) {
-    __shared__ __align__(16) NwSmem<kNwMoeM, 2, false> sm;
+    __shared__ __align__(16) NwSmem sm;
     static_assert(kNwYRows * kNwYRow * 4 <= (int)sizeof(sm), "staging tile exceeds the wide tile's LDS");
     const int tile = blockIdx.y;
     if (tile >= *p.ntiles) return;
@@ -1026,16 +1028,18 @@ __global__ __launch_bounds__(kNvThreads, 1) void moe_down_nvw_kernel(GemmParams 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int lr = lane & 15, lq = lane >> 4;
 
+    // A = Q(h): gate/up's codes in routed order, or injected codes by slot
+    const bool inj = p.dbg.h_codes_in != nullptr;
     NwSrc S{};
-    S.a = reinterpret_cast<const uint8_t*>(p.h16);
+    S.ac = inj ? p.dbg.h_codes_in : p.hc;
+    S.as = inj ? p.dbg.h_scales_in : p.hs;
     S.b = p.w2c + (int64_t)e * H * (I / 2);
     S.s = p.w2s + (int64_t)e * H * (I / 16);
-    const uint32_t apitch = (uint32_t)(I * 2), bpitch = (uint32_t)(I / 2), spitch = (uint32_t)(I / 16);
-#pragma unroll
-    for (int q = 0; q < kNwMoeM / 32; ++q) {
-        const int arow = nw_a_row<kNwMoeM>(q);
-        const int64_t pos = min(r0 + arow, rend - 1);
-        S.aoff[q] = (uint32_t)(p.h16_by_slot ? p.perm[pos] : pos) * apitch + nw_a_chunk(arow);
+    const uint32_t bpitch = (uint32_t)(I / 2), spitch = (uint32_t)(I / 16);
+    {
+        const int64_t cpos = min(r0 + nw_ac_row(), rend - 1), spos = min(r0 + nw_as_row(), rend - 1);
+        S.acoff = (uint32_t)(inj ? p.perm[cpos] : cpos) * bpitch + nw_ac_chunk();
+        S.asoff = (uint32_t)(inj ? p.perm[spos] : spos) * spitch + nw_s_col();
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -1045,9 +1049,9 @@ __global__ __launch_bounds__(kNvThreads, 1) void moe_down_nvw_kernel(GemmParams 
 #pragma unroll
     for (int j = 0; j < 2; ++j) S.soff[j] = (uint32_t)min(n0 + nw_s_row(j), H - 1) * spitch + nw_s_col();
 
-    v4f acc[kNwMoeMf][4];
+    v4f acc[kNwMf][4];
 #pragma unroll
-    for (int mf = 0; mf < kNwMoeMf; ++mf)
+    for (int mf = 0; mf < kNwMf; ++mf)
 #pragma unroll
         for (int nf = 0; nf < 4; ++nf) acc[mf][nf] = v4f{0.f, 0.f, 0.f, 0.f};
     nw_mainloop_rows(sm, S, (int)(I / kNwK), acc, rend - r0);
@@ -1055,7 +1059,7 @@ __global__ __launch_bounds__(kNvThreads, 1) void moe_down_nvw_kernel(GemmParams 
     const float yscale = __fmul_rn(p.act_ts[1], p.w2ts[e]);
     float* ysm = reinterpret_cast<float*>(&sm);
 #pragma unroll
-    for (int pass = 0; pass < kNwMoeM / kNwYRows; ++pass) {
+    for (int pass = 0; pass < kNwM / kNwYRows; ++pass) {
         if (r0 + pass * kNwYRows >= rend) break;          // no rows of the problem in this pass (uniform)
         __syncthreads();   // the staging tile reuses the stages (or the previous pass)
 #pragma unroll
@@ -1164,7 +1168,7 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t s) {
     const bool tiled = a.fmt == FP4_FMT_MX && H % 512 == 0 && I % 512 == 0;
     const bool nv_tiled = a.fmt == FP4_FMT_NV && H % 256 == 0 && I % 256 == 0;
     const bool nv_decode = T <= kNvDecodeTokens;       // 32-row, three-stage NV tiles
-    const int tile_rows = tiled ? kTileM : (nv_tiled ? (nv_decode ? 32 : kNwMoeM) : kBM);
+    const int tile_rows = tiled ? kTileM : (nv_tiled ? (nv_decode ? 32 : kNwM) : kBM);
     // grid rows: at most ceil(S / tile_rows) full tiles plus one partial tile
     // per active expert (the workgroups past the actual count exit at once)
     const unsigned grid_tiles = (unsigned)((S + tile_rows - 1) / tile_rows + (E < S ? E : S));
@@ -1204,27 +1208,26 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t s) {
     p.hs = hs;
     p.ybuf = ybuf;
     p.dbg = a.dbg;
-    uint16_t* x16 = reinterpret_cast<uint16_t*>(base + L.x16);
-    uint16_t* h16 = reinterpret_cast<uint16_t*>(base + L.h16);
+    uint16_t* x16 = L.x16_h16 ? reinterpret_cast<uint16_t*>(base + L.x16) : nullptr;
+    uint16_t* h16 = L.x16_h16 ? reinterpret_cast<uint16_t*>(base + L.h16) : nullptr;
     p.x16 = x16;
     p.h16 = h16;
     p.h16_by_slot = a.dbg.h_codes_in != nullptr;
     // 3. gate/up + SiLU*mul + quantize h; 4. down + weighted combine
-    if (nv_tiled) {
+    if (nv_tiled && nv_decode) {
         expand_nv16_kernel<<<stream_grid(T * H / 16), kThreads, 0, s>>>(xc, xs, T, H, x16);
-        if (nv_decode)
-            moe_gate_up_nv_kernel<32, 3><<<dim3((unsigned)(I / kNvGuCols), grid_tiles), kNvThreads, 0, s>>>(p);
-        else
-            moe_gate_up_nvw_kernel<<<dim3((unsigned)(I / kNwGuCols), grid_tiles), kNvThreads, 0, s>>>(p);
+        moe_gate_up_nv_kernel<32, 3><<<dim3((unsigned)(I / kNvGuCols), grid_tiles), kNvThreads, 0, s>>>(p);
         if ((err = hipGetLastError()) != hipSuccess || (err = mark(3)) != hipSuccess) return err;
         if (a.dbg.h_codes_in)      // injected Q(h), by slot: its expansion replaces the tiles' own
             expand_nv16_kernel<<<stream_grid(S * I / 16), kThreads, 0, s>>>(a.dbg.h_codes_in, a.dbg.h_scales_in, S, I,
                                                                              h16);
-        if (nv_decode)
-            moe_down_nv_kernel<32, 3><<<dim3((unsigned)(H / kNvTileN), grid_tiles), kNvThreads, 0, s>>>(p);
-        else
-            moe_down_nvw_kernel<<<dim3((unsigned)((H + kNwN - 1) / kNwN), grid_tiles), kNvThreads, 0, s>>>(
-                p);
+        moe_down_nv_kernel<32, 3><<<dim3((unsigned)(H / kNvTileN), grid_tiles), kNvThreads, 0, s>>>(p);
+        if ((err = hipGetLastError()) != hipSuccess || (err = mark(4)) != hipSuccess) return err;
+    } else if (nv_tiled) {
+        // wide tiles: Q(x) and Q(h) stay NVFP4 codes, expanded inside the tiles
+        moe_gate_up_nvw_kernel<<<dim3((unsigned)(I / kNwGuCols), grid_tiles), kNvThreads, 0, s>>>(p);
+        if ((err = hipGetLastError()) != hipSuccess || (err = mark(3)) != hipSuccess) return err;
+        moe_down_nvw_kernel<<<dim3((unsigned)((H + kNwN - 1) / kNwN), grid_tiles), kNvThreads, 0, s>>>(p);
         if ((err = hipGetLastError()) != hipSuccess || (err = mark(4)) != hipSuccess) return err;
     } else if (tiled) {
         const dim3 g_gu((unsigned)(I / kGu2Cols), grid_tiles);

@@ -67,7 +67,7 @@ def test_moe_tiled_mx_segments():
 
 def test_moe_tiled_nv_segments():
     """Hidden and intermediate multiples of 256 take the 128-row LDS-staged NV
-    tiles (fp16 expansion of the codes): segments spanning several tiles,
+    tiles (A read as NVFP4 codes and expanded in the tile): segments spanning several tiles,
     ragged last tiles of several row-fragment counts, and last tiles of at most
     64 rows (whose second staging pass of the down tile is skipped)."""
     case, eq = _small_case("nv", 105, 300, 256, 256, 4, 2)
@@ -134,7 +134,7 @@ def test_moe_workload5_decode_sampled():
 @pytest.mark.timeout(600)
 def test_moe_workload5_prefill_sampled():
     """NVFP4 MoE at hidden 7168 on a prefill batch of 16384 tokens (98,304
-    routed slots, the 64-row two-stage NV tiles), in the launch the benchmark
+    routed slots, the 128-row wide NV tiles), in the launch the benchmark
     times: routing checked whole, two tokens checked per stage."""
     case, eq, sample = _full_case(5, "nv", tokens=16384, sample=(3, 12345))
     _all_checks(case, oracle_expect(case, sample, eq), fill=True)
