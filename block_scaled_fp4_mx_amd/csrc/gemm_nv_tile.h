@@ -1,6 +1,9 @@
-// LDS-staged NVFP4 block tile for gfx950: TM rows of A (fp16) x 256 rows of B
-// (NVFP4 codes + E4M3 group scales), K advancing 256 values per step; 512
-// threads, 8 waves, each wave all TM A rows x 32 B rows (two 16-row fragments).
+// LDS-staged NVFP4 block tile for gfx950: 32 rows of A (fp16) x 256 rows of B
+// (NVFP4 codes + E4M3 group scales), K advancing 256 values per step through
+// three stages; 512 threads, 8 waves, each wave all 32 A rows x 32 B rows (two
+// 16-row fragments).  Used by the decode-sized MoE grouped GEMMs: few rows per
+// expert, the expert weights stream from HBM, and the third stage keeps two K
+// steps of weights in flight per workgroup.
 //
 // NVFP4 group scales are not a matrix-core scale format, so B is expanded in
 // registers to the exact fp16 values code * s_g (at most 6 significant bits,
@@ -13,14 +16,7 @@
 // Stage layout per K step: A TM rows x 512 B (16-byte chunk c of row r at
 // c ^ (r & 15)), B codes 256 rows x 128 B (chunk c of row r at c ^ (r & 7)), B
 // scales 256 rows x 16 B.  All of it goes from global memory straight into LDS
-// (global_load_lds_dwordx4 / _dword), as in the MX tile.  A may also arrive as
-// NVFP4 codes and scales (the dense GEMM), expanded into the fp16 A in LDS by
-// the whole workgroup each step.
-//
-// Configurations: 64 A rows with two stages (prefill-sized MoE segments, dense
-// GEMM) and 32 A rows with three stages (decode: few rows per expert, the
-// expert weights stream from HBM, and the third stage keeps two K steps of
-// weights in flight per workgroup).
+// (global_load_lds_dwordx4 / _dword), as in the MX tile.
 #pragma once
 
 #include "gemm_mx_tile.h"
@@ -35,17 +31,16 @@ constexpr int kNvSRow = 16;         // scale bytes of one B row per step
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 
-template <int TM, bool ACODES>
+template <int TM>
 struct NvStageT {
     uint8_t a[TM * kNvARow];                        // fp16 A
     uint8_t b[kNvTileN * kNvBRow];
     uint8_t s[kNvTileN * kNvSRow];
-    uint8_t ac[ACODES ? TM * kNvBRow : 16];         // A codes (row-major), when A comes as NVFP4
-    uint8_t as[ACODES ? TM * kNvSRow : 16];         // A scales, likewise
 };
-template <int TM, int NS, bool ACODES>
+template <int TM, int NS>
 struct NvSmemT {
-    NvStageT<TM, ACODES> st[NS];
+    static_assert(TM == 32 && NS == 3, "the copy counts below are those of 32 A rows in three stages");
+    NvStageT<TM> st[NS];
 };
 
 // Sources of one tile, as per-lane byte offsets from bases that are the same
@@ -53,18 +48,13 @@ struct NvSmemT {
 // wave * (TM/16) + q, i.e. row nv_a_row<TM>(q), LDS chunk lane % 32, from global
 // chunk (lane % 32) ^ (row & 15); aoff[q] is that row's byte offset plus the
 // chunk.  B codes: DMA q fills rows (wave * 4 + q) * 8 + lane / 8 as in the MX
-// tile (boff[q]).  B scales: two stages: waves 0-3 fill rows wave * 64 + lane
-// with one 16-byte DMA (soff); three stages: every wave fills its 512 bytes with
-// two 4-byte DMAs (sdw[j]: byte wave*512 + j*256 + 4*lane of the scale slab).
+// tile (boff[q]).  B scales: every wave fills its 512 bytes with two 4-byte
+// DMAs (sdw[j]: byte wave*512 + j*256 + 4*lane of the scale slab).
 struct NvSrc {
     const uint8_t* a;       // fp16 activations
     const uint8_t* b;       // codes, row pitch K/2
     const uint8_t* s;       // E4M3 bytes, row pitch K/16
-    uint32_t aoff[4], boff[4], soff, sdw[2];
-    // A as NVFP4 codes + E4M3 bytes: the code DMA of wave w fills rows
-    // w*8 + lane/8, chunk lane & 7 (acoff); wave 0's scale DMA fills row lane (asoff)
-    const uint8_t *ac, *as;
-    uint32_t acoff, asoff;
+    uint32_t aoff[4], boff[4], sdw[2];
 };
 
 template <int TM>
@@ -85,38 +75,25 @@ __device__ __forceinline__ void dma4(const uint8_t* base, uint32_t off, uint32_t
                  : "memory", "m0");
 }
 
-// DMA instructions each wave issues per K step in the three-stage
-// configuration (A 2, B codes 4, B scales 2): the count the waits rely on.
-constexpr int kNvDmaPerStep3 = 8;
+// DMA instructions each wave issues per K step (A 2, B codes 4, B scales 2):
+// the count the waits rely on.
+constexpr int kNvDmaPerStep = 8;
 
-// Copies of one K step.  With two stages only the A rows of the MF fragments
-// in use are fetched (a decode-sized segment needs a quarter of the A bytes);
-// with three stages every wave issues the same fixed number of copies.
-template <int TM, int NS, bool ACODES, int MF>
-__device__ __forceinline__ void nv_issue(NvStageT<TM, ACODES>& sm, const NvSrc& S, int ks) {
-    static_assert(NS == 2 || (TM == 32 && !ACODES), "the three-stage copy count assumes 32 fp16 A rows");
+// Copies of one K step: every wave issues the same fixed number of copies.
+template <int TM>
+__device__ __forceinline__ void nv_issue(NvStageT<TM>& sm, const NvSrc& S, int ks) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint8_t* b = S.b + (int64_t)ks * kNvBRow;
     const uint32_t lb = lds_addr(sm.b) + wave * 4 * 1024;
-    if (ACODES) {
-        dma16(S.ac + (int64_t)ks * kNvBRow, S.acoff, lds_addr(sm.ac) + wave * 1024);
-        if (wave == 0) dma16(S.as + (int64_t)ks * kNvSRow, S.asoff, lds_addr(sm.as));
-    } else {
-        constexpr int QA = TM / 16;
-        const uint8_t* a = S.a + (int64_t)ks * kNvARow;
-        const uint32_t la = lds_addr(sm.a) + wave * QA * 1024;
+    constexpr int QA = TM / 16;
+    const uint8_t* a = S.a + (int64_t)ks * kNvARow;
+    const uint32_t la = lds_addr(sm.a) + wave * QA * 1024;
 #pragma unroll
-        for (int q = 0; q < QA; ++q)
-            if (NS != 2 || wave * QA + q < MF * 8) dma16(a, S.aoff[q], la + q * 1024);   // block = 2 rows
-    }
+    for (int q = 0; q < QA; ++q) dma16(a, S.aoff[q], la + q * 1024);   // block = 2 rows
 #pragma unroll
     for (int q = 0; q < 4; ++q) dma16(b, S.boff[q], lb + q * 1024);
-    if (NS == 2) {
-        if (wave < 4) dma16(S.s + (int64_t)ks * kNvSRow, S.soff, lds_addr(sm.s) + wave * 1024);
-    } else {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) dma4(S.s + (int64_t)ks * kNvSRow, S.sdw[j], lds_addr(sm.s) + wave * 512 + j * 256);
-    }
+    for (int j = 0; j < 2; ++j) dma4(S.s + (int64_t)ks * kNvSRow, S.sdw[j], lds_addr(sm.s) + wave * 512 + j * 256);
 }
 
 // Two E4M3 group bytes (bits 15:0 of g2) -> the fp16 pair {s_g0, s_g1}.  Every
@@ -139,51 +116,29 @@ __device__ __forceinline__ h8_t nv_expand8(uint32_t w, _Float16 s) {
     return h8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-// A given as codes: the step's TM x 256 A values expanded to fp16 into st.a
-// (TM*16 groups over the workgroup), in the swizzled layout the fragment reads use.
-template <int TM>
-__device__ __forceinline__ void nv_expand_a(NvStageT<TM, true>& st) {
-#pragma unroll
-    for (int q = 0; q < TM * 16 / kNvThreads; ++q) {
-        const int id = (int)threadIdx.x + q * kNvThreads;
-        const int row = id >> 4, g = id & 15;
-        const uint2 c = *reinterpret_cast<const uint2*>(&st.ac[row * kNvBRow + g * 8]);
-        const _Float16 sg = nv_scale_pair(st.as[row * kNvSRow + g])[0];
-        *reinterpret_cast<h8_t*>(&st.a[row * kNvARow + (((2 * g) ^ (row & 15)) << 4)]) = nv_expand8(c.x, sg);
-        *reinterpret_cast<h8_t*>(&st.a[row * kNvARow + (((2 * g + 1) ^ (row & 15)) << 4)]) = nv_expand8(c.y, sg);
-    }
-}
-template <int TM>
-__device__ __forceinline__ void nv_expand_a(NvStageT<TM, false>&) {}
-
 // Full K loop of one TM x 256 tile for the MF A fragments (16 rows each) that
 // hold rows of the problem.  acc[mf][nf]: A rows mf*16 .., B rows of the wave's
 // fragment nf (wave * 32 + nf * 16 ..); D row = A row, D column = B row.
-// Every wave takes part in the copies and barriers.  With NS stages the copies
-// of step ks + NS - 1 are issued at step ks; the wait at step ks leaves the
-// copies of the later steps in flight.
-template <int TM, int NS, bool ACODES, int MF>
-__device__ __forceinline__ void nv_tile_mainloop(NvSmemT<TM, NS, ACODES>& sm, const NvSrc& S, int nsteps,
-                                                 v4f acc[4][2]) {
+// Every wave takes part in the copies and barriers.  The copies of step
+// ks + NS - 1 are issued at step ks; the wait at step ks leaves the copies of
+// the later steps in flight.
+template <int TM, int NS, int MF>
+__device__ __forceinline__ void nv_tile_mainloop(NvSmemT<TM, NS>& sm, const NvSrc& S, int nsteps, v4f acc[4][2]) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int lr = lane & 15, lq = lane >> 4;
 #pragma unroll
     for (int p = 0; p < NS - 1; ++p)
-        if (p < nsteps) nv_issue<TM, NS, ACODES, MF>(sm.st[p], S, p);
+        if (p < nsteps) nv_issue<TM>(sm.st[p], S, p);
     int cur = 0;
     for (int ks = 0; ks < nsteps; ++ks) {
-        if (NS == 3 && ks + 1 < nsteps)
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kNvDmaPerStep3) : "memory");   // step ks + 1 may still land
+        if (ks + 1 < nsteps)
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kNvDmaPerStep) : "memory");   // step ks + 1 may still land
         else
             wait_vm_zero();
         __syncthreads();
         const int nxt = cur == 0 ? NS - 1 : cur - 1;    // (ks + NS - 1) % NS
-        if (ks + NS - 1 < nsteps) nv_issue<TM, NS, ACODES, MF>(sm.st[nxt], S, ks + NS - 1);
-        if (ACODES) {
-            nv_expand_a<TM>(sm.st[cur]);
-            __syncthreads();
-        }
-        const NvStageT<TM, ACODES>& st = sm.st[cur];
+        if (ks + NS - 1 < nsteps) nv_issue<TM>(sm.st[nxt], S, ks + NS - 1);
+        const NvStageT<TM>& st = sm.st[cur];
         cur = cur + 1 == NS ? 0 : cur + 1;
         if (MF == 0) continue;
 #pragma unroll
@@ -218,17 +173,17 @@ __device__ __forceinline__ void nv_tile_mainloop(NvSmemT<TM, NS, ACODES>& sm, co
     }
 }
 
-template <int TM, int NS, bool ACODES>
-__device__ __forceinline__ void nv_tile_mainloop_rows(NvSmemT<TM, NS, ACODES>& sm, const NvSrc& S, int nsteps,
-                                                      v4f acc[4][2], int64_t rows) {
+template <int TM, int NS>
+__device__ __forceinline__ void nv_tile_mainloop_rows(NvSmemT<TM, NS>& sm, const NvSrc& S, int nsteps, v4f acc[4][2],
+                                                      int64_t rows) {
     constexpr int kMaxMf = TM / 16;
     const int mf = rows <= 0 ? 0 : (rows >= TM ? kMaxMf : (int)((rows + 15) >> 4));
     switch (__builtin_amdgcn_readfirstlane(mf)) {
-        case 4: if constexpr (kMaxMf >= 4) nv_tile_mainloop<TM, NS, ACODES, 4>(sm, S, nsteps, acc); break;
-        case 3: if constexpr (kMaxMf >= 3) nv_tile_mainloop<TM, NS, ACODES, 3>(sm, S, nsteps, acc); break;
-        case 2: nv_tile_mainloop<TM, NS, ACODES, 2>(sm, S, nsteps, acc); break;
-        case 1: nv_tile_mainloop<TM, NS, ACODES, 1>(sm, S, nsteps, acc); break;
-        default: nv_tile_mainloop<TM, NS, ACODES, 0>(sm, S, nsteps, acc); break;
+        case 4: if constexpr (kMaxMf >= 4) nv_tile_mainloop<TM, NS, 4>(sm, S, nsteps, acc); break;
+        case 3: if constexpr (kMaxMf >= 3) nv_tile_mainloop<TM, NS, 3>(sm, S, nsteps, acc); break;
+        case 2: nv_tile_mainloop<TM, NS, 2>(sm, S, nsteps, acc); break;
+        case 1: nv_tile_mainloop<TM, NS, 1>(sm, S, nsteps, acc); break;
+        default: nv_tile_mainloop<TM, NS, 0>(sm, S, nsteps, acc); break;
     }
 }
 

@@ -715,7 +715,7 @@ __device__ __forceinline__ int64_t gu_nv_row(int slab_row, int64_t c0, int64_t I
 
 template <int TM, int NS>
 __global__ __launch_bounds__(kNvThreads, 1) void moe_gate_up_nv_kernel(GemmParams p) {
-    __shared__ __align__(16) NvSmemT<TM, NS, false> sm;
+    __shared__ __align__(16) NvSmemT<TM, NS> sm;
     const int tile = blockIdx.y;
     if (tile >= *p.ntiles) return;
     const int e = p.tile_e[tile];
@@ -748,7 +748,6 @@ __global__ __launch_bounds__(kNvThreads, 1) void moe_gate_up_nv_kernel(GemmParam
             }
             S.boff[q] = (uint32_t)gu_nv_row(mx_code_row(q), c0, I) * bpitch + mx_chunk16();
         }
-        S.soff = (uint32_t)gu_nv_row(mx_scale_row(), c0, I) * spitch;
 #pragma unroll
         for (int j = 0; j < 2; ++j) S.sdw[j] = (uint32_t)gu_nv_row(nv_sdw_row(j), c0, I) * spitch + nv_sdw_col();
         nv_tile_mainloop_rows(sm, S, (int)(H / 256), acc, rend - r0);
@@ -821,7 +820,7 @@ constexpr int kNvYRow = kNvTileN + 4;   // fp32 row pitch of the combine staging
 
 template <int TM, int NS>
 __global__ __launch_bounds__(kNvThreads, 1) void moe_down_nv_kernel(GemmParams p) {
-    __shared__ __align__(16) NvSmemT<TM, NS, false> sm;
+    __shared__ __align__(16) NvSmemT<TM, NS> sm;
     static_assert(TM * kNvYRow * 4 <= (int)sizeof(sm), "staging tile exceeds the NV tile's LDS");
     const int tile = blockIdx.y;
     if (tile >= *p.ntiles) return;
@@ -847,7 +846,6 @@ __global__ __launch_bounds__(kNvThreads, 1) void moe_down_nv_kernel(GemmParams p
         }
         S.boff[q] = (uint32_t)min(n0 + mx_code_row(q), H - 1) * bpitch + mx_chunk16();
     }
-    S.soff = (uint32_t)min(n0 + mx_scale_row(), H - 1) * spitch;
 #pragma unroll
     for (int j = 0; j < 2; ++j) S.sdw[j] = (uint32_t)min(n0 + nv_sdw_row(j), H - 1) * spitch + nv_sdw_col();
 
