@@ -48,6 +48,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import glob
 import json
 import os
 import sys
@@ -65,6 +66,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_FILE = os.path.join(HERE, "profiles", "traffic.json")
 MOE_KERNELS = ("quantize_x", "routing", "gate_up", "down", "combine")
 SPACER_CYCLES = 4_000_000
+TIMING_BLOCKS = 5              # per-stage timing blocks of `steps` launches each
 
 
 def parse():
@@ -99,6 +101,7 @@ class Stage:
         self.kernel = kernel        # kernel name(s) as rocprofv3 reports them
         self.moe = moe              # MoE: dict with the stage events and per-kernel work
         self.times = []             # ms per launch
+        self.best = None            # ms per launch of the fastest timing block
 
 
 def roofline_entry(bound, work, ms, per_unit, kernel, extra=None):
@@ -316,15 +319,21 @@ def main():
 
     moe_marks = {}
     for s in stages:
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        spacer()
-        e0.record(stream)
-        for _ in range(args.steps):
-            s.launch()
-            st["i"] += 1
-        e1.record(stream)
-        torch.cuda.synchronize()
-        s.times = [e0.elapsed_time(e1) / args.steps]
+        # TIMING_BLOCKS blocks of `steps` launches: the mean over all launches,
+        # and the best block's mean (events between single launches would
+        # disturb the short kernels)
+        s.times = []
+        for _ in range(TIMING_BLOCKS):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            spacer()
+            e0.record(stream)
+            for _ in range(args.steps):
+                s.launch()
+                st["i"] += 1
+            e1.record(stream)
+            torch.cuda.synchronize()
+            s.times.append(e0.elapsed_time(e1) / args.steps)
+        s.best = min(s.times)
         if s.moe:
             # the MoE entry point records its stage events between its kernels
             evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
@@ -345,7 +354,7 @@ def main():
     kernel_rows = []                        # (ms, name, entry) for the dominant-kernel choice
     for s in stages:
         ms = float(np.mean(s.times))
-        e = roofline_entry(s.bound, s.work, ms, s.per_unit, s.kernel)
+        e = roofline_entry(s.bound, s.work, ms, s.per_unit, s.kernel, {"best_us": round(s.best * 1e3, 2)})
         if s.moe:
             e["kernels"] = {}
             evs = moe_marks[s.name]
@@ -431,6 +440,7 @@ def main():
         "roofline": {k: v for k, v in dom.items() if k in ("bound", "achieved", "peak", "unit", "frac", "traffic")}
                     | {"kernel": dom_name},
         "rooflines": rooflines,
+        "gpu": gpu_info(torch),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
@@ -565,9 +575,12 @@ def cpu_baseline():
     from oracle import quant as Q
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count() or 1])
+        pools = threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in pools] or [os.cpu_count() or 1])
+        blas = ", ".join(sorted({f"{i.get('internal_api')} {i.get('num_threads')} threads" for i in pools
+                                 if i.get("user_api") == "blas"})) or "none found"
     except Exception:
-        threads = os.cpu_count() or 1
+        threads, blas = os.cpu_count() or 1, "unknown"
     wl = W.workload3()
     ab = W.bf16_bits(wl.A)
     wb = W.bf16_bits(wl.W)
@@ -580,7 +593,44 @@ def cpu_baseline():
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": "the whole 4096^3 W4A4 MXFP4 GEMM: MX-quantize A (fp64 numpy) and the exact fp64 product "
                       "with its error bound, W pre-quantized; "
-                      f"{dt:.1f} s on {os.cpu_count()} host cores"}
+                      f"{dt:.1f} s on {os.cpu_count()} host cores",
+            "cpu_model": cpu_model(), "os_cpu_count": os.cpu_count(), "blas": blas}
+
+
+def gpu_info(torch):
+    """Device name, architecture, compute units and the engine clock levels the
+    driver lists (the stage times above run at whatever level the power
+    manager picks; the peaks assume 2.4 GHz)."""
+    info = {}
+    try:
+        p = torch.cuda.get_device_properties(0)
+        info = {"name": p.name, "arch": getattr(p, "gcnArchName", None), "compute_units": p.multi_processor_count}
+        rate = getattr(p, "clock_rate", None)
+        if rate:
+            info["max_sclk_mhz"] = round(rate / 1000)
+    except Exception:
+        pass
+    levels = []
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            with open(path) as f:
+                levels += [int(t.lower().split("mhz")[0].split()[-1]) for t in f.read().split("\n") if "mhz" in t.lower()]
+        except (OSError, ValueError, IndexError):
+            continue
+    if levels:
+        info["sclk_levels_mhz"] = sorted(set(levels))
+    return info
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 if __name__ == "__main__":
