@@ -97,12 +97,21 @@ __global__ __launch_bounds__(kThreads) void mx_quantize_kernel(
     const int64_t upr = k >> 3;
     const int64_t total = rows * upr;
     const int64_t step = (int64_t)gridDim.x * kThreads * kMxUnroll;
+    const bool small = total <= 0xFFFFFFFFll;        // row of a unit by 32-bit division
     for (int64_t base = (int64_t)blockIdx.x * kThreads * kMxUnroll + threadIdx.x; base < total; base += step) {
         uint4 v[kMxUnroll];
+        int64_t row[kMxUnroll];
+        int32_t slotv[kMxUnroll];                     // slot mode: loaded with x, used by the stores
 #pragma unroll
         for (int j = 0; j < kMxUnroll; ++j) {
             const int64_t u = base + (int64_t)j * kThreads;
-            if (u < total) v[j] = *reinterpret_cast<const uint4*>(x + x_offset<kContig>(u, upr, ldx));
+            if (u < total) {
+                v[j] = *reinterpret_cast<const uint4*>(x + x_offset<kContig>(u, upr, ldx));
+                if (kOut == kOutSlots) {
+                    row[j] = small ? (int64_t)((uint32_t)u / (uint32_t)upr) : u / upr;
+                    slotv[j] = slots[row[j]];
+                }
+            }
         }
 #pragma unroll
         for (int j = 0; j < kMxUnroll; ++j) {
@@ -115,8 +124,8 @@ __global__ __launch_bounds__(kThreads) void mx_quantize_kernel(
                     reinterpret_cast<uint32_t*>(codes)[u] = packed;
                     if ((threadIdx.x & 3) == 0) scales[u >> 2] = (uint8_t)sbyte;
                 } else if (kOut == kOutSlots) {
-                    const int64_t r = u / upr;
-                    const int64_t slot = slots[r];
+                    const int64_t r = row[j];
+                    const int64_t slot = slotv[j];
                     if (slot >= 0 && slot < capacity) {
                         const int64_t v = slot * upr + (u - r * upr);
                         reinterpret_cast<uint32_t*>(codes)[v] = packed;
