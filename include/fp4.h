@@ -137,8 +137,10 @@ int fp4_dequant(fp4_format fmt, const uint8_t* codes, const uint8_t* scales,
  * accumulator rescaled per block).  A_hat, B_hat are the exact dequantized
  * operands; B is given [n, k] (the nn.Linear weight layout), so C = A . B^T.
  *   MX: scaled MFMA with the UE8M0 block scales applied by the matrix core.
- *   NV: operands expanded exactly to bf16 (code * s_g) and multiplied with bf16
- *       MFMA; the product is scaled by (*a_tensor_scale) * (*b_tensor_scale).
+ *   NV: operands expanded exactly to a 16-bit float (code * s_g has at most 6
+ *       significant bits: fp16 in the tiled kernels, bf16 in the fallback) and
+ *       multiplied on the 16-bit MFMA; the product is scaled by
+ *       (*a_tensor_scale) * (*b_tensor_scale).
  * c: [m, ldc] of c_dtype.  Tensor scales are device floats (NV only, else NULL).
  * Errors: k % 32 (MX) or k % 16 (NV) != 0 -> FP4_ERR_SHAPE.
  */
