@@ -17,18 +17,22 @@
 // once per wave and feeds eight MFMAs; every weight byte fetched serves 128 rows,
 // and A arrives as codes, a quarter of the bytes of its fp16 form.
 //
-// Pipeline (one barrier per step).  Three rings in LDS:
+// Pipeline (one barrier per step).  Three two-slot rings in LDS:
 //   B stages   (codes + scales of 512 rows)  2 slots, step ks in slot ks & 1;
 //   A stages   (codes + scales of 128 rows)  2 slots, step ks in slot ks & 1;
 //   fp16 A     (expanded)                    2 slots, step ks in slot ks & 1.
 // At step ks, after the wait for this wave's copies and the barrier, the
-// workgroup issues the copies of B(ks + 1) and A(ks + 2), expands A(ks + 1)
-// into its fp16 slot, and multiplies A(ks) by B(ks).  Every slot written in
-// step ks was last read in step ks - 1, which the barrier closes, and every slot
-// read in step ks was filled (copy landed, or expansion written) before it.
-// The expansion needs no barrier of its own: the next step's barrier orders
-// it before the fragment reads (it runs at the start of the step, where only
-// the accumulators hold registers).
+// workgroup issues the copies of A(ks + 2), reads B(ks) into registers,
+// expands A(ks + 1) into its fp16 slot, issues the copies of B(ks + 2) into
+// the B slot just read, and multiplies A(ks) by B(ks).  A slots (codes and
+// fp16) are shared: every one written in step ks was last read in step ks - 1,
+// which the barrier closes, and every one read in step ks was filled before
+// it.  B slots are private to a wave (wave w copies and reads only B rows
+// w*64 .. w*64 + 63), so a B slot is refilled as soon as the wave's own reads
+// of it have finished, and the weights get two steps of copy time.  The
+// expansion needs no barrier of its own: the next step's barrier orders it
+// before the fragment reads (it runs at the start of the step, where only the
+// accumulators hold registers).
 //
 // Stage layout per K step (128 values):
 //   fp16 A  128 rows x 256 B, 16-byte chunk c of row r at slot c ^ (r & 15);
@@ -118,6 +122,9 @@ __device__ __forceinline__ void nw_issue_a(NwAStage& st, const NwSrc& S, int ks)
     if (wave >= 4) dma4(S.as + (int64_t)ks * kNwSRow, S.asoff, lds_addr(st.s) + (wave - 4) * 256);
 }
 
+// Wait until at most one step of B copies (6 per wave) is in flight.
+__device__ __forceinline__ void nw_wait_b_in_flight() { asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); }
+
 // Half h (rows 64 h .. 64 h + 63) of one step's A expanded to fp16: each thread
 // expands one 16-group, in the swizzled layout the fragment reads use.
 __device__ __forceinline__ void nw_expand_a_half(const NwAStage& st, uint8_t* a16, int h) {
@@ -143,23 +150,26 @@ __device__ __forceinline__ void nw_mainloop(NwSmem& sm, const NwSrc& S, int nste
     const int lr = lane & 15, lq = lane >> 4;
     static_assert(MF >= 1 && MF <= kNwMf, "fragment count");
     constexpr int kHalves = MF > 4 ? 2 : 1;   // expanded 64-row halves of A
+    // copy order A(0), B(0), A(1), B(1), then per step A(ks + 2), B(ks + 2): the
+    // wait at the top of step ks (for B(ks) and A(ks + 1)) leaves B(ks + 1) in flight
     nw_issue_a(sm.a[0], S, 0);
     nw_issue_b(sm.b[0], S, 0);
-    if (nsteps > 1) nw_issue_a(sm.a[1], S, 1);
-    wait_vm_zero();
+    nw_wait_b_in_flight();                             // A(0)
     __syncthreads();
 #pragma unroll
     for (int h = 0; h < kHalves; ++h) nw_expand_a_half(sm.a[0], sm.a16[0], h);
+    if (nsteps > 1) {
+        nw_issue_a(sm.a[1], S, 1);
+        nw_issue_b(sm.b[1], S, 1);
+    }
     for (int ks = 0; ks < nsteps; ++ks) {
-        wait_vm_zero();
+        if (ks + 1 < nsteps)
+            nw_wait_b_in_flight();
+        else
+            wait_vm_zero();
         __syncthreads();
         const int cur = ks & 1, nxt = cur ^ 1;
-        if (ks + 1 < nsteps) nw_issue_b(sm.b[nxt], S, ks + 1);
         if (ks + 2 < nsteps) nw_issue_a(sm.a[cur], S, ks + 2);
-        // the next step's A (its codes landed with this step's copies)
-        if (ks + 1 < nsteps)
-#pragma unroll
-            for (int h = 0; h < kHalves; ++h) nw_expand_a_half(sm.a[nxt], sm.a16[nxt], h);
         const NwBStage& st = sm.b[cur];
         const uint8_t* ab = sm.a16[cur];
         // B: the lane's 32 codes of its row in each of the wave's fragments
@@ -170,6 +180,16 @@ __device__ __forceinline__ void nw_mainloop(NwSmem& sm, const NwSrc& S, int nste
             const int row = wave * 64 + nf * 16 + lr;
             c[nf] = *reinterpret_cast<const uint4*>(&st.b[row * kNwBRow + ((lq ^ nw_swz(row)) << 4)]);
             sp[nf] = nv_scale_pair(*reinterpret_cast<const uint16_t*>(&st.s[row * kNwSRow + lq * 2]));
+        }
+        // the next step's A (its codes landed with this step's wait)
+        if (ks + 1 < nsteps)
+#pragma unroll
+            for (int h = 0; h < kHalves; ++h) nw_expand_a_half(sm.a[nxt], sm.a16[nxt], h);
+        // B(ks + 2) into the slot just read: the wave's own rows, so its own
+        // reads are all that must finish first
+        if (ks + 2 < nsteps) {
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            nw_issue_b(sm.b[cur], S, ks + 2);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
