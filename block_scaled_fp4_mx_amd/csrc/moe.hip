@@ -10,10 +10,10 @@
 //      the quantized X rows through perm; each wave holds g and u for the same
 //      (row, column) positions, so the epilogue forms h = SiLU(g) * u in
 //      registers, rounds it to bf16 and quantizes it (MX or NV) straight from LDS;
-//   4. grouped down GEMM on the quantized h rows (NV: their exact fp16
-//      expansion, written by the gate/up epilogue), whose epilogue multiplies by
-//      the routing weight and writes the fp32 row of the slot into a
-//      [slots, hidden] buffer;
+//   4. grouped down GEMM on the quantized h rows (NV decode batches: their
+//      exact fp16 expansion, written by the gate/up epilogue; NV prefill and
+//      MX: the codes and scales), whose epilogue multiplies by the routing
+//      weight and writes the fp32 row of the slot into a [slots, hidden] buffer;
 //   5. combine: each token's topk rows summed in fp32 in slot order, then
 //      rounded to bf16 (no atomics, so the output is deterministic).
 // The steps follow the expert path of the routed experts' w1/w3/w2 projections
@@ -1007,9 +1007,9 @@ __global__ __launch_bounds__(kNvThreads, 1) void moe_gate_up_nvw_kernel(GemmPara
     }
 }
 
-// down: the fp16 expansion of Q(h) for the tile's rows times w2 rows n0 .. n0 + 511
-// (rows past H are clamped and their columns never stored).  The fp32 result
-// leaves through LDS in two passes of 64 rows.
+// down: Q(h) of the tile's rows (codes + E4M3 scales) times w2 rows
+// n0 .. n0 + 511 (rows past H are clamped and their columns never stored).  The
+// fp32 result leaves through LDS in two passes of 64 rows.
 constexpr int kNwYRow = kNwN + 4;   // fp32 row pitch of the combine staging tile
 constexpr int kNwYRows = 64;        // rows per staging pass
 
