@@ -15,7 +15,7 @@ Modules
   formats  -- E2M1 / E4M3 / UE8M0 / fp32 / bf16 encodings and correct rounding
   quant    -- MX and NV quantize, MX->NV remap, dequantize
   gemm     -- C = A . B^T over dequantized operands, error bound S
-  moe      -- routed-expert SwiGLU MoE (gate/up, SiLU*mul, down, combine)
+  moe      -- routed-expert SwiGLU MoE (gate/up, SiLU*mul, down, weighted sum)
 
 Parity pins: every function here is pinned by tests under ``tests/`` marked
 ``not gpu`` against the page's printed E2M1 table, library casts, closed forms,

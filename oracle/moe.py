@@ -18,9 +18,9 @@ rows 0..I-1 are w1 (gate) and I..2I-1 are w3 (up), w2 codes [E, H, I/2]; for
 NV each expert matrix is its own tensor with its own fp32 s_t.  NV activation
 tensor scales (for X and for h) are calibrated inputs [V41-NVFP4 s4].
 
-The staged functions let a test feed the GPU's own intermediates back in, so
-each stage is checked on identical inputs (fp32 summation order is the only
-freedom of the GEMM stages; SiLU's exp may differ in its last bit).
+The per-expert functions (gate/up, SiLU*mul, down) let a test compute each
+stage's expectation on its own inputs; the weighted sum over a token's slots
+is the last step of moe_forward.
 """
 from __future__ import annotations
 
@@ -102,12 +102,6 @@ def moe_forward(fmt: str, xbits: np.ndarray, ids: np.ndarray, weights: np.ndarra
     return dict(g=g, u=u, h_bits=h_bits, h_codes=hq[0], h_scales=hq[1], h_st=hq[2],
                 y=y, S_y=Sy, out_f64=out, out_bound=bound,
                 out_bits=F.bf16_rne_of_f64(out), x_codes=xq[0], x_scales=xq[1], x_st=xq[2])
-
-
-def combine(weights: np.ndarray, y: np.ndarray, S_y: np.ndarray):
-    """out_f64[t] = sum_j w[t,j] y[t,j] and its bound, from given y (fp64)."""
-    w = np.asarray(weights, np.float32).astype(np.float64)
-    return np.einsum("tj,tjh->th", w, y), np.einsum("tj,tjh->th", np.abs(w), S_y)
 
 
 def routing_metadata(ids: np.ndarray, num_experts: int):

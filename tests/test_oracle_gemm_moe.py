@@ -4,6 +4,8 @@ dense chain, identical experts, token permutation, brute-force gate/up)."""
 from fractions import Fraction
 
 import numpy as np
+import scipy.special
+import torch
 import pytest
 
 import workloads as W
@@ -177,6 +179,45 @@ def test_silu_mul_reference_values():
     expect = [0.0, 2 / (1 + np.exp(-1.0)), -2 / (1 + np.e), 20 / (1 + np.exp(-20.0)), -0.0]
     for a, b in zip(h, expect):
         assert F.bf16_bits_to_fraction(int(F.bf16_rne_of_f64(np.array([b]))[0])) == Fraction(a)
+
+
+def _silu_mul_expit_bf16(g, u):
+    """SiLU(g)*u from scipy's logistic function z*expit(z) (fp64), rounded to bf16
+    by torch's own float64 -> bfloat16 cast: no code shared with the oracle."""
+    h = g * scipy.special.expit(g) * u
+    return torch.from_numpy(h).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def test_silu_mul_against_scipy_expit():
+    """h = bf16(SiLU(g) u) against an independent evaluation, z*expit(z), over a
+    sweep of g that spans saturation on both sides (|g| up to 1e4, past the
+    fp64 overflow of exp(-g) at g < -709) and a spread of u."""
+    rng = np.random.default_rng(51)
+    g = np.concatenate([np.linspace(-40, 40, 4001), -np.logspace(-3, 4, 800), np.logspace(-3, 4, 800),
+                        rng.standard_normal(20000) * 3, [-700.0, -709.5, -745.0, -750.0, 709.5, 1e4]])
+    u = rng.choice([-7.0, -1.0, 0.37, 1.0, 2.5, 1e3], g.size) * rng.uniform(0.5, 2.0, g.size)
+    got = M.silu_mul_bf16(g, u)
+    exp = _silu_mul_expit_bf16(g, u)
+    assert np.array_equal(got, exp)
+
+
+def test_silu_closed_forms():
+    """Closed forms of SiLU(z) = z*sigmoid(z) through the oracle's h with u = 1:
+    SiLU(0) = 0; SiLU(z) rounds to z for large z and to zero for very negative
+    z; 0 < SiLU(z) <= z for z > 0 (after rounding); and SiLU(z) - SiLU(-z) = z (sigmoid(z) +
+    sigmoid(-z) = 1), up to the two bf16 roundings."""
+    one = lambda z: np.ones_like(z)
+    assert M.silu_mul_bf16(np.array([0.0]), np.array([5.0]))[0] & 0x7FFF == 0
+    big = np.array([40.0, 100.0, 1000.0])
+    assert np.array_equal(M.silu_mul_bf16(big, one(big)), F.bf16_rne_of_f64(big))
+    neg = np.array([-200.0, -1000.0, -1e5])
+    assert np.all((M.silu_mul_bf16(neg, one(neg)) & 0x7FFF) == 0)
+    z = np.array([0.5, 1.0, 2.0, 3.0, 8.0])
+    hp = F.bf16_bits_to_f64(M.silu_mul_bf16(z, one(z)))
+    assert np.all(hp <= z) and np.all(hp > 0)
+    zz = np.array([-3.0, -0.75, 0.125, 1.5, 6.0])
+    d = F.bf16_bits_to_f64(M.silu_mul_bf16(zz, one(zz))) - F.bf16_bits_to_f64(M.silu_mul_bf16(-zz, one(zz)))
+    assert np.all(np.abs(d - zz) <= 2.0 ** -8 * 2 * np.abs(zz))
 
 
 def test_routing_metadata_brute_force():
