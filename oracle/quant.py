@@ -46,6 +46,21 @@ FP4 -> FP8 [V4-QAT s4.2, V4-ARCH s6.3: FP4 data dequantize to FP8 without
 loss]: every E2M1 magnitude is an E4M3 value, so an MXFP4 block becomes an
 MXFP8 block with the same scale byte and each code re-encoded exactly.
 
+FP4 -> FP8 dequantization through E4M3 block scales [V4-QAT s4.2, its four
+steps; V4-ARCH s6.3: lossless while the block scale ratio stays under a
+threshold].  The pages re-encode the UE8M0 scale array in E4M3, widen every
+E2M1 code to E4M3, and multiply scale by data in FP8.  They name no tensor
+scale; E4M3 only spans 2**-9 .. 448, so the reading taken here puts one fp32
+power of two s_t = 2**k per tensor in front, k = E_max - 6 (E_max the largest
+block exponent), which maps the largest block's top code 6 to 6 * 2**6 = 384
+and never saturates.  Per block b with j = E_b - k:
+  s8_b = RNE_E4M3(2**j)             (step 2; exact iff j >= -9)
+  v8   = RNE_E4M3(MAG * s8_b)       (steps 3-4; sign copied from the code)
+The dequantized value is v8 * s_t.  A block is inexact when some element's
+v8 * s_t differs from its MX value; every block is exact when its exponent
+is at least E_max - 14, i.e. when the ratio of the largest to the smallest
+block scale is at most 2**14 (the threshold, under this reading).
+
 Dequantize [V41-NVFP4 s2: the accumulator multiplies scales back;
 V4-QAT s4.2 FP4 dequant through the scale]:
   MX: (-1)^s MAG[i] 2**E, exact in fp32 and bf16.
@@ -224,6 +239,56 @@ def mx_to_mxfp8(codes: np.ndarray) -> np.ndarray:
     bytes carry over unchanged): exact, as E2M1 magnitudes are E4M3 values."""
     c4 = unpack_nibbles(codes)
     return (E2M1_TO_E4M3[c4 & 7] | ((c4 & 8) << 4)).astype(np.uint8)
+
+
+# ====================================================================== FP4 -> FP8 dequant
+MX_FP8_TOP = 6                   # k = E_max - 6: the largest block's code 6 becomes 384
+
+
+def mx_dequant_fp8(codes: np.ndarray, scales: np.ndarray):
+    """MXFP4 (codes [R, K/2], UE8M0 scales [R, K/32]) -> (E4M3 values [R, K],
+    E4M3 block scales [R, K/32], fp32 tensor scale s_t, n_inexact blocks).
+
+    fp64 is exact: 2**j and MAG * s8_b are short dyadic numbers, and the E4M3
+    rounding compares them with exact midpoints of the E4M3 table."""
+    sc = np.asarray(scales, dtype=np.int64)
+    R, nb = sc.shape
+    if sc.size == 0:
+        return np.zeros((R, nb * MX_BLOCK), np.uint8), np.zeros((R, nb), np.uint8), np.float32(1.0), 0
+    Emax = int(sc.max()) - 127
+    k = Emax - MX_FP8_TOP
+    j = sc - 127 - k                                        # <= 6
+    s8 = F.e4m3_rne_sat_f64(np.ldexp(1.0, j))               # step 2: the scale array in E4M3
+    c4 = unpack_nibbles(codes).reshape(R, nb, MX_BLOCK)
+    prod = F.E2M1_MAG_F64[c4 & 7] * F.e4m3_value_f64(s8)[..., None]
+    v8 = F.e4m3_rne_sat_f64(prod) | ((c4 & 8) << 4)         # steps 3-4, sign from the code
+    exact = e4m3_signed_f64(v8) * np.ldexp(1.0, k) == code_values_f64(c4) * np.ldexp(1.0, sc - 127)[..., None]
+    n_inexact = int((~exact.all(axis=-1)).sum())
+    return v8.reshape(R, nb * MX_BLOCK).astype(np.uint8), s8.astype(np.uint8), np.float32(np.ldexp(1.0, k)), n_inexact
+
+
+def mx_dequant_fp8_exact(codes: np.ndarray, scales: np.ndarray):
+    """Scalar-loop form of mx_dequant_fp8 for small inputs (Fraction arithmetic)."""
+    R, nb = scales.shape
+    Emax = max(int(b) - 127 for b in scales.ravel())
+    k = Emax - MX_FP8_TOP
+    c4 = unpack_nibbles(codes)
+    v8 = np.zeros((R, nb * MX_BLOCK), np.uint8)
+    s8 = np.zeros((R, nb), np.uint8)
+    n_inexact = 0
+    for r in range(R):
+        for b in range(nb):
+            Eb = int(scales[r, b]) - 127
+            sb = F.round_e4m3_sat(Fraction(2) ** (Eb - k))
+            s8[r, b] = F.e4m3_encode(sb)
+            inexact = False
+            for i in range(MX_BLOCK):
+                c = int(c4[r, b * MX_BLOCK + i])
+                v = F.round_e4m3_sat(F.E2M1_MAG[c & 7] * sb)
+                v8[r, b * MX_BLOCK + i] = F.e4m3_encode(v) | (0x80 if c & 8 else 0)
+                inexact |= v * Fraction(2) ** k != F.E2M1_MAG[c & 7] * Fraction(2) ** Eb
+            n_inexact += inexact
+    return v8, s8, np.float32(float(Fraction(2) ** k)), n_inexact
 
 
 # ====================================================================== NV
