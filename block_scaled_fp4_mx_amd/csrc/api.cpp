@@ -261,6 +261,22 @@ int fp4_quantize_mxfp8(const void* x_bf16, int64_t rows, int64_t k, int64_t ld_x
                       "fp4_quantize_mxfp8 launch");
 }
 
+int fp4_mx_dequant_fp8(const uint8_t* codes, const uint8_t* scales_e8m0, int64_t rows, int64_t k,
+                       uint8_t* values_e4m3, uint8_t* block_scales_e4m3, float* tensor_scale,
+                       int32_t* n_inexact_blocks, void* stream) {
+    FP4_REQUIRE(rows >= 0 && k >= 0, FP4_ERR_INVALID, "negative size rows=%lld k=%lld", (long long)rows, (long long)k);
+    FP4_REQUIRE(k % 32 == 0, FP4_ERR_SHAPE, "k=%lld is not a multiple of 32", (long long)k);
+    if (rows == 0 || k == 0) return ok();
+    FP4_PTR(codes);
+    FP4_PTR(scales_e8m0);
+    FP4_PTR(values_e4m3);
+    FP4_SCALAR_PTR(tensor_scale);
+    FP4_SCALAR_PTR(n_inexact_blocks);
+    return hip_status(fp4::launch_dequant_fp8(codes, scales_e8m0, rows, k, values_e4m3, block_scales_e4m3,
+                                              tensor_scale, n_inexact_blocks, static_cast<hipStream_t>(stream)),
+                      "fp4_mx_dequant_fp8 launch");
+}
+
 int fp4_mx_to_mxfp8(const uint8_t* codes, int64_t rows, int64_t k, uint8_t* codes8, void* stream) {
     FP4_REQUIRE(rows >= 0 && k >= 0, FP4_ERR_INVALID, "negative size rows=%lld k=%lld", (long long)rows, (long long)k);
     FP4_REQUIRE(k % 32 == 0, FP4_ERR_SHAPE, "k=%lld is not a multiple of 32", (long long)k);
@@ -313,6 +329,19 @@ int fp4_moe_grouped_gemm(fp4_format fmt, const void* x_bf16, int64_t tokens, int
                 (long long)hidden, (long long)inter);
     FP4_REQUIRE(tokens * topk < (int64_t)1 << 30 && fp4::moe_max_tiles(tokens, topk, num_experts) <= 65535,
                 FP4_ERR_SHAPE, "tokens*topk=%lld too large", (long long)(tokens * topk));
+    {
+        // The grouped GEMM tiles address each operand with 32-bit byte offsets
+        // from its base: the gathered activation rows (Q(x) by token, Q(h) by
+        // routed slot; NV also their fp16 expansions) and one expert's weight
+        // slab.  Each must stay below 2 GiB.
+        const int64_t lim = (int64_t)1 << 31, S = tokens * topk;
+        const int64_t act_x = fmt == FP4_FMT_NV ? tokens * hidden * 2 : tokens * (hidden / 2);
+        const int64_t act_h = fmt == FP4_FMT_NV ? S * inter * 2 : S * (inter / 2);
+        FP4_REQUIRE(act_x < lim && act_h < lim && inter * hidden < lim, FP4_ERR_SHAPE,
+                    "operand too large for 32-bit tile offsets: activations %lld and %lld bytes, expert slab %lld "
+                    "bytes (each must be below 2^31)",
+                    (long long)act_x, (long long)act_h, (long long)(inter * hidden));
+    }
     if (tokens == 0) return ok();
     FP4_PTR(x_bf16);
     FP4_SCALAR_PTR(topk_ids);

@@ -91,6 +91,8 @@ hipError_t launch_ste_backward(const void* g, int g_f32, int64_t rows, int64_t k
                                int accumulate, hipStream_t s);
 hipError_t launch_remap(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t k,
                         uint8_t* scales_nv, float* tensor_scale, int32_t* n_inexact, hipStream_t s);
+hipError_t launch_dequant_fp8(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t k, uint8_t* v8,
+                              uint8_t* s8, float* tensor_scale, int32_t* n_inexact, hipStream_t s);
 hipError_t launch_dequant(int fmt, const uint8_t* codes, const uint8_t* scales, const float* ts,
                           int64_t rows, int64_t k, void* out, int out_f32, int64_t ld_out,
                           hipStream_t s);

@@ -396,68 +396,254 @@ __global__ __launch_bounds__(kThreads) void ste_backward_kernel(const void* __re
     }
 }
 
-// ------------------------------------------------------------------ MX -> NV remap
-// Pass 1 (one workgroup): the largest scale byte E_max + 127 over the tensor,
-// s_t = 2^(E_max - 8), and the inexact-block counter cleared.  Pass 2 writes
-// both E4M3 group scales of every block and counts blocks that lose precision.
-constexpr int kRemapMaxThreads = 1024;
+// ------------------------------------------------------------------ tensor-wide scale passes
+// The MX -> NV remap and the MX -> FP8 dequantization both need E_max, the
+// largest block exponent of the whole tensor, before any output is final.
+// Both run as two launches of many workgroups, without workspace:
+//   pass 1 (scale_max_kernel): workgroup g writes the largest scale byte of its
+//     share to byte g of the output array (a scratch use of bytes that pass 2
+//     rewrites last) and workgroup 0 clears the two result words (the int32
+//     counter and the fp32 tensor scale, used as integers until the end);
+//   pass 2: every workgroup reduces the pass-1 bytes to E_max, converts its
+//     blocks except the first `reserved` ones (whose output bytes hold the
+//     pass-1 maxima), adds its inexact blocks to the tensor-scale word and then
+//     takes a ticket from the counter word.  The workgroup that draws the last
+//     ticket knows every other workgroup has finished reading the pass-1 bytes:
+//     it converts the reserved blocks, then writes the final count and the
+//     tensor scale over the two words.
+constexpr int kScaleMaxChunk = 4096;   // scale bytes per pass-1 workgroup
+constexpr int kScaleMaxGroups = 256;   // at most one byte per pass-2 thread
 
-__global__ __launch_bounds__(kRemapMaxThreads) void remap_max_kernel(const uint8_t* __restrict__ s, int64_t nb,
-                                                                     float* __restrict__ ts,
-                                                                     int32_t* __restrict__ n_inexact) {
+__global__ __launch_bounds__(kThreads) void scale_max_kernel(const uint8_t* __restrict__ s, int64_t nb,
+                                                             uint8_t* __restrict__ part, uint32_t* __restrict__ w0,
+                                                             uint32_t* __restrict__ w1) {
+    const int64_t lo = (int64_t)blockIdx.x * nb / gridDim.x, hi = (int64_t)(blockIdx.x + 1) * nb / gridDim.x;
     uint32_t m = 0;
-    const int64_t n16 = nb >> 4;
-    const uint4* s16 = reinterpret_cast<const uint4*>(s);
-    constexpr int kDepth = 4;           // 16-byte loads in flight per thread (deeper measured no faster)
-    for (int64_t i = threadIdx.x; i < n16; i += kDepth * kRemapMaxThreads) {
-        uint4 v[kDepth];
+    // bytes before the first 16-byte boundary, the 16-byte body, then the tail
+    const int64_t a0 = min((lo + 15) & ~(int64_t)15, hi), a1 = max(a0, hi & ~(int64_t)15);
+    for (int64_t i = lo + threadIdx.x; i < a0; i += kThreads) m = max(m, (uint32_t)s[i]);
+    for (int64_t i = a1 + threadIdx.x; i < hi; i += kThreads) m = max(m, (uint32_t)s[i]);
+    const uint4* s16 = reinterpret_cast<const uint4*>(s + a0);
+    for (int64_t q = threadIdx.x; q < (a1 - a0) >> 4; q += kThreads) {
+        const uint4 v = s16[q];
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-        for (int j = 0; j < kDepth; ++j) {
-            const int64_t q = i + (int64_t)j * kRemapMaxThreads;
-            v[j] = q < n16 ? s16[q] : make_uint4(0, 0, 0, 0);
-        }
-#pragma unroll
-        for (int j = 0; j < kDepth; ++j) {
-            const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-                m = max(m, max(max(w[t] & 0xFFu, (w[t] >> 8) & 0xFFu), max((w[t] >> 16) & 0xFFu, w[t] >> 24)));
-        }
+        for (int t = 0; t < 4; ++t)
+            m = max(m, max(max(w[t] & 0xFFu, (w[t] >> 8) & 0xFFu), max((w[t] >> 16) & 0xFFu, w[t] >> 24)));
     }
-    for (int64_t i = (n16 << 4) + threadIdx.x; i < nb; i += kRemapMaxThreads) m = max(m, (uint32_t)s[i]);
     for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
-    __shared__ uint32_t red[kRemapMaxThreads / 64];
+    __shared__ uint32_t red[kThreads / 64];
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
     __syncthreads();
     if (threadIdx.x == 0) {
-        for (int i = 0; i < kRemapMaxThreads / 64; ++i) m = max(m, red[i]);
-        *ts = ldexpf(1.0f, (int)m - 127 - 8);    // 2^-135 .. 2^119; below 2^-126 a subnormal
-        *n_inexact = 0;
+        for (int i = 1; i < kThreads / 64; ++i) m = max(m, red[i]);
+        part[blockIdx.x] = (uint8_t)m;
+        if (blockIdx.x == 0) {
+            *w0 = 0u;
+            *w1 = 0u;
+        }
     }
+}
+
+inline unsigned scale_max_groups(int64_t nb) {
+    int64_t g = (nb + kScaleMaxChunk - 1) / kScaleMaxChunk;
+    return (unsigned)(g < 1 ? 1 : (g > kScaleMaxGroups ? kScaleMaxGroups : g));
+}
+
+// E_max + 127 from the pass-1 bytes (every thread gets it).
+__device__ __forceinline__ uint32_t reduce_part(const uint8_t* part, int npart, uint32_t* red) {
+    uint32_t m = threadIdx.x < (unsigned)npart ? (uint32_t)part[threadIdx.x] : 0u;
+    for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    m = red[0];
+    for (int i = 1; i < kThreads / 64; ++i) m = max(m, red[i]);
+    return m;
+}
+
+// The end of pass 2: per-workgroup inexact count `mine`, then the ticket; true
+// in the one workgroup that must finish the reserved blocks (all threads).
+__device__ __forceinline__ bool ticket_last(uint32_t mine, uint32_t* cnt_word, uint32_t* ticket_word,
+                                            uint32_t* sh) {
+    for (int off = 32; off > 0; off >>= 1) mine += (uint32_t)__shfl_xor((int)mine, off);
+    __syncthreads();                       // the reduce_part slots are free again
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = mine;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t t = 0;
+        for (int i = 0; i < kThreads / 64; ++i) t += sh[i];
+        if (t) atomicAdd(cnt_word, t);
+        __threadfence();
+        sh[0] = atomicAdd(ticket_word, 1u) == gridDim.x - 1 ? 1u : 0u;
+    }
+    __syncthreads();
+    const bool last = sh[0] != 0u;
+    __syncthreads();
+    return last;
+}
+
+// ------------------------------------------------------------------ MX -> NV remap
+// s_t = 2^(E_max - 8); both E4M3 group scales of block b are 2^(E_b - k),
+// exact for j = E_b - k in [-9, 8]; a block with a nonzero code below that
+// range is inexact (2^-10 ties to 0).  One lane per block.
+__device__ __forceinline__ uint32_t remap_block(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ s,
+                                                uint8_t* __restrict__ snv, int64_t i, int kexp) {
+    const int j = (int)s[i] - 127 - kexp;                 // <= 8
+    uint32_t sg, bad = 0;
+    if (j >= -6) {
+        sg = (uint32_t)(j + 7) << 3;                      // normal 2^j
+    } else if (j >= -9) {
+        sg = 1u << (j + 9);                               // subnormal 2^j = 2^(j+9) * 2^-9
+    } else {
+        sg = 0u;                                          // 2^-10 ties to 0, below rounds to 0
+        const uint4 a = reinterpret_cast<const uint4*>(codes + i * 16)[0];
+        bad = ((a.x | a.y | a.z | a.w) & 0x77777777u) ? 1u : 0u;
+    }
+    reinterpret_cast<uint16_t*>(snv)[i] = (uint16_t)(sg | (sg << 8));
+    return bad;
 }
 
 __global__ __launch_bounds__(kThreads) void remap_kernel(const uint8_t* __restrict__ codes,
                                                          const uint8_t* __restrict__ s, int64_t nb,
-                                                         uint8_t* __restrict__ snv, const float* ts,
-                                                         int32_t* n_inexact) {
-    const int kexp = ilogbf(*ts);          // k = E_max - 8 (exact for subnormal 2^k too)
+                                                         uint8_t* __restrict__ snv, int npart, int64_t reserved,
+                                                         float* __restrict__ ts, int32_t* __restrict__ n_inexact) {
+    __shared__ uint32_t red[kThreads / 64];
+    const int kexp = (int)reduce_part(snv, npart, red) - 127 - 8;
+    uint32_t bad = 0;
     const int64_t stride = (int64_t)gridDim.x * kThreads;
-    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nb; i += stride) {
-        const int j = (int)s[i] - 127 - kexp;              // <= 8
-        uint32_t sg;
-        if (j >= -6) {
-            sg = (uint32_t)(j + 7) << 3;                      // normal 2^j
-        } else if (j >= -9) {
-            sg = 1u << (j + 9);                               // subnormal 2^j = 2^(j+9) * 2^-9
+    for (int64_t i = reserved + (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nb; i += stride)
+        bad += remap_block(codes, s, snv, i, kexp);
+    uint32_t* cnt = reinterpret_cast<uint32_t*>(ts);
+    uint32_t* tk = reinterpret_cast<uint32_t*>(n_inexact);
+    if (!ticket_last(bad, cnt, tk, red)) return;
+    bad = 0;
+    for (int64_t i = threadIdx.x; i < reserved; i += kThreads) bad += remap_block(codes, s, snv, i, kexp);
+    for (int off = 32; off > 0; off >>= 1) bad += (uint32_t)__shfl_xor((int)bad, off);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = bad;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t t = atomicAdd(cnt, 0u);
+        for (int i = 0; i < kThreads / 64; ++i) t += red[i];
+        *n_inexact = (int32_t)t;
+        *ts = ldexpf(1.0f, kexp);          // 2^-135 .. 2^119; below 2^-126 a subnormal
+    }
+}
+
+// ------------------------------------------------------------------ MX -> FP8 dequant
+// s_t = 2^k with k = E_max - 6.  For block exponent j = E_b - k (<= 6) the E4M3
+// block scale is s8 = RNE(2^j) (exact for j >= -9, 2^-10 ties to 0) and each
+// element becomes RNE_E4M3(MAG * s8) with the code's sign.  MAG = (1 + h/2) 2^p
+// for magnitude index i >= 1 (p = -1, 0, 0, 1, 1, 2, 2; h = i + 1 & 1 beyond
+// i = 1), so with s8 = 2^j the value is (1 + h/2) 2^e, e = p + j >= -10:
+//   e >= -6       normal byte (e + 7) << 3 | h << 2 (exact; e <= 8 gives 384),
+//   e = -7, -8    subnormal (2 + h) << (e + 8) (exact),
+//   e = -9        (2 + h) / 2: h = 0 gives 1; h = 1 ties 1.5 to 2 (inexact),
+//   e = -10       (2 + h) / 4: 0.5 ties to 0, 0.75 rounds to 1 (both inexact).
+// The block's 8 value bytes go into two words, so v_perm_b32 maps four codes'
+// magnitude indices to their bytes at once.  `bad` has bit i set when
+// magnitude i is inexact in this block.
+__device__ __forceinline__ void fp8_block_table(int j, uint32_t& tlo, uint32_t& thi, uint32_t& bad, uint32_t& s8) {
+    tlo = thi = 0u;
+    bad = 0u;
+    if (j < -9) {                               // the scale itself rounds to zero
+        s8 = 0u;
+        bad = 0xFEu;
+        return;
+    }
+    s8 = j >= -6 ? (uint32_t)(j + 7) << 3 : 1u << (j + 9);
+#pragma unroll
+    for (int i = 1; i < 8; ++i) {
+        const int p = i == 1 ? -1 : (i >> 1) - 1;
+        const uint32_t h = i == 1 ? 0u : (uint32_t)(i & 1);
+        const int e = p + j;
+        uint32_t b;
+        if (e >= -6) {
+            b = ((uint32_t)(e + 7) << 3) | (h << 2);
+        } else if (e >= -8) {
+            b = (2u + h) << (e + 8);
+        } else if (e == -9) {
+            b = h ? 2u : 1u;
+            bad |= h << i;
         } else {
-            sg = 0u;                                          // 2^-10 ties to 0, below rounds to 0
-            const uint4* c = reinterpret_cast<const uint4*>(codes + i * 16);
-            const uint4 a = c[0];
-            const uint32_t nz = (a.x | a.y | a.z | a.w) & 0x77777777u;
-            if (nz) atomicAdd(n_inexact, 1);
+            b = h;
+            bad |= 1u << i;
         }
-        const uint16_t pair = (uint16_t)(sg | (sg << 8));
-        reinterpret_cast<uint16_t*>(snv)[i] = pair;
+        if (i < 4) tlo |= b << (8 * i);
+        else thi |= b << (8 * (i - 4));
+    }
+}
+
+// Eight codes (one word) -> eight E4M3 bytes (two words); `hit` collects the
+// magnitude indices present.
+__device__ __forceinline__ uint2 fp8_expand8(uint32_t c, uint32_t tlo, uint32_t thi, uint32_t& hit) {
+    const uint32_t mag = c & 0x77777777u;
+    const uint32_t sgn = c & 0x88888888u;
+    // magnitude nibbles 0..3 and 4..7 spread into bytes (perm selectors)
+    const uint32_t sel0 = (mag & 0x7u) | ((mag >> 4) & 0x7u) << 8 | ((mag >> 8) & 0x7u) << 16 | ((mag >> 12) & 0x7u) << 24;
+    const uint32_t sel1 = ((mag >> 16) & 0x7u) | ((mag >> 20) & 0x7u) << 8 | ((mag >> 24) & 0x7u) << 16 | (mag >> 28) << 24;
+    uint2 r;
+    r.x = __builtin_amdgcn_perm(thi, tlo, sel0);
+    r.y = __builtin_amdgcn_perm(thi, tlo, sel1);
+    // sign bit 3 of nibble q goes to bit 7 of byte q
+    r.x |= ((sgn & 0x8u) << 4) | ((sgn & 0x80u) << 8) | ((sgn & 0x800u) << 12) | ((sgn & 0x8000u) << 16);
+    r.y |= ((sgn >> 16) & 0x8u) << 4 | ((sgn >> 16) & 0x80u) << 8 | ((sgn >> 16) & 0x800u) << 12 |
+           ((sgn >> 16) & 0x8000u) << 16;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) hit |= 1u << ((mag >> (4 * q)) & 7u);
+    return r;
+}
+
+// Half a block per lane (16 codes in, 16 bytes out); returns 1 on the even lane
+// of a block pair when the block is inexact.  Both lanes of a pair are active
+// together (units are whole blocks).
+__device__ __forceinline__ uint32_t fp8_half_block(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ s,
+                                                   uint8_t* __restrict__ v8, uint8_t* __restrict__ s8out,
+                                                   int64_t u, int kexp) {
+    const int64_t b = u >> 1;
+    const int j = (int)s[b] - 127 - kexp;
+    uint32_t tlo, thi, badm, s8;
+    fp8_block_table(j, tlo, thi, badm, s8);
+    const uint2 c = reinterpret_cast<const uint2*>(codes)[u];
+    uint32_t hit = 0;
+    const uint2 lo = fp8_expand8(c.x, tlo, thi, hit);
+    const uint2 hi = fp8_expand8(c.y, tlo, thi, hit);
+    reinterpret_cast<uint4*>(v8)[u] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    if (s8out != nullptr && (u & 1) == 0) s8out[b] = (uint8_t)s8;
+    return (hit & badm) ? 1u : 0u;
+}
+
+__global__ __launch_bounds__(kThreads) void fp8_dequant_kernel(const uint8_t* __restrict__ codes,
+                                                               const uint8_t* __restrict__ s, int64_t nb,
+                                                               uint8_t* __restrict__ v8, uint8_t* __restrict__ s8out,
+                                                               int npart, int64_t reserved, float* __restrict__ ts,
+                                                               int32_t* __restrict__ n_inexact) {
+    __shared__ uint32_t red[kThreads / 64];
+    const int kexp = (int)reduce_part(v8, npart, red) - 127 - 6;
+    const int64_t units = nb * 2, ures = reserved * 2;
+    const int64_t stride = (int64_t)gridDim.x * kThreads;     // even, so a pair stays in one wave
+    uint32_t bad = 0;
+    for (int64_t u = ures + (int64_t)blockIdx.x * kThreads + threadIdx.x; u < units; u += stride) {
+        uint32_t f = fp8_half_block(codes, s, v8, s8out, u, kexp);
+        f |= (uint32_t)__shfl_xor((int)f, 1);
+        if ((u & 1) == 0) bad += f;
+    }
+    uint32_t* cnt = reinterpret_cast<uint32_t*>(ts);
+    uint32_t* tk = reinterpret_cast<uint32_t*>(n_inexact);
+    if (!ticket_last(bad, cnt, tk, red)) return;
+    bad = 0;
+    for (int64_t u = threadIdx.x; u < ures; u += kThreads) {
+        uint32_t f = fp8_half_block(codes, s, v8, s8out, u, kexp);
+        f |= (uint32_t)__shfl_xor((int)f, 1);
+        if ((u & 1) == 0) bad += f;
+    }
+    for (int off = 32; off > 0; off >>= 1) bad += (uint32_t)__shfl_xor((int)bad, off);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = bad;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t t = atomicAdd(cnt, 0u);
+        for (int i = 0; i < kThreads / 64; ++i) t += red[i];
+        *n_inexact = (int32_t)t;
+        *ts = ldexpf(1.0f, kexp);          // 2^-133 .. 2^121; below 2^-126 a subnormal
     }
 }
 
@@ -577,8 +763,26 @@ hipError_t launch_ste_backward(const void* g, int g_f32, int64_t rows, int64_t k
 hipError_t launch_remap(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t k,
                         uint8_t* scales_nv, float* ts, int32_t* n_inexact, hipStream_t s) {
     const int64_t nb = rows * (k / 32);
-    remap_max_kernel<<<1, kRemapMaxThreads, 0, s>>>(scales, nb, ts, n_inexact);
-    remap_kernel<<<grid_for(nb), kThreads, 0, s>>>(codes, scales, nb, scales_nv, ts, n_inexact);
+    const unsigned g1 = scale_max_groups(nb);
+    scale_max_kernel<<<g1, kThreads, 0, s>>>(scales, nb, scales_nv, reinterpret_cast<uint32_t*>(ts),
+                                              reinterpret_cast<uint32_t*>(n_inexact));
+    const int64_t reserved = min((int64_t)(g1 + 1) / 2, nb);   // blocks whose 2 output bytes hold pass-1 maxima
+    unsigned g2 = grid_for(nb - reserved);
+    if (g2 > kMxMaxBlocks) g2 = kMxMaxBlocks;
+    remap_kernel<<<g2, kThreads, 0, s>>>(codes, scales, nb, scales_nv, (int)g1, reserved, ts, n_inexact);
+    return hipGetLastError();
+}
+
+hipError_t launch_dequant_fp8(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t k, uint8_t* v8,
+                              uint8_t* s8, float* ts, int32_t* n_inexact, hipStream_t s) {
+    const int64_t nb = rows * (k / 32);
+    const unsigned g1 = scale_max_groups(nb);
+    scale_max_kernel<<<g1, kThreads, 0, s>>>(scales, nb, v8, reinterpret_cast<uint32_t*>(ts),
+                                              reinterpret_cast<uint32_t*>(n_inexact));
+    const int64_t reserved = min((int64_t)(g1 + 31) / 32, nb);  // blocks whose 32 output bytes hold pass-1 maxima
+    unsigned g2 = grid_for(2 * (nb - reserved));
+    if (g2 > kMxMaxBlocks) g2 = kMxMaxBlocks;
+    fp8_dequant_kernel<<<g2, kThreads, 0, s>>>(codes, scales, nb, v8, s8, (int)g1, reserved, ts, n_inexact);
     return hipGetLastError();
 }
 

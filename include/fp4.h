@@ -232,6 +232,33 @@ int fp4_quantize_mxfp8(const void* x_bf16, int64_t rows, int64_t k, int64_t ld_x
 int fp4_mx_to_mxfp8(const uint8_t* codes, int64_t rows, int64_t k, uint8_t* codes8, void* stream);
 
 /*
+ * MXFP4 -> FP8 dequantization through E4M3 block scales ("DeepSeek-V4 FP4 QAT"
+ * article, section 4.2: the scale array is re-encoded in E4M3, the 4-bit codes
+ * are widened to FP8 and the FP8 scale multiplies the FP8 data; "DeepSeek-V4"
+ * architecture article, section 6.3: lossless while the block scale ratio stays
+ * under a threshold).  E4M3 spans only 2^-9 .. 448, so the tensor carries one
+ * fp32 power of two in front:
+ *   E_max = max over blocks of (scale byte - 127); k = E_max - 6;
+ *   *tensor_scale = 2^k;  for block b, j = E_b - k (<= 6):
+ *   block_scales_e4m3[b] = E4M3 round-to-nearest-even of 2^j (exact for j >= -9;
+ *     2^-10 ties to 0);
+ *   values_e4m3[r, c] = E4M3 round-to-nearest-even of MAG(code) * block scale,
+ *     with the code's sign bit in bit 7 (the largest value is 6 * 2^6 = 384, so
+ *     nothing saturates); the dequantized element is that value * 2^k.
+ *   *n_inexact_blocks = number of blocks holding an element whose value * 2^k
+ *     differs from its MX value.  It is 0 whenever every block exponent is at
+ *     least E_max - 14 (a largest-to-smallest block scale ratio of at most 2^14).
+ * codes: [rows, k/2]; scales_e8m0: [rows, k/32]; values_e4m3: [rows, k] bytes;
+ * block_scales_e4m3: [rows, k/32] or NULL (not written); tensor_scale: 1 device
+ * float; n_inexact_blocks: 1 device int32.  Both are written by the call (they
+ * also serve as its counters while it runs).
+ * Errors: k % 32 != 0 -> FP4_ERR_SHAPE.
+ */
+int fp4_mx_dequant_fp8(const uint8_t* codes, const uint8_t* scales_e8m0, int64_t rows, int64_t k,
+                       uint8_t* values_e4m3, uint8_t* block_scales_e4m3, float* tensor_scale,
+                       int32_t* n_inexact_blocks, void* stream);
+
+/*
  * W4A8 GEMM: C[m, n] = sum_k A_hat[m, k] * B_hat[n, k] with fp32 accumulation,
  * A_hat the MXFP8 activations (a_codes8 [m, k] E4M3 bytes, a_scales [m, k/32])
  * and B_hat the MXFP4 weights (b_codes [n, k/2], b_scales [n, k/32]), both

@@ -124,6 +124,12 @@ def test_moe_rejections_and_workspace(F):
     assert call(ws_ptr=None) == WORKSPACE
     assert call(fmt=1) == INVALID                   # NV needs tensor scales
     assert call(tokens=0, ws_ptr=None, ws_bytes=0) == OK
+    # operands past the 32-bit tile offsets: 163840 tokens x top-8 at H=4096,
+    # I=8192 puts Q(h) at 5.4e9 bytes; NV's fp16 activations at 2^31 bytes
+    assert call(tokens=163840, hidden=4096, topk=8, E=64, inter=8192) == SHAPE
+    assert b"32-bit" in F.lib.fp4_last_error()
+    assert call(fmt=1, tokens=131072, hidden=8192, topk=1, E=8, inter=128, act=FAKE) == SHAPE
+    assert call(tokens=8, hidden=65536, topk=1, E=8, inter=32768) == SHAPE          # one expert slab of 2^31 bytes
 
 
 def test_w4a8_rejections(F):
@@ -167,3 +173,50 @@ def test_fake_quant_ste_and_kv_rejections(F):
     assert kv(FAKE, 4, 32, 32, FAKE + 2, FAKE, FAKE, 16, None) == ALIGN    # slots need 4-byte alignment
     assert kv(FAKE, 4, 32, 32, FAKE, FAKE, FAKE, -1, None) == INVALID
     assert kv(None, 0, 32, 32, None, None, None, 16, None) == OK
+
+
+def test_fp8_dequant_rejections(F):
+    d = F.lib.fp4_mx_dequant_fp8
+    assert d(FAKE, FAKE, 4, 48, FAKE, None, FAKE, FAKE, None) == SHAPE            # k % 32
+    assert d(FAKE, FAKE, 4, 64, FAKE, None, None, FAKE, None) == INVALID          # tensor scale
+    assert d(FAKE, FAKE, 4, 64, FAKE, None, FAKE, None, None) == INVALID          # count
+    assert d(FAKE, FAKE, 4, 64, MISALIGNED, None, FAKE, FAKE, None) == ALIGN
+    assert d(None, None, 0, 64, None, None, None, None, None) == OK
+
+
+def test_binding_rejects_what_the_c_side_would_misread(F):
+    """The Python wrappers check dtype, device, layout and operand agreement
+    before any pointer is passed (these calls never reach the library)."""
+    import torch
+    u8 = lambda *s: torch.zeros(s, dtype=torch.uint8)
+    x = torch.zeros((8, 64), dtype=torch.bfloat16)
+    with pytest.raises(TypeError, match="bfloat16"):
+        F.fp4_quantize_mx(x.float(), u8(8, 32), u8(8, 2))
+    with pytest.raises(ValueError, match="GPU"):
+        F.fp4_quantize_mx(x, u8(8, 32), u8(8, 2))
+    with pytest.raises(TypeError, match="int32"):
+        F.fp4_moe_grouped_gemm(F.FMT_MX, x, torch.zeros((8, 2), dtype=torch.int64), torch.zeros((8, 2)), 4, 128,
+                               u8(4, 256, 32), u8(4, 256, 2), u8(4, 64, 64), u8(4, 64, 4), x.clone(), u8(64))
+    with pytest.raises(TypeError, match="float32"):
+        F.fp4_moe_grouped_gemm(F.FMT_MX, x, torch.zeros((8, 2), dtype=torch.int32),
+                               torch.zeros((8, 2), dtype=torch.bfloat16), 4, 128, u8(4, 256, 32), u8(4, 256, 2),
+                               u8(4, 64, 64), u8(4, 64, 4), x.clone(), u8(64))
+    with pytest.raises(ValueError, match="contiguous"):
+        F.fp4_moe_grouped_gemm(F.FMT_MX, torch.zeros((8, 128), dtype=torch.bfloat16)[:, :64],
+                               torch.zeros((8, 2), dtype=torch.int32), torch.zeros((8, 2)), 4, 128, u8(4, 256, 32),
+                               u8(4, 256, 2), u8(4, 64, 64), u8(4, 64, 4), x.clone(), u8(64))
+    with pytest.raises(TypeError, match="uint8"):
+        F.fp4_gemm(F.FMT_MX, u8(8, 32), u8(8, 2), torch.zeros((8, 32), dtype=torch.int8), u8(8, 2),
+                   torch.zeros((8, 8)))
+
+
+def test_binding_checks_operand_shapes():
+    """Shape agreement is checked with the tensors' shapes alone (no device needed):
+    a B operand narrower than A's K would make the kernels read past it."""
+    import torch
+    import block_scaled_fp4_mx_amd as F
+    with pytest.raises(ValueError, match="b_codes"):
+        F._shape("fp4_gemm", "b_codes", torch.zeros((8, 16)), (8, 32), rows_at_least=True)
+    F._shape("fp4_gemm", "b_codes", torch.zeros((12, 32)), (8, 32), rows_at_least=True)
+    with pytest.raises(ValueError, match="w13_codes"):
+        F._shape("fp4_moe_grouped_gemm", "w13_codes", torch.zeros((4, 256, 16)), (4, 256, 32))
