@@ -196,3 +196,97 @@ def test_gemm_mx_skinny_streaming(m, n, k, dtype, pad):
     _assert_within(c, Cref, S)
     if pad:
         assert torch.isnan(buf[:, n:].float()).all()
+
+
+# ---------------------------------------------------------------- crafted blocks
+def _crafted_operands(seed, m, n, k, pairs, zero_p=0.1, sat_p=0.1, huge_zero=False):
+    """MX operands written directly as codes and scale bytes.  K block b gets
+    scale byte alpha_b in every A row and beta_b in every B row, cycling through
+    `pairs`, so the two extremes of a pair (e.g. 254 with 0, 1 with 253) put a
+    product's scale 2^(alpha + beta - 254) where the pair says while A's rows
+    mix bytes 0, 1, 253 and 254.  Some blocks are all zero codes (signed zeros
+    included), some saturated (every code +-6).  huge_zero: the zero blocks of
+    A carry byte 254 while B's block byte is 254 too (a scale product of 2^254
+    multiplying only zeros)."""
+    rng = np.random.default_rng(seed)
+    nb = k // 32
+    al = np.array([pairs[b % len(pairs)][0] for b in range(nb)], np.uint8)
+    be = np.array([pairs[b % len(pairs)][1] for b in range(nb)], np.uint8)
+
+    def side(rows, sc):
+        c4 = rng.integers(0, 16, (rows, k), dtype=np.uint8)
+        s = np.tile(sc, (rows, 1))
+        blk = c4.reshape(rows, nb, 32)
+        zero = rng.random((rows, nb)) < zero_p
+        sat = (rng.random((rows, nb)) < sat_p) & ~zero
+        blk[zero] = rng.choice(np.array([0, 8], np.uint8), (int(zero.sum()), 32))
+        blk[sat] = rng.choice(np.array([7, 15], np.uint8), (int(sat.sum()), 32))
+        return Q.pack_nibbles(blk.reshape(rows, k)), s, zero
+
+    ac, as_, az = side(m, al)
+    bc, bs, _ = side(n, be)
+    if huge_zero:
+        as_[az] = 254
+        bs[:, az.any(axis=0)] = 254
+    return (ac, as_), (bc, bs)
+
+
+_PAIRS = [(254, 0), (0, 254), (253, 1), (1, 253), (254, 3), (0, 250), (127, 127), (200, 60), (30, 221)]
+_SHAPES = [(37, 75, 288), (2048, 2048, 512), (48, 4096, 512)]     # fallback, 256x256 tile, skinny
+
+
+def _crafted_case(a, b, dtype):
+    at = tuple(torch.from_numpy(np.ascontiguousarray(t)).to(DEV) for t in a)
+    bt = tuple(torch.from_numpy(np.ascontiguousarray(t)).to(DEV) for t in b)
+    c = _run_gemm("mx", at, bt, dtype)
+    Cref, S = G.gemm_ref("mx", *a, *b)
+    return c, Cref, S
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("m,n,k", _SHAPES)
+def test_gemm_mx_crafted_extreme_scale_bytes(m, n, k, dtype):
+    """Scale bytes 0, 1, 253 and 254 mixed within each row (2^-127 is an fp32
+    subnormal, 2^127 the largest power of two), zero and saturated blocks, on
+    the fallback kernel, the 256x256 tile and the skinny kernel; every product
+    lies in fp32's normal range, so the usual bar holds."""
+    a, b = _crafted_operands(m + n + k, m, n, k, _PAIRS)
+    c, Cref, S = _crafted_case(a, b, dtype)
+    _assert_within(c, Cref, S)
+
+
+def test_gemm_mx_crafted_brute_force_fraction():
+    """A slice of the crafted case against exact Fraction dot products."""
+    a, b = _crafted_operands(5, 37, 75, 288, _PAIRS)
+    c, Cref, S = _crafted_case(a, b, torch.float32)
+    ex = G.gemm_exact_fraction("mx", a[0][:4], a[1][:4], b[0][:6], b[1][:6])
+    got = c.cpu().numpy()
+    for i in range(4):
+        for j in range(6):
+            assert abs(float(got[i, j]) - float(ex[i][j])) <= TOL * S[i, j]
+
+
+@pytest.mark.parametrize("m,n,k", _SHAPES)
+def test_gemm_mx_zero_blocks_under_huge_scales(m, n, k):
+    """Zero-code blocks whose scale product is 2^254 (beyond fp32) contribute
+    exactly zero: no inf * 0 reaches the accumulator."""
+    a, b = _crafted_operands(7 + m, m, n, k, [(120, 130), (127, 127)], zero_p=0.2, sat_p=0.05, huge_zero=True)
+    assert (a[1] == 254).any() and (b[1] == 254).any()
+    c, Cref, S = _crafted_case(a, b, torch.float32)
+    assert torch.isfinite(c).all()
+    _assert_within(c, Cref, S)
+
+
+@pytest.mark.parametrize("m,n,k", _SHAPES)
+def test_gemm_mx_results_near_fp32_limits(m, n, k):
+    """Outputs near the top of fp32 (block scale products 2^110 .. 2^111, sums
+    up to about 2^126) and near the bottom of its normal range (block scale
+    products 2^-119 .. 2^-117, single products down to 2^-121; a cancelling sum
+    can land among the subnormals, where 1e-5 * S, about 2^-126, is still far
+    above their spacing 2^-149): the bar holds there too."""
+    for pairs in ([(254, 111), (253, 110), (230, 130)], [(0, 136), (1, 134), (20, 117)]):
+        a, b = _crafted_operands(11 + k, m, n, k, pairs, zero_p=0.0, sat_p=0.3)
+        c, Cref, S = _crafted_case(a, b, torch.float32)
+        assert np.isfinite(Cref).all() and np.abs(Cref).max() < 2.0 ** 128
+        assert torch.isfinite(c).all()
+        _assert_within(c, Cref, S)

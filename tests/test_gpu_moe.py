@@ -10,8 +10,9 @@ import numpy as np
 import pytest
 
 import workloads as W
-from moe_check import (Case, calibrate_act_scales, check_down_stage, check_end_to_end, check_gate_up_stage,
+from moe_check import (DEV, Case, check_down_stage, check_end_to_end, check_gate_up_stage, device_weight_quant,
                        oracle_expect, oracle_expert_quant, run_gpu)
+from oracle import moe as M
 
 pytestmark = pytest.mark.gpu
 
@@ -28,10 +29,7 @@ def _small_case(fmt, seed, T, H, I, E, topk, ids=None, weights=None):
     wts = m.weights if weights is None else weights
     experts = {e: _expert(seed, e, H, I) for e in range(E)}
     case = Case(fmt, W.bf16_bits(m.X), ids, wts, E, H, I, experts)
-    eq = oracle_expert_quant(case)
-    if fmt == "nv":
-        case.act_st = calibrate_act_scales(case, eq, np.arange(case.T))
-    return case, eq
+    return case, oracle_expert_quant(case)
 
 
 def _all_checks(case, exp, fill=False):
@@ -45,14 +43,14 @@ def _all_checks(case, exp, fill=False):
 @pytest.mark.parametrize("fmt", ["mx", "nv"])
 def test_moe_small(fmt):
     case, eq = _small_case(fmt, 100, 40, 256, 256, 8, 3)
-    _all_checks(case, oracle_expect(case, np.arange(case.T), eq))
+    _all_checks(case, oracle_expect(case, np.arange(case.T), eq, calibrate_h=True))
 
 
 @pytest.mark.parametrize("fmt", ["mx", "nv"])
 def test_moe_multi_tile_segments(fmt):
     """Experts with more than one 128-row tile and ragged last tiles."""
     case, eq = _small_case(fmt, 101, 300, 128, 128, 4, 2)
-    _all_checks(case, oracle_expect(case, np.arange(case.T), eq))
+    _all_checks(case, oracle_expect(case, np.arange(case.T), eq, calibrate_h=True))
 
 
 def test_moe_tiled_mx_segments():
@@ -62,7 +60,7 @@ def test_moe_tiled_mx_segments():
     case, eq = _small_case("mx", 104, 700, 512, 512, 4, 2)
     counts = np.bincount(case.ids.ravel(), minlength=4)
     assert counts.max() > 256 and ((counts % 256) <= 128).any()
-    _all_checks(case, oracle_expect(case, np.arange(case.T), eq))
+    _all_checks(case, oracle_expect(case, np.arange(case.T), eq, calibrate_h=True))
 
 
 def test_moe_tiled_nv_segments():
@@ -74,7 +72,7 @@ def test_moe_tiled_nv_segments():
     counts = np.bincount(case.ids.ravel(), minlength=4)
     last = counts % 128
     assert counts.max() > 128 and len(set((last + 15) // 16)) > 2 and ((last > 0) & (last <= 64)).any()
-    _all_checks(case, oracle_expect(case, np.arange(case.T), eq))
+    _all_checks(case, oracle_expect(case, np.arange(case.T), eq, calibrate_h=True))
 
 
 def test_moe_decode_nv_segments():
@@ -84,14 +82,14 @@ def test_moe_decode_nv_segments():
     case, eq = _small_case("nv", 106, 100, 1024, 768, 8, 6)
     counts = np.bincount(case.ids.ravel(), minlength=8)
     assert counts.max() > 64 and (counts % 32 != 0).any()
-    _all_checks(case, oracle_expect(case, np.arange(case.T), eq))
+    _all_checks(case, oracle_expect(case, np.arange(case.T), eq, calibrate_h=True))
 
 
 def test_moe_single_expert_topk1():
     T, H, I, E = 33, 128, 256, 5
     ids = np.full((T, 1), 3, np.int32)
     case, eq = _small_case("mx", 102, T, H, I, E, 1, ids=ids, weights=np.ones((T, 1), np.float32))
-    _all_checks(case, oracle_expect(case, np.arange(T), eq))
+    _all_checks(case, oracle_expect(case, np.arange(T), eq, calibrate_h=True))
 
 
 def test_moe_ids_outside_range_route_nowhere():
@@ -101,40 +99,71 @@ def test_moe_ids_outside_range_route_nowhere():
     ids[::5, 1] = -1
     ids[::7, 2] = E + 3
     case, eq = _small_case("mx", 103, T, H, I, E, k, ids=ids)
-    _all_checks(case, oracle_expect(case, np.arange(T), eq))
+    _all_checks(case, oracle_expect(case, np.arange(T), eq, calibrate_h=True))
 
 
-def _full_case(workload, fmt, tokens=None, sample=(0,)):
+def _sample_tokens(ids, E):
+    """Tokens whose slots reach the tiles most likely to go wrong: one slot of
+    every expert with at most 4 routed slots (cold experts, nearly empty
+    tiles), the first and the last slot of the four busiest experts (the last
+    one is the last row of the expert's ragged last tile); checked on the host."""
+    topk = ids.shape[1]
+    counts, offsets, perm = M.routing_metadata(ids, E)
+    cold = np.nonzero((counts > 0) & (counts <= 4))[0]
+    hot = np.argsort(-counts, kind="stable")[:4]
+    toks = {int(perm[offsets[e]]) // topk for e in cold}
+    for e in hot:
+        toks |= {int(perm[offsets[e]]) // topk, int(perm[offsets[e + 1] - 1]) // topk}
+    toks = np.array(sorted(toks))
+    reached = set(int(v) for v in ids[toks].ravel())
+    assert all(int(e) in reached for e in cold)
+    last = {int(perm[offsets[e + 1] - 1]) for e in hot}
+    slots = set((toks[:, None] * topk + np.arange(topk)[None, :]).ravel().tolist())
+    assert last <= slots
+    return toks, len(cold)
+
+
+def _full_case(workload, fmt, tokens=None, all_tokens=False):
+    """The full-size workload with every active expert's weights drawn on the
+    device (seeded); the oracle reads back the exact bf16 of the experts it checks."""
     m = W.moe_workload(workload, tokens)
-    sample = np.asarray(sample)
-    need = sorted(set(int(e) for e in m.ids[sample].ravel()))
-    experts = {e: _expert(1000 + workload, e, m.hidden, m.inter) for e in need}
-    case = Case(fmt, W.bf16_bits(m.X), m.ids, m.weights, m.num_experts, m.hidden, m.inter, experts)
-    eq = oracle_expert_quant(case)
-    if fmt == "nv":
-        case.act_st = calibrate_act_scales(case, eq, sample)
-    return case, eq, sample
-
-
-@pytest.mark.timeout(400)
-def test_moe_workload4_full_size_sampled():
-    """MoE at hidden 4096 (8192 tokens, 384 experts, top-6, MXFP4) in the launch
-    the benchmark times: routing checked whole, two tokens checked per stage."""
-    case, eq, sample = _full_case(4, "mx", sample=(5, 4321))
-    _all_checks(case, oracle_expect(case, sample, eq), fill=True)
-
-
-@pytest.mark.timeout(400)
-def test_moe_workload5_decode_sampled():
-    """NVFP4 MoE at hidden 7168, decode batch of 64 tokens; one token per stage."""
-    case, eq, sample = _full_case(5, "nv", sample=(17,))
-    _all_checks(case, oracle_expect(case, sample, eq), fill=True)
+    active = set(int(v) for v in np.unique(m.ids))
+    wdev = {e: (a, b) for e, a, b in W.expert_weights_device(1000 + workload, m.num_experts, m.hidden, m.inter, DEV)
+            if e in active}
+    case = Case(fmt, W.bf16_bits(m.X), m.ids, m.weights, m.num_experts, m.hidden, m.inter, {}, wdev=wdev)
+    if all_tokens:
+        sample, ncold = np.arange(m.X.shape[0]), -1
+    else:
+        sample, ncold = _sample_tokens(m.ids, m.num_experts)
+    exp = oracle_expect(case, sample, device_weight_quant(case), calibrate_h=fmt == "nv")
+    print(f"workload {workload} {fmt}: {len(sample)} tokens checked, {ncold} cold experts reached, "
+          f"{len(set(int(v) for v in m.ids[sample].ravel()))} experts")
+    return case, exp
 
 
 @pytest.mark.timeout(600)
+def test_moe_workload4_full_size_sampled():
+    """MoE at hidden 4096 (8192 tokens, 384 experts, top-6, MXFP4) in the launch
+    the benchmark times: routing checked whole; every stage checked on the
+    tokens that reach each cold expert and the busiest experts' first and last
+    tile rows."""
+    case, exp = _full_case(4, "mx")
+    _all_checks(case, exp)
+
+
+@pytest.mark.timeout(600)
+def test_moe_workload5_decode_all_tokens():
+    """NVFP4 MoE at hidden 7168, decode batch of 64 tokens: every token checked
+    at every stage."""
+    case, exp = _full_case(5, "nv", all_tokens=True)
+    _all_checks(case, exp)
+
+
+@pytest.mark.timeout(900)
 def test_moe_workload5_prefill_sampled():
     """NVFP4 MoE at hidden 7168 on a prefill batch of 16384 tokens (98,304
     routed slots, the 128-row wide NV tiles), in the launch the benchmark
-    times: routing checked whole, two tokens checked per stage."""
-    case, eq, sample = _full_case(5, "nv", tokens=16384, sample=(3, 12345))
-    _all_checks(case, oracle_expect(case, sample, eq), fill=True)
+    times: routing checked whole; every stage checked on the tokens that reach
+    each cold expert and the busiest experts' first and last tile rows."""
+    case, exp = _full_case(5, "nv", tokens=16384)
+    _all_checks(case, exp)

@@ -10,6 +10,7 @@ import block_scaled_fp4_mx_amd as F
 import workloads as W
 from oracle import formats as OF
 from oracle import quant as Q
+import bf16_patterns as BP
 from gpu_util import (DEV, chunked, describe_mismatch, dev_bf16, empty_u8, host_u8, quantize_mx,
                       quantize_nv)
 
@@ -86,30 +87,52 @@ def test_mx_quantize_strided_rows():
     assert np.array_equal(host_u8(s), es) and np.array_equal(host_u8(c), ec)
 
 
+def _rows_of(blocks, per_row):
+    pad = (-blocks.shape[0]) % per_row
+    blocks = np.concatenate([blocks, np.zeros((pad, blocks.shape[1]), np.uint16)])
+    return blocks.reshape(-1, per_row * blocks.shape[1])
+
+
 def test_mx_quantize_exhaustive_bf16_patterns():
-    """Every finite bf16 pattern, placed in blocks whose amax fixes a range of
-    block exponents (each block: one anchor value and 31 patterns)."""
-    pats = np.arange(1 << 16, dtype=np.uint32)
-    pats = pats[((pats >> 7) & 0xFF) != 0xFF].astype(np.uint16)
-    mags = OF.bf16_bits_to_f64(pats & 0x7FFF)
-    rows = []
-    rows.append(np.zeros((1, 32), np.uint16))
-    for anchor_exp in range(-133, 128, 3):
-        anchor = 1.5 * 2.0 ** anchor_exp
-        sel = pats[mags <= anchor]
-        if len(sel) == 0:
-            continue
-        sel = sel[:: max(1, len(sel) // (31 * 64))][: 31 * 64]
-        n = len(sel) // 31
-        if n == 0:
-            continue
-        blk = sel[: n * 31].reshape(n, 31)
-        a = W.bf16_bits(W.to_bf16(np.full((n, 1), anchor)))
-        rows.append(np.concatenate([a, blk], axis=1))
-    bits = np.concatenate(rows).reshape(-1, 32)
-    pad = (-bits.shape[0]) % 4
-    bits = np.concatenate([bits, np.zeros((pad, 32), np.uint16)]).reshape(-1, 128)
-    _check_mx(bits)
+    """All 65,280 finite bf16 patterns: as their own block maximum (sorted
+    blocks), 0, 1, 2, 3, 4, 5 and 8 binades below the block maximum (every
+    pattern whose binade leaves room for the offset), and in random blocks.
+    The offsets run through normal, subnormal and clamped block exponents."""
+    sb, rb = BP.sorted_blocks(32), BP.random_blocks(32, 7)
+    ob, _ = BP.offset_blocks(32, [0, 1, 2, 3, 4, 5, 8])
+    assert BP.covered(sb) == BP.covered(rb) == BP.covered(ob[:, 1:]) == BP.N_FINITE
+    _check_mx(_rows_of(np.concatenate([sb, rb, ob]), 128))
+
+
+def test_nv_quantize_exhaustive_bf16_patterns():
+    """All 65,280 finite bf16 patterns in 16-element groups 0, 1, 2, 3, 4 and 6
+    binades below the group maximum, under supplied tensor scales that put the
+    group scale amax / (6 s_t) in E4M3's normal range, its subnormal range, and
+    past 448 (saturated); plus every pattern as its own group maximum and in
+    random groups under a computed tensor scale."""
+    ob, ea = BP.offset_blocks(16, [0, 1, 2, 3, 4, 6])
+    assert BP.covered(ob[:, 1:]) == BP.N_FINITE
+    calls = []
+    for f in np.unique(ea):
+        grp = ob[ea == f]
+        a = float(OF.bf16_bits_to_f64(grp[:1, 0])[0])
+        lg = int(np.frexp(a)[1]) - 1
+        for shift in (-4, 6, -12):                       # normal, subnormal, saturated group scales
+            s_t = float(np.float32(np.ldexp(1.0, int(np.clip(lg + shift, -149, 127)))))
+            calls.append((_rows_of(grp, 8), s_t))
+    outs = []
+    for bits, s_t in calls:
+        x = dev_bf16(bits)
+        outs.append((bits, s_t) + quantize_nv(x, s_t))
+    torch.cuda.synchronize()
+    bad = []
+    for bits, s_t, c, s, ts in outs:
+        ec, es, _ = Q.nv_quantize(bits, s_t=s_t)
+        if not (np.array_equal(host_u8(s), es) and np.array_equal(host_u8(c), ec)):
+            bad.append((s_t, describe_mismatch("nv scales", host_u8(s), es), describe_mismatch("nv codes", host_u8(c), ec)))
+    assert not bad, f"{len(bad)} of {len(outs)} calls differ; first: {bad[0]}"
+    sb, rb = BP.sorted_blocks(16), BP.random_blocks(16, 8)
+    _check_nv(_rows_of(np.concatenate([sb, rb]), 64))
 
 
 @pytest.mark.parametrize("which", ["A", "W"])

@@ -25,6 +25,7 @@ import workloads as W
 from oracle import formats as OF
 from oracle import gemm as G
 from oracle import quant as Q
+import bf16_patterns as BP
 from conftest import parse_float, read_records
 from gpu_util import DEV, chunked, describe_mismatch, dev_bf16, empty_u8, host_u8, quantize_mx
 
@@ -113,26 +114,16 @@ def test_mxfp8_quantize_strided_rows():
 
 
 def test_mxfp8_quantize_exhaustive_bf16_patterns():
-    """Every finite bf16 pattern, in blocks whose anchor fixes a range of block
-    exponents (each block: one anchor value and 31 patterns at most its size)."""
-    pats = np.arange(1 << 16, dtype=np.uint32)
-    pats = pats[((pats >> 7) & 0xFF) != 0xFF].astype(np.uint16)
-    mags = OF.bf16_bits_to_f64(pats & 0x7FFF)
-    rows = [np.zeros((1, 32), np.uint16)]
-    for anchor_exp in range(-133, 128, 2):
-        anchor = 1.75 * 2.0 ** anchor_exp
-        sel = pats[mags <= anchor]
-        if len(sel) == 0:
-            continue
-        sel = sel[:: max(1, len(sel) // (31 * 64))][: 31 * 64]
-        n = len(sel) // 31
-        if n == 0:
-            continue
-        a = W.bf16_bits(W.to_bf16(np.full((n, 1), anchor)))
-        rows.append(np.concatenate([a, sel[: n * 31].reshape(n, 31)], axis=1))
-    bits = np.concatenate(rows).reshape(-1, 32)
-    pad = (-bits.shape[0]) % 4
-    _check_mxfp8(np.concatenate([bits, np.zeros((pad, 32), np.uint16)]).reshape(-1, 128))
+    """All 65,280 finite bf16 patterns: as their own block maximum, 0 to 18 and
+    20 binades below the block maximum (every offset at which an element can
+    still round to a nonzero E4M3 subnormal, and one past it), and in random
+    blocks; the offsets run through normal, subnormal and clamped block exponents."""
+    sb, rb = BP.sorted_blocks(32), BP.random_blocks(32, 9)
+    ob, _ = BP.offset_blocks(32, list(range(19)) + [20])
+    assert BP.covered(sb) == BP.covered(rb) == BP.covered(ob[:, 1:]) == BP.N_FINITE
+    blocks = np.concatenate([sb, rb, ob])
+    pad = (-blocks.shape[0]) % 128
+    _check_mxfp8(np.concatenate([blocks, np.zeros((pad, 32), np.uint16)]).reshape(-1, 4096))
 
 
 def test_mx_to_mxfp8_every_code_byte():
