@@ -199,15 +199,15 @@ def test_gemm_mx_skinny_streaming(m, n, k, dtype, pad):
 
 
 # ---------------------------------------------------------------- crafted blocks
-def _crafted_operands(seed, m, n, k, pairs, zero_p=0.1, sat_p=0.1, huge_zero=False):
+def _crafted_operands(seed, m, n, k, pairs, zero_p=0.1, sat_p=0.1, huge_zero_blocks=()):
     """MX operands written directly as codes and scale bytes.  K block b gets
     scale byte alpha_b in every A row and beta_b in every B row, cycling through
     `pairs`, so the two extremes of a pair (e.g. 254 with 0, 1 with 253) put a
     product's scale 2^(alpha + beta - 254) where the pair says while A's rows
     mix bytes 0, 1, 253 and 254.  Some blocks are all zero codes (signed zeros
-    included), some saturated (every code +-6).  huge_zero: the zero blocks of
-    A carry byte 254 while B's block byte is 254 too (a scale product of 2^254
-    multiplying only zeros)."""
+    included), some saturated (every code +-6).  huge_zero_blocks: K blocks in
+    which every A row holds only zero codes under byte 254 while B's rows hold
+    nonzero codes under byte 254 (a scale product of 2^254 multiplying zeros)."""
     rng = np.random.default_rng(seed)
     nb = k // 32
     al = np.array([pairs[b % len(pairs)][0] for b in range(nb)], np.uint8)
@@ -221,14 +221,15 @@ def _crafted_operands(seed, m, n, k, pairs, zero_p=0.1, sat_p=0.1, huge_zero=Fal
         sat = (rng.random((rows, nb)) < sat_p) & ~zero
         blk[zero] = rng.choice(np.array([0, 8], np.uint8), (int(zero.sum()), 32))
         blk[sat] = rng.choice(np.array([7, 15], np.uint8), (int(sat.sum()), 32))
-        return Q.pack_nibbles(blk.reshape(rows, k)), s, zero
+        return blk, s
 
-    ac, as_, az = side(m, al)
-    bc, bs, _ = side(n, be)
-    if huge_zero:
-        as_[az] = 254
-        bs[:, az.any(axis=0)] = 254
-    return (ac, as_), (bc, bs)
+    ab, as_ = side(m, al)
+    bb, bs = side(n, be)
+    for b in huge_zero_blocks:
+        ab[:, b] = rng.choice(np.array([0, 8], np.uint8), (m, 32))
+        bb[:, b] = rng.choice(np.array([1, 7, 9, 15], np.uint8), (n, 32))
+        as_[:, b] = bs[:, b] = 254
+    return (Q.pack_nibbles(ab.reshape(m, k)), as_), (Q.pack_nibbles(bb.reshape(n, k)), bs)
 
 
 _PAIRS = [(254, 0), (0, 254), (253, 1), (1, 253), (254, 3), (0, 250), (127, 127), (200, 60), (30, 221)]
@@ -268,13 +269,33 @@ def test_gemm_mx_crafted_brute_force_fraction():
 
 @pytest.mark.parametrize("m,n,k", _SHAPES)
 def test_gemm_mx_zero_blocks_under_huge_scales(m, n, k):
-    """Zero-code blocks whose scale product is 2^254 (beyond fp32) contribute
-    exactly zero: no inf * 0 reaches the accumulator."""
-    a, b = _crafted_operands(7 + m, m, n, k, [(120, 130), (127, 127)], zero_p=0.2, sat_p=0.05, huge_zero=True)
-    assert (a[1] == 254).any() and (b[1] == 254).any()
+    """K blocks where A holds only (signed) zero codes under byte 254 and B
+    nonzero codes under byte 254: a scale product of 2^254, beyond fp32, times
+    zeros contributes exactly zero (no inf * 0 reaches the accumulator)."""
+    a, b = _crafted_operands(7 + m, m, n, k, [(120, 130), (127, 127)], zero_p=0.1, sat_p=0.05,
+                             huge_zero_blocks=(0, 3, k // 32 - 1))
     c, Cref, S = _crafted_case(a, b, torch.float32)
     assert torch.isfinite(c).all()
     _assert_within(c, Cref, S)
+
+
+@pytest.mark.parametrize("m,n,k", _SHAPES)
+def test_gemm_mx_results_beyond_fp32_are_infinite(m, n, k):
+    """Exact results beyond fp32's range come out as the infinity of their sign,
+    as fp32 rounding defines (bf16 output likewise).  Every A row holds codes of
+    one sign and every B code is positive, so partial sums never change sign
+    (with mixed signs, a partial sum that overflows can make inf - inf)."""
+    rng = np.random.default_rng(17 + m)
+    sign = np.where(rng.random((m, 1)) < 0.5, 8, 0).astype(np.uint8)
+    a4 = rng.choice(np.array([5, 6, 7], np.uint8), (m, k)) | sign
+    b4 = rng.choice(np.array([4, 5, 6, 7], np.uint8), (n, k))
+    a = (Q.pack_nibbles(a4), np.full((m, k // 32), 254, np.uint8))
+    b = (Q.pack_nibbles(b4), np.full((n, k // 32), 125, np.uint8))      # products of 6 * 2^125 and up
+    for dtype in (torch.float32, torch.bfloat16):
+        c, Cref, S = _crafted_case(a, b, dtype)
+        assert (np.abs(Cref) >= 2.0 ** 129).all()
+        got = c.float().cpu().numpy()
+        assert np.array_equal(got, np.copysign(np.inf, Cref))
 
 
 @pytest.mark.parametrize("m,n,k", _SHAPES)
