@@ -15,7 +15,7 @@ import torch
 
 __all__ = [
     "lib", "Fp4Error", "FMT_MX", "FMT_NV", "DT_BF16", "DT_F32",
-    "fp4_quantize_mx", "fp4_quantize_nv", "fp4_quantize_nv_workspace_bytes", "fp4_remap_mx_to_nv",
+    "fp4_quantize_mx", "fp4_quantize_nv", "fp4_quantize_nv_workspace_bytes", "fp4_quantize_nv_noalloc", "fp4_remap_mx_to_nv",
     "fp4_dequant", "fp4_gemm", "fp4_quantize_mxfp8", "fp4_mx_to_mxfp8", "fp4_mx_dequant_fp8", "fp4_gemm_w4a8", "fp4_fake_quant",
     "fp4_ste_backward", "fp4_kv_append_mx", "fp4_moe_grouped_gemm", "fp4_moe_workspace_bytes", "MoeDebug",
     "fp4_abi_version", "LIB_PATH",
@@ -43,6 +43,7 @@ _SIGS = {
     "fp4_quantize_mx": (_i32, [_vp, _i64, _i64, _i64, _vp, _vp, _vp]),
     "fp4_quantize_nv": (_i32, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _i32, _vp, _sz, _vp]),
     "fp4_quantize_nv_workspace_bytes": (_sz, [_i64, _i64]),
+    "fp4_quantize_nv_noalloc": (_i32, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _i32, _vp]),
     "fp4_remap_mx_to_nv": (_i32, [_vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp]),
     "fp4_dequant": (_i32, [_i32, _vp, _vp, _vp, _i64, _i64, _vp, _i32, _i64, _vp]),
     "fp4_gemm": (_i32, [_i32, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _i32, _i64, _vp]),
@@ -182,6 +183,22 @@ def fp4_quantize_nv(x, codes, scales, tensor_scale, tensor_scale_is_input=False,
     _check("fp4_quantize_nv", lib.fp4_quantize_nv(_ptr(x), rows, k, ld_x, _ptr(codes), _ptr(scales),
                                                   _ptr(tensor_scale), int(bool(tensor_scale_is_input)),
                                                   _ptr(workspace), wsb, _stream(stream)))
+
+
+def fp4_quantize_nv_noalloc(x, codes, scales, tensor_scale, tensor_scale_is_input=False, rows=None, k=None,
+                            ld_x=None, stream=None):
+    rows = x.shape[0] if rows is None else rows
+    k = x.shape[1] if k is None else k
+    ld_x = x.stride(0) if ld_x is None else ld_x
+    fn = "fp4_quantize_nv_noalloc"
+    a = _Args(fn)
+    a("x", x, _BF16, dense=False)
+    a("codes", codes, _U8)
+    a("scales", scales, _U8)
+    a("tensor_scale", tensor_scale, _F32)
+    a.on_device()
+    _check(fn, lib.fp4_quantize_nv_noalloc(_ptr(x), rows, k, ld_x, _ptr(codes), _ptr(scales), _ptr(tensor_scale),
+                                           int(bool(tensor_scale_is_input)), _stream(stream)))
 
 
 def fp4_remap_mx_to_nv(codes, scales_e8m0, scales_e4m3, tensor_scale, n_inexact, rows=None, k=None, stream=None):

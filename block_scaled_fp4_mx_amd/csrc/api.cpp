@@ -117,6 +117,27 @@ int fp4_quantize_nv(const void* x_bf16, int64_t rows, int64_t k, int64_t ld_x, u
                       "fp4_quantize_nv launch");
 }
 
+int fp4_quantize_nv_noalloc(const void* x_bf16, int64_t rows, int64_t k, int64_t ld_x, uint8_t* codes,
+                            uint8_t* scales, float* tensor_scale, int tensor_scale_is_input, void* stream) {
+    FP4_REQUIRE(rows >= 0 && k >= 0, FP4_ERR_INVALID, "negative size rows=%lld k=%lld", (long long)rows, (long long)k);
+    FP4_REQUIRE(k % 16 == 0, FP4_ERR_SHAPE, "k=%lld is not a multiple of 16", (long long)k);
+    if (rows == 0 || k == 0) return ok();
+    FP4_PTR(x_bf16);
+    FP4_PTR(codes);
+    FP4_PTR(scales);
+    FP4_SCALAR_PTR(tensor_scale);
+    if (int e = check_ld(ld_x, k, "ld_x")) return e;
+    // The partial maxima need one word per pass-1 workgroup; the grid is capped
+    // so that every shape fits the static array.
+    FP4_REQUIRE(nv_ws_bytes() <= fp4::nv_scratch_bytes(), FP4_ERR_WORKSPACE,
+                "the NV quantize needs %zu bytes of scratch, the static array holds %zu", nv_ws_bytes(),
+                fp4::nv_scratch_bytes());
+    return hip_status(fp4::launch_quantize_nv_noalloc(static_cast<const uint16_t*>(x_bf16), rows, k, ld_x, codes,
+                                                      scales, tensor_scale, tensor_scale_is_input != 0,
+                                                      static_cast<hipStream_t>(stream)),
+                      "fp4_quantize_nv_noalloc launch");
+}
+
 int fp4_remap_mx_to_nv(const uint8_t* codes, const uint8_t* scales_e8m0, int64_t rows, int64_t k,
                        uint8_t* scales_e4m3, float* tensor_scale, int32_t* n_inexact_blocks, void* stream) {
     FP4_REQUIRE(rows >= 0 && k >= 0, FP4_ERR_INVALID, "negative size rows=%lld k=%lld", (long long)rows, (long long)k);

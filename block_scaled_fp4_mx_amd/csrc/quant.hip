@@ -6,6 +6,8 @@
 // contiguous input per instruction.  An MX block (32 elements) spans 4 adjacent
 // lanes and an NV group (16 elements) 2 lanes; the block/group amax is
 // combined across those lanes with DPP quad permutes (no LDS traffic).
+#include <mutex>
+
 #include "quant_device.h"
 
 namespace fp4 {
@@ -706,6 +708,52 @@ hipError_t launch_quantize_nv(const uint16_t* x, int64_t rows, int64_t k, int64_
     else
         nv_quantize_kernel<false><<<gq, kThreads, 0, s>>>(x, rows, k, ldx, codes, scales, ts, amax_ws, npart);
     return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ allocation-free NV quantize
+// Scratch of the NV quantize for callers that cannot allocate: the pass-1
+// partial maxima of the tensor amax (one word per pass-1 workgroup, at most
+// kNvAmaxBlocks).  Each GPU holds its own copy of this array for the life of
+// the process; host code reaches it only through the address that
+// hipGetSymbolAddress returns for the current device (the array's name is a
+// host-side stand-in, not a device address).  Pass 1 writes every word that
+// pass 2 reads, so nothing needs clearing between calls; calls that overlap
+// in time on one GPU share the array and race.
+constexpr int kNvScratchWords = 1024;
+static_assert(kNvAmaxBlocks <= kNvScratchWords, "pass 1 writes at most kNvAmaxBlocks partial maxima");
+static __device__ __align__(256) uint32_t scratch[kNvScratchWords];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static uint32_t* g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch address on the current device (looked up once per device).
+static hipError_t nv_scratch(uint32_t** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = static_cast<uint32_t*>(p);
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
+size_t nv_scratch_bytes() { return sizeof(uint32_t) * kNvScratchWords; }
+
+hipError_t launch_quantize_nv_noalloc(const uint16_t* x, int64_t rows, int64_t k, int64_t ldx, uint8_t* codes,
+                                      uint8_t* scales, float* ts, bool ts_is_input, hipStream_t s) {
+    uint32_t* ws = nullptr;
+    if (!ts_is_input) {
+        const hipError_t e = nv_scratch(&ws);
+        if (e != hipSuccess) return e;
+    }
+    return launch_quantize_nv(x, rows, k, ldx, codes, scales, ts, ts_is_input, ws, s);
 }
 
 hipError_t launch_kv_append(const uint16_t* x, int64_t tokens, int64_t d, int64_t ldx, const int32_t* slots,

@@ -101,6 +101,23 @@ int fp4_quantize_nv(const void* x_bf16, int64_t rows, int64_t k, int64_t ld_x,
 size_t fp4_quantize_nv_workspace_bytes(int64_t rows, int64_t k);
 
 /*
+ * fp4_quantize_nv for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same operation, arguments and results as fp4_quantize_nv without the
+ * workspace.  The tensor-amax partial maxima go to a static device array of
+ * the library (4 KiB per GPU, held until the process ends); the call allocates
+ * nothing.  Every call on a GPU shares that GPU's array, so calls that overlap
+ * in time on one GPU (different streams or threads) race and must be ordered
+ * by the caller.  The array's size covers every shape; FP4_ERR_WORKSPACE
+ * reports a library built with a smaller one.  A HIP error in looking up the
+ * array's address on the current device returns FP4_ERR_HIP.
+ * Errors: as fp4_quantize_nv.
+ */
+int fp4_quantize_nv_noalloc(const void* x_bf16, int64_t rows, int64_t k, int64_t ld_x,
+                            uint8_t* codes, uint8_t* scales, float* tensor_scale,
+                            int tensor_scale_is_input, void* stream);
+
+/*
  * Lossless MXFP4 -> NVFP4 scale remap (explainer, section 1: NVFP4's finer
  * 16-element scale layout can re-express MXFP4 weights block by block without
  * loss; section 6: the conversion script's E2M1 -> E4M3 remap).
