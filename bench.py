@@ -42,7 +42,8 @@ step time (algorithmic work per launch over its event-measured duration) and
 rocprofv3 FETCH_SIZE / WRITE_SIZE counters recorded in profiles/traffic.json
 (written by profile_counters.sh), scaled by what the same counters read for a
 plain copy of known size; it is null when the kernel sources changed since.
-`cpu_baseline` times the CPU oracle on the whole GEMM workload.
+`cpu_baseline` times the CPU oracle on the whole GEMM workload (its
+`per_workload` list: every workload, the MoE ones on bounded token samples).
 """
 from __future__ import annotations
 
@@ -174,6 +175,10 @@ def main():
     rem_ts = torch.zeros(1, dtype=torch.float32, device=dev)
     rem_n = torch.zeros(1, dtype=torch.int32, device=dev)
     deq = torch.empty((4096, 4096), dtype=torch.bfloat16, device=dev)
+    fp8_v = torch.empty((4096, 4096), dtype=torch.uint8, device=dev)
+    fp8_s = torch.empty((4096, 4096 // 32), dtype=torch.uint8, device=dev)
+    fp8_ts = torch.zeros(1, dtype=torch.float32, device=dev)
+    fp8_n = torch.zeros(1, dtype=torch.int32, device=dev)
     fq_out = torch.empty((4096, 4096), dtype=torch.bfloat16, device=dev)
     masters = rot_copies(torch.zeros((4096, 4096), dtype=torch.float32, device=dev), 4096 * 4096 * 4)
     W2mx_rot = []
@@ -243,7 +248,11 @@ def main():
               M2a * NVB, "2.5625 B/elem (calibrated s_t: one pass)", "nv_quantize_kernel"),
         Stage("remap_W", lambda: F.fp4_remap_mx_to_nv(cur(W2mx_rot)[0], cur(W2mx_rot)[1], rem_s, rem_ts, rem_n),
               "hbm", M2 * (1 / 32 + 1 / 16), "0.09375 B/elem (scale bytes in and out)",
-              "remap_max_kernel + remap_kernel"),
+              "scale_max_kernel + remap_kernel"),
+        Stage("dequant_fp8_W", lambda: F.fp4_mx_dequant_fp8(cur(W2mx_rot)[0], cur(W2mx_rot)[1], fp8_v, fp8_ts, fp8_n,
+                                                            fp8_s), "hbm", M2 * (0.5 + 1 / 32 + 1 + 1 / 32),
+              "1.5625 B/elem (codes + UE8M0 scale in, E4M3 value + E4M3 block scale out)",
+              "scale_max_kernel + fp8_dequant_kernel"),
         Stage("dequant_mx_W", lambda: F.fp4_dequant(F.FMT_MX, cur(W2mx_rot)[0], cur(W2mx_rot)[1], None, deq), "hbm",
               M2 * (0.5 + 1 / 32 + 2), "2.53125 B/elem (codes + scale in, bf16 out)", "dequant_kernel"),
         Stage("fake_quant_mx_W", lambda: F.fp4_fake_quant(F.FMT_MX, cur(W2s), fq_out), "hbm", M2 * 4.0,
@@ -369,9 +378,13 @@ def main():
         rooflines[s.name] = e
     if traffic:
         for _, name, e in kernel_rows:
-            t = traffic["kernels"].get(name)
+            t = traffic.get("kernels", {}).get(name)
             if t is not None:
                 e["traffic"] = t["bytes_per_launch"]
+            mf = traffic.get("mfma", {}).get(name)
+            if mf is not None:
+                e["mfma_busy"] = mf["mfma_busy"]
+                e["lds_bank_conflicts_per_access"] = mf["lds_bank_conflicts_per_access"]
 
     dom_ms, dom_name, dom = max(kernel_rows, key=lambda r: r[0])
     comps = {}
@@ -396,7 +409,7 @@ def main():
         comps["gemm_nv_tflops"] = rooflines["gemm_nv_4096"]["achieved"]
         comps["gemm_nv_frac_16bit_peak"] = rooflines["gemm_nv_4096"]["frac"]
     for n in ("quantize_mx_W", "quantize_mx_A", "quantize_nv_W", "quantize_nv_A", "quantize_nv_A_calibrated",
-              "gemm_quantize_A", "gemm_quantize_A_mxfp8", "fake_quant_mx_W", "fake_quant_nv_W", "ste_backward_W",
+              "remap_W", "dequant_mx_W", "dequant_fp8_W", "gemm_quantize_A", "gemm_quantize_A_mxfp8", "fake_quant_mx_W", "fake_quant_nv_W", "ste_backward_W",
               "kv_append_prefill16384", "indexer_scores_64x32768"):
         if n in rooflines:
             comps[n + "_GBps"] = rooflines[n]["achieved"]
@@ -430,6 +443,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": "W4A4 MXFP4 GEMM M=N=K=4096 (bf16 out, fp32 accumulate) for value; per step also "
                                "MX/NV quantize of linear 4096x4096 W and 2048x4096 A, MX->NV remap, MX dequant, "
+                               "MX -> FP8 dequant, "
                                "MX/NV fake-quant of W and its STE backward, MXFP4 KV-cache append (16384 x 512) "
                                "and FP4 indexer scores (64 x 32768 x 512), "
                                "NVFP4 and W4A8 (MXFP8 x MXFP4) GEMMs at 4096^3, "
@@ -565,14 +579,7 @@ def build_moe_nv(torch, F, W, dev, tokens, name, bound):
                      len(active) * per_expert, 4.0 * S * H * I, 2.0 * S * H * I, bound)
 
 
-def cpu_baseline():
-    """The CPU oracle on the whole W4A4 GEMM workload (M=N=K=4096): W is
-    MX-quantized beforehand (pre-quantized weights, as in the workload), then
-    the timed part quantizes A and forms the exact fp64 product with its error
-    bound."""
-    import workloads as W
-    from oracle import gemm as G
-    from oracle import quant as Q
+def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
         pools = threadpool_info()
@@ -581,20 +588,106 @@ def cpu_baseline():
                                  if i.get("user_api") == "blas"})) or "none found"
     except Exception:
         threads, blas = os.cpu_count() or 1, "unknown"
+    return int(threads), blas
+
+
+def _rows(fn, bits, n=512):
+    return tuple(np.concatenate(p) for p in zip(*[fn(bits[i:i + n]) for i in range(0, bits.shape[0], n)]))
+
+
+def _cpu_moe(workload, tokens, sample_tokens, fmt):
+    """The MoE oracle (moe_forward) on the first `sample_tokens` tokens of the
+    workload's batch.  Expert weights are pre-quantized inputs of the path, so
+    the touched experts get seeded random codes and scales (the oracle's time
+    does not depend on their values) and the routing ids are renumbered to them."""
+    import workloads as W
+    from oracle import moe as M
+    m = W.moe_workload(workload, tokens)
+    xb = W.bf16_bits(m.X[:sample_tokens])
+    ids = m.ids[:sample_tokens]
+    touched = np.unique(ids)
+    local = np.searchsorted(touched, ids).astype(np.int32)
+    n, H, I = len(touched), m.hidden, m.inter
+    blk = 32 if fmt == "mx" else 16
+    rng = np.random.default_rng(5)
+    w13c = rng.integers(0, 256, (n, 2 * I, H // 2), dtype=np.uint8)
+    w2c = rng.integers(0, 256, (n, H, I // 2), dtype=np.uint8)
+    lo, hi = (118, 128) if fmt == "mx" else (0x28, 0x48)      # UE8M0 bytes / finite E4M3 bytes
+    w13s = rng.integers(lo, hi, (n, 2 * I, H // blk), dtype=np.uint8)
+    w2s = rng.integers(lo, hi, (n, H, I // blk), dtype=np.uint8)
+    st = (np.full(n, 1e-3, np.float32), np.full(n, 1e-3, np.float32)) if fmt == "nv" else (None, None)
+    act = (np.float32(2e-3), np.float32(1e-3)) if fmt == "nv" else (None, None)
+    t0 = time.perf_counter()
+    M.moe_forward(fmt, xb, local, m.weights[:sample_tokens], w13c, w13s, w2c, w2s, st[0], st[1], act_st=act)
+    dt = time.perf_counter() - t0
+    return dt, n
+
+
+def cpu_baseline():
+    """The CPU oracle, as it stands, timed on the host cores for every
+    workload: the whole W4A4 GEMM (the `value` workload), the linear workload's
+    quantizers and remap, the tiny workload, and bounded token samples of the
+    three MoE workloads (stated in each entry's `sample`)."""
+    import workloads as W
+    from oracle import gemm as G
+    from oracle import quant as Q
+    threads, blas = _blas_threads()
+    base = {"cores": threads, "kind": "oracle"}
+    per = []
+    # tiny workload: MX quantize of A and W and the GEMM
+    wl1 = W.workload1()
+    a1, w1 = W.bf16_bits(wl1.A), W.bf16_bits(wl1.W)
+    t0 = time.perf_counter()
+    G.gemm_ref("mx", *Q.mx_quantize(a1), *Q.mx_quantize(w1))
+    dt = time.perf_counter() - t0
+    per.append(dict(base, workload="tiny MXFP4 quantize + GEMM 32x512x256", value=round(dt * 1e6, 1),
+                    unit="us per pass", sample="whole workload"))
+    # linear workload: quantizers and remap
+    wl2 = W.workload2()
+    for name, bits in (("W 4096x4096", W.bf16_bits(wl2.W)), ("A 2048x4096", W.bf16_bits(wl2.A))):
+        n = bits.size
+        t0 = time.perf_counter()
+        mq = _rows(Q.mx_quantize, bits)
+        t_mx = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        Q.nv_quantize(bits)
+        t_nv = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        Q.remap_mx_to_nv(*mq)
+        t_rm = time.perf_counter() - t0
+        per.append(dict(base, workload=f"linear {name}: MX quantize", value=round(n * 2.53125 / t_mx / 1e9, 4),
+                        unit="GB/s", sample="whole tensor"))
+        per.append(dict(base, workload=f"linear {name}: NV quantize (computed s_t)",
+                        value=round(n * 2.5625 / t_nv / 1e9, 4), unit="GB/s", sample="whole tensor"))
+        per.append(dict(base, workload=f"linear {name}: MX->NV remap", value=round(n * 0.09375 / t_rm / 1e9, 4),
+                        unit="GB/s", sample="whole tensor"))
+    # GEMM workload: A quantized, exact fp64 product and its bound, W pre-quantized
     wl = W.workload3()
     ab = W.bf16_bits(wl.A)
-    wb = W.bf16_bits(wl.W)
-    eb = tuple(np.concatenate(p) for p in zip(*[Q.mx_quantize(wb[i:i + 512]) for i in range(0, 4096, 512)]))
+    eb = _rows(Q.mx_quantize, W.bf16_bits(wl.W))
     t0 = time.perf_counter()
-    ea = tuple(np.concatenate(p) for p in zip(*[Q.mx_quantize(ab[i:i + 512]) for i in range(0, 4096, 512)]))
+    ea = _rows(Q.mx_quantize, ab)
     G.gemm_ref("mx", *ea, *eb)
-    dt = time.perf_counter() - t0
+    dt_gemm = time.perf_counter() - t0
     flops = 2.0 * 4096 ** 3
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": "the whole 4096^3 W4A4 MXFP4 GEMM: MX-quantize A (fp64 numpy) and the exact fp64 product "
-                      "with its error bound, W pre-quantized; "
-                      f"{dt:.1f} s on {os.cpu_count()} host cores",
-            "cpu_model": cpu_model(), "os_cpu_count": os.cpu_count(), "blas": blas}
+    gemm = dict(base, workload="W4A4 MXFP4 GEMM 4096^3", value=round(flops / dt_gemm / 1e12, 6), unit="TFLOP/s",
+                sample="the whole 4096^3 W4A4 MXFP4 GEMM: MX-quantize A (fp64 numpy) and the exact fp64 product "
+                       f"with its error bound, W pre-quantized; {dt_gemm:.1f} s")
+    per.append(gemm)
+    # MoE workloads on token samples
+    for wl_, T, ns, fmt, label in ((4, None, 8, "mx", "MoE h4096 MXFP4, 8192 tokens"),
+                                   (5, 64, 4, "nv", "MoE h7168 NVFP4, decode 64 tokens"),
+                                   (5, 16384, 4, "nv", "MoE h7168 NVFP4, prefill 16384 tokens")):
+        dt, ne = _cpu_moe(wl_, T, ns, fmt)
+        per.append(dict(base, workload=label, value=round(ns / dt, 4), unit="tokens/s",
+                        sample=f"the first {ns} tokens of the batch ({ns * 6} routed slots, {ne} experts): "
+                               f"{dt:.1f} s; tokens/s = {ns} / time, extrapolated to the batch by token count "
+                               "(each expert's weights are dequantized once per call, so a whole batch "
+                               "would amortize that over more tokens)"))
+    out = dict(gemm)
+    out["sample"] = gemm["sample"] + f" (on {os.cpu_count()} host cores)"
+    out.update(cpu_model=cpu_model(), os_cpu_count=os.cpu_count(), blas=blas, per_workload=per)
+    return out
 
 
 def gpu_info(torch):

@@ -7,8 +7,12 @@ Writes into the profiles directory:
                               kernels (FETCH_SIZE, WRITE_SIZE), each scaled by
                               what the same counter reads for a plain 256 MiB
                               device copy (256 MiB read, 256 MiB written);
-  traffic.json                the same figures for bench.py, tagged with the
-                              digest of the kernel sources they were taken on.
+  mfma_lds_bench_stages.txt   matrix-core busy fraction, MFMA operations and
+                              LDS bank conflicts per launch of the MFMA-bound
+                              stages' kernels;
+  traffic.json                the traffic and matrix-core figures for bench.py,
+                              tagged with the digest of the kernel sources they
+                              were taken on.
 usage: python3 profile_summary.py <raw output dir> <profiles dir>
 """
 from __future__ import annotations
@@ -27,6 +31,26 @@ TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d <out>/trac
              "python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline")
 PMC_CMD = ("rocprofv3 --pmc <FETCH_SIZE|WRITE_SIZE> --output-format csv -d <out>/pmc_<stage>_<counter> -o run -- "
            "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --copy-calibration --only <stage>")
+MFMA_CMD = ("rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_F6F4 SQ_INSTS_VALU_MFMA_MOPS_F16 "
+            "SQ_INSTS_VALU_MFMA_MOPS_F8 SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_ACTIVE_INST_LDS GRBM_GUI_ACTIVE "
+            "--output-format csv -d <out>/mfma_<stage> -o run -- python3 bench.py --steps 3 --warmup 1 "
+            "--no-cpu-baseline --only <stage>")
+MFMA_CTRS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_F6F4", "SQ_INSTS_VALU_MFMA_MOPS_F16",
+             "SQ_INSTS_VALU_MFMA_MOPS_F8", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_ACTIVE_INST_LDS",
+             "GRBM_GUI_ACTIVE")
+SIMDS = 1024          # 256 compute units x 4 SIMDs
+XCCS = 8              # GRBM_GUI_ACTIVE is counted once per XCC; the sum over them is 8x the busy cycles
+MFMA_ROWS = {
+    "gemm_mx_4096": ("gemm_mx_4096", "gemm_mx_256_kernel", 2.0 * 4096 ** 3),
+    "gemm_nv_4096": ("gemm_nv_4096", "gemm_nv_tile_kernel", 2.0 * 4096 ** 3),
+    "gemm_w4a8_4096": ("gemm_w4a8_4096", "gemm_w4a8_256_kernel", 2.0 * 4096 ** 3),
+    "moe_h4096.gate_up": ("moe_h4096", "moe_gate_up_mx256_kernel", 4.0 * 49152 * 4096 * 2048),
+    "moe_h4096.down": ("moe_h4096", "moe_down_mx256_kernel", 2.0 * 49152 * 4096 * 2048),
+    "moe_h7168_decode64.gate_up": ("moe_h7168_decode64", "moe_gate_up_nv_kernel", 4.0 * 384 * 7168 * 3072),
+    "moe_h7168_decode64.down": ("moe_h7168_decode64", "moe_down_nv_kernel", 2.0 * 384 * 7168 * 3072),
+    "moe_h7168_prefill16384.gate_up": ("moe_h7168_prefill16384", "moe_gate_up_nvw_kernel", 4.0 * 98304 * 7168 * 3072),
+    "moe_h7168_prefill16384.down": ("moe_h7168_prefill16384", "moe_down_nvw_kernel", 2.0 * 98304 * 7168 * 3072),
+}
 COPY_BYTES = 256 << 20
 
 # bench row -> (profiled stage, [(kernel-name substring, grid size or None)]); the
@@ -35,6 +59,7 @@ ROWS = {
     "gemm_mx_4096": ("gemm_mx_4096", [("gemm_mx_256_kernel", None)]),
     "quantize_mx_W": ("quantize_mx_W", [("mx_quantize_kernel", None)]),
     "quantize_nv_W": ("quantize_nv_W", [("nv_amax_kernel", None), ("nv_quantize_kernel", None)]),
+    "dequant_fp8_W": ("dequant_fp8_W", [("scale_max_kernel", None), ("fp8_dequant_kernel", None)]),
     "moe_h4096.gate_up": ("moe_h4096", [("moe_gate_up_mx256_kernel", None)]),
     "moe_h4096.down": ("moe_h4096", [("moe_down_mx256_kernel", None)]),
     "moe_h4096.combine": ("moe_h4096", [("combine_kernel", None)]),
@@ -60,9 +85,11 @@ def short(name):
     return n.split("(")[0][:70]
 
 
-def read_counter(raw, stage, counter):
-    """Per dispatch: (kernel name, grid size, value) of one counter pass."""
-    files = glob.glob(os.path.join(raw, f"pmc_{stage}_{counter}", "**", "*counter_collection.csv"), recursive=True)
+def read_counter(raw, stage, counter, folder=None):
+    """Per dispatch: (kernel name, grid size, value) of one counter of a pass
+    (values summed over the counter's instances)."""
+    folder = folder or f"pmc_{stage}_{counter}"
+    files = glob.glob(os.path.join(raw, folder, "**", "*counter_collection.csv"), recursive=True)
     if not files:
         return []
     vals = {}
@@ -100,18 +127,39 @@ def main(raw, prof):
                 f.write(f"{short(r['Name']):72s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
                         f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} "
                         f"{float(r['TotalDurationNs']) / 1e6:10.3f}\n")
-    # ---- traffic
+    prev = {}
+    try:
+        with open(os.path.join(prof, "traffic.json")) as f:
+            prev = json.load(f)
+    except (OSError, ValueError):
+        pass
+    keep = prev if prev.get("source_digest") == source_digest() else {}
+    out = {"source_digest": source_digest(), "counter_units": "KiB per dispatch"}
+    t = traffic_summary(raw, prof)
+    if t is not None:
+        out.update(t)
+    elif "kernels" in keep:
+        out.update({k: keep[k] for k in ("copy_calibration", "kernels") if k in keep})
+    m = mfma_summary(raw, prof)
+    if m is not None:
+        out["mfma"] = m
+    elif "mfma" in keep:
+        out["mfma"] = keep["mfma"]
+    with open(os.path.join(prof, "traffic.json"), "w") as f:
+        json.dump(out, f, indent=1)
+
+
+def traffic_summary(raw, prof):
     cf = read_counter(raw, "copy_256MiB", "FETCH_SIZE")
     cw = read_counter(raw, "copy_256MiB", "WRITE_SIZE")
     big = lambda d: max((x for x in d if "copy" in x[0].lower() or "Copy" in x[0]), key=lambda x: x[2], default=None)
     bf, bw = big(cf), big(cw)
     if not bf or not bw:
         print("no copy calibration found; traffic not written")
-        return
+        return None
     ff = COPY_BYTES / (bf[2] * 1024.0)
     fw = COPY_BYTES / (bw[2] * 1024.0)
-    out = {"source_digest": source_digest(), "counter_units": "KiB per dispatch",
-           "copy_calibration": {"kernel": short(bf[0]), "fetch_kib": bf[2], "write_kib": bw[2],
+    out = {"copy_calibration": {"kernel": short(bf[0]), "fetch_kib": bf[2], "write_kib": bw[2],
                                 "factor_fetch": ff, "factor_write": fw}, "kernels": {}}
     lines = []
     for row, (stage, parts) in ROWS.items():
@@ -134,18 +182,63 @@ def main(raw, prof):
                                "bytes_per_launch": round(fsum + wsum)}
         lines.append(f"{row:30s} read {fsum / 1e6:10.2f} MB  written {wsum / 1e6:10.2f} MB  total "
                      f"{(fsum + wsum) / 1e6:10.2f} MB   ({'; '.join(detail)})")
-    with open(os.path.join(prof, "traffic.json"), "w") as f:
-        json.dump(out, f, indent=1)
     with open(os.path.join(prof, "traffic_bench_stages.txt"), "w") as f:
         f.write("HBM traffic per launch of bench.py stages on MI355X (rocprofv3 counters, one counter per pass).\n")
         f.write(f"command (per stage and counter): {PMC_CMD}\n")
         f.write(f"calibration: a 256 MiB device copy ({short(bf[0])}) reads FETCH_SIZE {bf[2]:.0f} KiB and "
                 f"WRITE_SIZE {bw[2]:.0f} KiB; bytes = counter * 1024 * (256 MiB / copy's counter bytes), "
                 f"factors {ff:.4f} (fetch) and {fw:.4f} (write).\n")
-        f.write(f"kernel sources digest: {out['source_digest']}\n\n")
+        f.write(f"kernel sources digest: {source_digest()}\n\n")
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
+    return out
 
+
+def mfma_summary(raw, prof):
+    """Per kernel, means over its dispatches: matrix-core busy fraction
+    (SQ_VALU_MFMA_BUSY_CYCLES summed over the SIMDs / (GRBM_GUI_ACTIVE per XCC
+    x 1024 SIMDs)), matrix operations (MOPS x 512) against the algorithmic
+    flops, and LDS bank-conflict cycles per LDS access cycle."""
+    res, lines = {}, []
+    for row, (stage, sub, flops) in MFMA_ROWS.items():
+        vals = {}
+        for c in MFMA_CTRS:
+            d = read_counter(raw, stage, c, folder=f"mfma_{stage}")
+            m, n = mean_for(d, sub, None)
+            if m is None:
+                break
+            vals[c] = m
+        if len(vals) != len(MFMA_CTRS):
+            continue
+        gui = vals["GRBM_GUI_ACTIVE"] / XCCS
+        busy = vals["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * SIMDS) if gui else None
+        ops = 512.0 * (vals["SQ_INSTS_VALU_MFMA_MOPS_F6F4"] + vals["SQ_INSTS_VALU_MFMA_MOPS_F16"] +
+                       vals["SQ_INSTS_VALU_MFMA_MOPS_F8"])
+        lds = vals["SQ_LDS_IDX_ACTIVE"] - vals["SQ_LDS_BANK_CONFLICT"]
+        conf = vals["SQ_LDS_BANK_CONFLICT"] / lds if lds > 0 else None
+        res[row] = {"mfma_busy": round(busy, 4) if busy is not None else None, "gui_active_cycles": round(gui),
+                    "mfma_ops": ops, "algorithmic_flops": flops,
+                    "lds_bank_conflicts_per_access": round(conf, 4) if conf is not None else None,
+                    "raw": vals}
+        lines.append(f"{row:32s} MFMA busy {100 * busy:6.1f}%  matrix ops {ops:.4g} (algorithmic {flops:.4g}, "
+                     f"x{ops / flops:.3f})  LDS bank conflicts {conf if conf is None else round(conf, 4)} per access "
+                     f"({vals['SQ_LDS_BANK_CONFLICT']:.4g} conflict / {vals['SQ_LDS_IDX_ACTIVE']:.4g} active cycles)  "
+                     f"GUI active {gui:.4g} cycles")
+    if not res:
+        print("no matrix-core counters found")
+        return None
+    with open(os.path.join(prof, "mfma_lds_bench_stages.txt"), "w") as f:
+        f.write("Matrix-core utilisation and LDS bank conflicts per launch of the MFMA-bound kernels of bench.py "
+                "on MI355X (rocprofv3 counters, one pass per stage).\n")
+        f.write(f"command (per stage): {MFMA_CMD}\n")
+        f.write("MFMA busy = sum of SQ_VALU_MFMA_BUSY_CYCLES over the 1024 SIMDs / (GRBM_GUI_ACTIVE per XCC x 1024); "
+                "matrix ops = 512 x (MOPS_F6F4 + MOPS_F16 + MOPS_F8); LDS bank conflicts per access = "
+                "SQ_LDS_BANK_CONFLICT / (SQ_LDS_IDX_ACTIVE - SQ_LDS_BANK_CONFLICT).  Means over the kernel's "
+                "dispatches in the run (setup calls included).\n")
+        f.write(f"kernel sources digest: {source_digest()}\n\n")
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+    return res
 
 if __name__ == "__main__":
     main(sys.argv[1], sys.argv[2])
