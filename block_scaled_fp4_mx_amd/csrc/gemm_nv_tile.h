@@ -14,7 +14,7 @@
 // bytes go to fp16 in one v_cvt_scalef32_pk_f16_fp8) finishes the exact value.
 //
 // Stage layout per K step: A TM rows x 512 B (16-byte chunk c of row r at
-// c ^ (r & 15)), B codes 256 rows x 128 B (chunk c of row r at c ^ (r & 7)), B
+// c ^ nv_a_swz(r)), B codes 256 rows x 128 B (chunk c of row r at c ^ (r & 7)), B
 // scales 256 rows x 16 B.  All of it goes from global memory straight into LDS
 // (global_load_lds_dwordx4 / _dword), as in the MX tile.
 #pragma once
@@ -46,7 +46,7 @@ struct NvSmemT {
 // Sources of one tile, as per-lane byte offsets from bases that are the same
 // for the whole workgroup.  A (fp16): DMA q of a lane fills 1 KiB block
 // wave * (TM/16) + q, i.e. row nv_a_row<TM>(q), LDS chunk lane % 32, from global
-// chunk (lane % 32) ^ (row & 15); aoff[q] is that row's byte offset plus the
+// chunk (lane % 32) ^ nv_a_swz(row); aoff[q] is that row's byte offset plus the
 // chunk.  B codes: DMA q fills rows (wave * 4 + q) * 8 + lane / 8 as in the MX
 // tile (boff[q]).  B scales: every wave fills its 512 bytes with two 4-byte
 // DMAs (sdw[j]: byte wave*512 + j*256 + 4*lane of the scale slab).
@@ -61,8 +61,15 @@ template <int TM>
 __device__ __forceinline__ int nv_a_row(int q) {
     return 2 * ((int)(threadIdx.x >> 6) * (TM / 16) + q) + (int)((threadIdx.x & 63) >> 5);
 }
+// fp16 A rows: 16-byte chunk c of row r sits at slot c ^ nv_a_swz(r).  With
+// the plain mask r & 15, the fragment reads of lanes (r, lq) and (r ^ 4, lq ^ 1)
+// of one instruction land on the same banks (measured with the LDS bank-conflict
+// counter: one stall cycle per access); this mask, linear in r, pairs no two
+// lanes of a fragment read that way.
+__device__ __forceinline__ int nv_a_swz(int row) { return ((row & 7) << 1) | ((row >> 3) & 1); }
+
 __device__ __forceinline__ uint32_t nv_a_chunk(int row) {
-    return (((threadIdx.x & 31) ^ (uint32_t)(row & 15)) * 16);
+    return (((threadIdx.x & 31) ^ (uint32_t)nv_a_swz(row)) * 16);
 }
 // Three-stage scale DMA j of this lane: slab row, and byte within the row's 16.
 __device__ __forceinline__ int nv_sdw_row(int j) {
@@ -162,7 +169,7 @@ __device__ __forceinline__ void nv_tile_mainloop(NvSmemT<TM, NS>& sm, const NvSr
                 const int row = mf * 16 + lr;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int ch = (hs * 16 + lq * 4 + i) ^ (row & 15);
+                    const int ch = (hs * 16 + lq * 4 + i) ^ nv_a_swz(row);
                     const h8_t a = *reinterpret_cast<const h8_t*>(&st.a[row * kNvARow + ch * 16]);
 #pragma unroll
                     for (int nf = 0; nf < 2; ++nf)

@@ -35,10 +35,11 @@
 // accumulators hold registers).
 //
 // Stage layout per K step (128 values):
-//   fp16 A  128 rows x 256 B, 16-byte chunk c of row r at slot c ^ (r & 15);
-//   B codes 512 rows x 64 B, chunk c of row r at slot c ^ nw_swz(r), which
-//           puts any 8 (and any 16) consecutive rows of a fragment read on
-//           different 16-byte bank groups;
+//   fp16 A  128 rows x 256 B, 16-byte chunk c of row r at slot c ^ nv_a_swz(r);
+//   B codes 512 rows x 64 B in blocks of 16 rows (1 KiB), chunk-major inside a
+//           block: chunk c of row r at (r & ~15) * 64 + c * 256 + (r & 15) * 16,
+//           so a fragment read (lane = 16 * chunk + row within the block) is one
+//           contiguous KiB;
 //   B E4M3  512 rows x 8 B, row-major;
 //   A codes 128 rows x 64 B and A E4M3 128 rows x 8 B, row-major.
 // Every stage arrives by global_load_lds DMA (dwordx4 for codes, dword for the
@@ -76,7 +77,8 @@ struct NwSmem {
 static_assert(sizeof(NwSmem) <= 160 * 1024, "the wide tile exceeds the LDS of one workgroup");
 
 // Sources of one tile as per-lane byte offsets from workgroup-uniform bases.
-//   B codes: DMA q (0..3) of wave w fills rows nw_b_row(q) (16 rows per KiB);
+//   B codes: DMA q (0..3) of wave w fills rows nw_b_row(q) (one 16-row block
+//     per KiB, lane l taking chunk l / 16 of row l % 16 of the block);
 //   B scales: dword DMA j (0..1) of wave w fills rows nw_s_row(j), 4 of the
 //     row's 8 bytes (nw_s_col);
 //   A codes: one DMA per wave, rows nw_ac_row() (16 rows per KiB);
@@ -93,9 +95,12 @@ struct NwSrc {
 };
 
 __device__ __forceinline__ int nw_wave() { return (int)(threadIdx.x >> 6); }
-__device__ __forceinline__ int nw_b_row(int q) { return 64 * nw_wave() + 16 * q + (int)((threadIdx.x & 63) >> 2); }
-__device__ __forceinline__ uint32_t nw_swz(int row) { return (uint32_t)((row >> 1) ^ (row >> 3)) & 3u; }
-__device__ __forceinline__ uint32_t nw_b_chunk(int row) { return ((threadIdx.x & 3u) ^ nw_swz(row)) << 4; }
+__device__ __forceinline__ int nw_b_row(int q) { return 64 * nw_wave() + 16 * q + (int)(threadIdx.x & 15); }
+__device__ __forceinline__ uint32_t nw_b_chunk(int row) {
+    (void)row;
+    return ((threadIdx.x & 63u) >> 4) << 4;
+}
+
 __device__ __forceinline__ int nw_s_row(int j) { return 64 * nw_wave() + 32 * j + (int)((threadIdx.x & 63) >> 1); }
 __device__ __forceinline__ uint32_t nw_s_col() { return (threadIdx.x & 1u) << 2; }
 __device__ __forceinline__ int nw_ac_row() { return 16 * nw_wave() + (int)((threadIdx.x & 63) >> 2); }
@@ -131,8 +136,8 @@ __device__ __forceinline__ void nw_expand_a_half(const NwAStage& st, uint8_t* a1
     const int row = h * 64 + (int)(threadIdx.x >> 3), g = (int)(threadIdx.x & 7);
     const uint2 c = *reinterpret_cast<const uint2*>(&st.c[row * kNwBRow + g * 8]);
     const _Float16 sg = nv_scale_pair(st.s[row * kNwSRow + g])[0];
-    *reinterpret_cast<h8_t*>(&a16[row * kNwARow + (((2 * g) ^ (row & 15)) << 4)]) = nv_expand8(c.x, sg);
-    *reinterpret_cast<h8_t*>(&a16[row * kNwARow + (((2 * g + 1) ^ (row & 15)) << 4)]) = nv_expand8(c.y, sg);
+    *reinterpret_cast<h8_t*>(&a16[row * kNwARow + (((2 * g) ^ nv_a_swz(row)) << 4)]) = nv_expand8(c.x, sg);
+    *reinterpret_cast<h8_t*>(&a16[row * kNwARow + (((2 * g + 1) ^ nv_a_swz(row)) << 4)]) = nv_expand8(c.y, sg);
 }
 
 __device__ __forceinline__ uint32_t nw_word(const uint4& c, int i) {
@@ -178,7 +183,7 @@ __device__ __forceinline__ void nw_mainloop(NwSmem& sm, const NwSrc& S, int nste
 #pragma unroll
         for (int nf = 0; nf < 4; ++nf) {
             const int row = wave * 64 + nf * 16 + lr;
-            c[nf] = *reinterpret_cast<const uint4*>(&st.b[row * kNwBRow + ((lq ^ nw_swz(row)) << 4)]);
+            c[nf] = *reinterpret_cast<const uint4*>(&st.b[(row & ~15) * kNwBRow + lq * 256 + lr * 16]);
             sp[nf] = nv_scale_pair(*reinterpret_cast<const uint16_t*>(&st.s[row * kNwSRow + lq * 2]));
         }
         // the next step's A (its codes landed with this step's wait)
@@ -198,7 +203,7 @@ __device__ __forceinline__ void nw_mainloop(NwSmem& sm, const NwSrc& S, int nste
 #pragma unroll
             for (int mf = 0; mf < MF; ++mf) {
                 const int row = mf * 16 + lr;
-                a[mf] = *reinterpret_cast<const h8_t*>(&ab[row * kNwARow + (((4 * lq + i) ^ (row & 15)) << 4)]);
+                a[mf] = *reinterpret_cast<const h8_t*>(&ab[row * kNwARow + (((4 * lq + i) ^ nv_a_swz(row)) << 4)]);
             }
             h8_t bx[4];
 #pragma unroll

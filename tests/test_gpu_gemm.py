@@ -130,9 +130,10 @@ def test_gemm_nv_ragged(m, n, k):
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("pad", [0, 4])
 def test_gemm_nv_tiled_ragged_strided(dtype, pad):
-    """K a multiple of 128 and at least 32 tiles: the 64x512 LDS-staged NV tile
-    (A expanded to fp16 in LDS, B in registers), ragged M and N, both output
-    types and a padded output row pitch."""
+    """K a multiple of 128 and at least 16 tiles: the 128x512 wide NV tile (both
+    operands staged as NVFP4 codes, A expanded to fp16 in LDS one step ahead, B
+    expanded in registers), ragged M and N (24 tiles here), both output types
+    and a padded output row pitch."""
     m, n, k = 1000, 1100, 1024
     wl = W.random_linear(5151 + pad, m, n, k, outlier_p=0.01)
     ab, wb = W.bf16_bits(wl.A), W.bf16_bits(wl.W)
