@@ -401,24 +401,22 @@ __global__ __launch_bounds__(kThreads) void ste_backward_kernel(const void* __re
 // ------------------------------------------------------------------ tensor-wide scale passes
 // The MX -> NV remap and the MX -> FP8 dequantization both need E_max, the
 // largest block exponent of the whole tensor, before any output is final.
-// Both run as two launches of many workgroups, without workspace:
-//   pass 1 (scale_max_kernel): workgroup g writes the largest scale byte of its
-//     share to byte g of the output array (a scratch use of bytes that pass 2
-//     rewrites last) and workgroup 0 clears the two result words (the int32
-//     counter and the fp32 tensor scale, used as integers until the end);
-//   pass 2: every workgroup reduces the pass-1 bytes to E_max, converts its
-//     blocks except the first `reserved` ones (whose output bytes hold the
-//     pass-1 maxima), adds its inexact blocks to the tensor-scale word and then
-//     takes a ticket from the counter word.  The workgroup that draws the last
-//     ticket knows every other workgroup has finished reading the pass-1 bytes:
-//     it converts the reserved blocks, then writes the final count and the
-//     tensor scale over the two words.
+// Three launches, without workspace:
+//   pass 1 (scale_max_kernel, many workgroups): workgroup g writes the largest
+//     scale byte of its share to byte g of the output array (a scratch use of
+//     bytes that pass 3 rewrites) and workgroup 0 clears the inexact counter;
+//   pass 2 (many workgroups): each workgroup reduces the pass-1 bytes to E_max
+//     and converts its blocks, except the first `reserved` ones, whose output
+//     bytes hold the pass-1 maxima; inexact blocks are added to the counter
+//     (one atomic per workgroup that found any);
+//   pass 3 (one workgroup): the reserved blocks and the tensor scale.
+// (A grid-wide "last workgroup finishes" ticket in pass 2 would save a launch,
+// but thousands of same-address atomics serialize: measured 44 us for 4096^2.)
 constexpr int kScaleMaxChunk = 4096;   // scale bytes per pass-1 workgroup
 constexpr int kScaleMaxGroups = 256;   // at most one byte per pass-2 thread
 
 __global__ __launch_bounds__(kThreads) void scale_max_kernel(const uint8_t* __restrict__ s, int64_t nb,
-                                                             uint8_t* __restrict__ part, uint32_t* __restrict__ w0,
-                                                             uint32_t* __restrict__ w1) {
+                                                             uint8_t* __restrict__ part, int32_t* __restrict__ cnt) {
     const int64_t lo = (int64_t)blockIdx.x * nb / gridDim.x, hi = (int64_t)(blockIdx.x + 1) * nb / gridDim.x;
     uint32_t m = 0;
     // bytes before the first 16-byte boundary, the 16-byte body, then the tail
@@ -440,10 +438,7 @@ __global__ __launch_bounds__(kThreads) void scale_max_kernel(const uint8_t* __re
     if (threadIdx.x == 0) {
         for (int i = 1; i < kThreads / 64; ++i) m = max(m, red[i]);
         part[blockIdx.x] = (uint8_t)m;
-        if (blockIdx.x == 0) {
-            *w0 = 0u;
-            *w1 = 0u;
-        }
+        if (blockIdx.x == 0) *cnt = 0;
     }
 }
 
@@ -463,10 +458,8 @@ __device__ __forceinline__ uint32_t reduce_part(const uint8_t* part, int npart, 
     return m;
 }
 
-// The end of pass 2: per-workgroup inexact count `mine`, then the ticket; true
-// in the one workgroup that must finish the reserved blocks (all threads).
-__device__ __forceinline__ bool ticket_last(uint32_t mine, uint32_t* cnt_word, uint32_t* ticket_word,
-                                            uint32_t* sh) {
+// Adds the workgroup's inexact blocks to the counter (one atomic, if any).
+__device__ __forceinline__ void add_count(uint32_t mine, int32_t* cnt, uint32_t* sh) {
     for (int off = 32; off > 0; off >>= 1) mine += (uint32_t)__shfl_xor((int)mine, off);
     __syncthreads();                       // the reduce_part slots are free again
     if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = mine;
@@ -474,14 +467,8 @@ __device__ __forceinline__ bool ticket_last(uint32_t mine, uint32_t* cnt_word, u
     if (threadIdx.x == 0) {
         uint32_t t = 0;
         for (int i = 0; i < kThreads / 64; ++i) t += sh[i];
-        if (t) atomicAdd(cnt_word, t);
-        __threadfence();
-        sh[0] = atomicAdd(ticket_word, 1u) == gridDim.x - 1 ? 1u : 0u;
+        if (t) atomicAdd(cnt, (int32_t)t);
     }
-    __syncthreads();
-    const bool last = sh[0] != 0u;
-    __syncthreads();
-    return last;
 }
 
 // ------------------------------------------------------------------ MX -> NV remap
@@ -505,30 +492,23 @@ __device__ __forceinline__ uint32_t remap_block(const uint8_t* __restrict__ code
     return bad;
 }
 
+// Pass 2 (kFinish false): blocks [reserved, nb); pass 3 (kFinish true, one
+// workgroup): blocks [0, reserved) and the tensor scale.
+template <bool kFinish>
 __global__ __launch_bounds__(kThreads) void remap_kernel(const uint8_t* __restrict__ codes,
                                                          const uint8_t* __restrict__ s, int64_t nb,
                                                          uint8_t* __restrict__ snv, int npart, int64_t reserved,
                                                          float* __restrict__ ts, int32_t* __restrict__ n_inexact) {
     __shared__ uint32_t red[kThreads / 64];
     const int kexp = (int)reduce_part(snv, npart, red) - 127 - 8;
+    __syncthreads();                       // every thread has read the pass-1 bytes before any is rewritten
     uint32_t bad = 0;
     const int64_t stride = (int64_t)gridDim.x * kThreads;
-    for (int64_t i = reserved + (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nb; i += stride)
+    const int64_t i0 = kFinish ? 0 : reserved, i1 = kFinish ? reserved : nb;
+    for (int64_t i = i0 + (int64_t)blockIdx.x * kThreads + threadIdx.x; i < i1; i += stride)
         bad += remap_block(codes, s, snv, i, kexp);
-    uint32_t* cnt = reinterpret_cast<uint32_t*>(ts);
-    uint32_t* tk = reinterpret_cast<uint32_t*>(n_inexact);
-    if (!ticket_last(bad, cnt, tk, red)) return;
-    bad = 0;
-    for (int64_t i = threadIdx.x; i < reserved; i += kThreads) bad += remap_block(codes, s, snv, i, kexp);
-    for (int off = 32; off > 0; off >>= 1) bad += (uint32_t)__shfl_xor((int)bad, off);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = bad;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t t = atomicAdd(cnt, 0u);
-        for (int i = 0; i < kThreads / 64; ++i) t += red[i];
-        *n_inexact = (int32_t)t;
-        *ts = ldexpf(1.0f, kexp);          // 2^-135 .. 2^119; below 2^-126 a subnormal
-    }
+    add_count(bad, n_inexact, red);
+    if (kFinish && threadIdx.x == 0) *ts = ldexpf(1.0f, kexp);   // 2^-135 .. 2^119; below 2^-126 a subnormal
 }
 
 // ------------------------------------------------------------------ MX -> FP8 dequant
@@ -595,25 +575,41 @@ __device__ __forceinline__ uint2 fp8_expand8(uint32_t c, uint32_t tlo, uint32_t 
     return r;
 }
 
-// Half a block per lane (16 codes in, 16 bytes out); returns 1 on the even lane
-// of a block pair when the block is inexact.  Both lanes of a pair are active
-// together (units are whole blocks).
-__device__ __forceinline__ uint32_t fp8_half_block(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ s,
-                                                   uint8_t* __restrict__ v8, uint8_t* __restrict__ s8out,
-                                                   int64_t u, int kexp) {
-    const int64_t b = u >> 1;
-    const int j = (int)s[b] - 127 - kexp;
+// One block per lane: 16 code bytes in, 32 E4M3 bytes out.  Blocks within 11
+// binades of the largest (j >= -5) have every value normal and exact: the table
+// is the E4M3 bytes of the E2M1 magnitudes at j = 0 (0x30, 0x38, 0x3C, 0x40,
+// 0x44, 0x48, 0x4C) with j added to each nonzero byte's exponent field (no
+// byte drops below 8, so no borrow crosses bytes).  Other blocks take the
+// general table.  Returns 1 for an inexact block.
+__device__ __forceinline__ uint32_t fp8_block(uint4 c, uint32_t sbyte, uint8_t* __restrict__ v8,
+                                              uint8_t* __restrict__ s8out, int64_t b, int kexp) {
+    const int j = (int)sbyte - 127 - kexp;
     uint32_t tlo, thi, badm, s8;
-    fp8_block_table(j, tlo, thi, badm, s8);
-    const uint2 c = reinterpret_cast<const uint2*>(codes)[u];
+    if (j >= -5) {
+        tlo = 0x3C383000u + (uint32_t)(j * 0x08080800);
+        thi = 0x4C484440u + (uint32_t)(j * 0x08080808);
+        badm = 0u;
+        s8 = (uint32_t)(j + 7) << 3;
+    } else {
+        fp8_block_table(j, tlo, thi, badm, s8);
+    }
     uint32_t hit = 0;
-    const uint2 lo = fp8_expand8(c.x, tlo, thi, hit);
-    const uint2 hi = fp8_expand8(c.y, tlo, thi, hit);
-    reinterpret_cast<uint4*>(v8)[u] = make_uint4(lo.x, lo.y, hi.x, hi.y);
-    if (s8out != nullptr && (u & 1) == 0) s8out[b] = (uint8_t)s8;
+    const uint2 o0 = fp8_expand8(c.x, tlo, thi, hit);
+    const uint2 o1 = fp8_expand8(c.y, tlo, thi, hit);
+    const uint2 o2 = fp8_expand8(c.z, tlo, thi, hit);
+    const uint2 o3 = fp8_expand8(c.w, tlo, thi, hit);
+    uint4* o = reinterpret_cast<uint4*>(v8 + b * 32);
+    o[0] = make_uint4(o0.x, o0.y, o1.x, o1.y);
+    o[1] = make_uint4(o2.x, o2.y, o3.x, o3.y);
+    if (s8out != nullptr) s8out[b] = (uint8_t)s8;
     return (hit & badm) ? 1u : 0u;
 }
 
+constexpr int kFp8Depth = 4;
+
+// Pass 2 (kFinish false): blocks [reserved, nb); pass 3 (kFinish true, one
+// workgroup): blocks [0, reserved) and the tensor scale.
+template <bool kFinish>
 __global__ __launch_bounds__(kThreads) void fp8_dequant_kernel(const uint8_t* __restrict__ codes,
                                                                const uint8_t* __restrict__ s, int64_t nb,
                                                                uint8_t* __restrict__ v8, uint8_t* __restrict__ s8out,
@@ -621,32 +617,30 @@ __global__ __launch_bounds__(kThreads) void fp8_dequant_kernel(const uint8_t* __
                                                                int32_t* __restrict__ n_inexact) {
     __shared__ uint32_t red[kThreads / 64];
     const int kexp = (int)reduce_part(v8, npart, red) - 127 - 6;
-    const int64_t units = nb * 2, ures = reserved * 2;
-    const int64_t stride = (int64_t)gridDim.x * kThreads;     // even, so a pair stays in one wave
+    __syncthreads();                       // every thread has read the pass-1 bytes before any is rewritten
+    const int64_t b0 = kFinish ? 0 : reserved, b1 = kFinish ? reserved : nb;
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
     uint32_t bad = 0;
-    for (int64_t u = ures + (int64_t)blockIdx.x * kThreads + threadIdx.x; u < units; u += stride) {
-        uint32_t f = fp8_half_block(codes, s, v8, s8out, u, kexp);
-        f |= (uint32_t)__shfl_xor((int)f, 1);
-        if ((u & 1) == 0) bad += f;
+    // kFp8Depth blocks per lane: every load is issued before the first conversion
+    for (int64_t b = b0 + (int64_t)blockIdx.x * kThreads + threadIdx.x; b < b1; b += kFp8Depth * stride) {
+        uint4 c[kFp8Depth];
+        uint32_t sb[kFp8Depth];
+#pragma unroll
+        for (int d = 0; d < kFp8Depth; ++d) {
+            const int64_t bd = b + d * stride;
+            if (bd < b1) {
+                c[d] = reinterpret_cast<const uint4*>(codes)[bd];
+                sb[d] = s[bd];
+            }
+        }
+#pragma unroll
+        for (int d = 0; d < kFp8Depth; ++d) {
+            const int64_t bd = b + d * stride;
+            if (bd < b1) bad += fp8_block(c[d], sb[d], v8, s8out, bd, kexp);
+        }
     }
-    uint32_t* cnt = reinterpret_cast<uint32_t*>(ts);
-    uint32_t* tk = reinterpret_cast<uint32_t*>(n_inexact);
-    if (!ticket_last(bad, cnt, tk, red)) return;
-    bad = 0;
-    for (int64_t u = threadIdx.x; u < ures; u += kThreads) {
-        uint32_t f = fp8_half_block(codes, s, v8, s8out, u, kexp);
-        f |= (uint32_t)__shfl_xor((int)f, 1);
-        if ((u & 1) == 0) bad += f;
-    }
-    for (int off = 32; off > 0; off >>= 1) bad += (uint32_t)__shfl_xor((int)bad, off);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = bad;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t t = atomicAdd(cnt, 0u);
-        for (int i = 0; i < kThreads / 64; ++i) t += red[i];
-        *n_inexact = (int32_t)t;
-        *ts = ldexpf(1.0f, kexp);          // 2^-133 .. 2^121; below 2^-126 a subnormal
-    }
+    add_count(bad, n_inexact, red);
+    if (kFinish && threadIdx.x == 0) *ts = ldexpf(1.0f, kexp);   // 2^-133 .. 2^121; below 2^-126 a subnormal
 }
 
 }  // namespace
@@ -812,12 +806,12 @@ hipError_t launch_remap(const uint8_t* codes, const uint8_t* scales, int64_t row
                         uint8_t* scales_nv, float* ts, int32_t* n_inexact, hipStream_t s) {
     const int64_t nb = rows * (k / 32);
     const unsigned g1 = scale_max_groups(nb);
-    scale_max_kernel<<<g1, kThreads, 0, s>>>(scales, nb, scales_nv, reinterpret_cast<uint32_t*>(ts),
-                                              reinterpret_cast<uint32_t*>(n_inexact));
+    scale_max_kernel<<<g1, kThreads, 0, s>>>(scales, nb, scales_nv, n_inexact);
     const int64_t reserved = min((int64_t)(g1 + 1) / 2, nb);   // blocks whose 2 output bytes hold pass-1 maxima
-    unsigned g2 = grid_for(nb - reserved);
+    unsigned g2 = grid_for(nb - reserved, 4);
     if (g2 > kMxMaxBlocks) g2 = kMxMaxBlocks;
-    remap_kernel<<<g2, kThreads, 0, s>>>(codes, scales, nb, scales_nv, (int)g1, reserved, ts, n_inexact);
+    remap_kernel<false><<<g2, kThreads, 0, s>>>(codes, scales, nb, scales_nv, (int)g1, reserved, ts, n_inexact);
+    remap_kernel<true><<<1, kThreads, 0, s>>>(codes, scales, nb, scales_nv, (int)g1, reserved, ts, n_inexact);
     return hipGetLastError();
 }
 
@@ -825,12 +819,12 @@ hipError_t launch_dequant_fp8(const uint8_t* codes, const uint8_t* scales, int64
                               uint8_t* s8, float* ts, int32_t* n_inexact, hipStream_t s) {
     const int64_t nb = rows * (k / 32);
     const unsigned g1 = scale_max_groups(nb);
-    scale_max_kernel<<<g1, kThreads, 0, s>>>(scales, nb, v8, reinterpret_cast<uint32_t*>(ts),
-                                              reinterpret_cast<uint32_t*>(n_inexact));
+    scale_max_kernel<<<g1, kThreads, 0, s>>>(scales, nb, v8, n_inexact);
     const int64_t reserved = min((int64_t)(g1 + 31) / 32, nb);  // blocks whose 32 output bytes hold pass-1 maxima
-    unsigned g2 = grid_for(2 * (nb - reserved));
+    unsigned g2 = grid_for(nb - reserved, kFp8Depth);
     if (g2 > kMxMaxBlocks) g2 = kMxMaxBlocks;
-    fp8_dequant_kernel<<<g2, kThreads, 0, s>>>(codes, scales, nb, v8, s8, (int)g1, reserved, ts, n_inexact);
+    fp8_dequant_kernel<false><<<g2, kThreads, 0, s>>>(codes, scales, nb, v8, s8, (int)g1, reserved, ts, n_inexact);
+    fp8_dequant_kernel<true><<<1, kThreads, 0, s>>>(codes, scales, nb, v8, s8, (int)g1, reserved, ts, n_inexact);
     return hipGetLastError();
 }
 

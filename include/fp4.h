@@ -267,8 +267,8 @@ int fp4_mx_to_mxfp8(const uint8_t* codes, int64_t rows, int64_t k, uint8_t* code
  *     least E_max - 14 (a largest-to-smallest block scale ratio of at most 2^14).
  * codes: [rows, k/2]; scales_e8m0: [rows, k/32]; values_e4m3: [rows, k] bytes;
  * block_scales_e4m3: [rows, k/32] or NULL (not written); tensor_scale: 1 device
- * float; n_inexact_blocks: 1 device int32.  Both are written by the call (they
- * also serve as its counters while it runs).
+ * float; n_inexact_blocks: 1 device int32 (cleared, then accumulated, while the
+ * call runs).
  * Errors: k % 32 != 0 -> FP4_ERR_SHAPE.
  */
 int fp4_mx_dequant_fp8(const uint8_t* codes, const uint8_t* scales_e8m0, int64_t rows, int64_t k,
