@@ -170,6 +170,7 @@ def main():
     tsW = torch.zeros(1, dtype=torch.float32, device=dev)
     tsA = torch.zeros(1, dtype=torch.float32, device=dev)
     tsA_cal = (A2.abs().max().float() / 2688.0).reshape(1).contiguous()   # a calibrated activation scale
+    tsW_cal = (W2.abs().max().float() / 2688.0).reshape(1).contiguous()
     nvws = torch.empty(F.fp4_quantize_nv_workspace_bytes(4096, 4096), dtype=torch.uint8, device=dev)
     rem_s = torch.empty((4096, 4096 // 16), dtype=torch.uint8, device=dev)
     rem_ts = torch.zeros(1, dtype=torch.float32, device=dev)
@@ -246,6 +247,8 @@ def main():
               "2.5625 B/elem; the tensor-amax read is not counted", "nv_amax_kernel + nv_quantize_kernel"),
         Stage("quantize_nv_A_calibrated", lambda: F.fp4_quantize_nv(cur(A2s), *A2nv, tsA_cal, True, nvws), "hbm",
               M2a * NVB, "2.5625 B/elem (calibrated s_t: one pass)", "nv_quantize_kernel"),
+        Stage("quantize_nv_W_calibrated", lambda: F.fp4_quantize_nv(cur(W2s), *W2nv, tsW_cal, True, nvws), "hbm",
+              M2 * NVB, "2.5625 B/elem (supplied s_t: the second pass alone)", "nv_quantize_kernel"),
         Stage("remap_W", lambda: F.fp4_remap_mx_to_nv(cur(W2mx_rot)[0], cur(W2mx_rot)[1], rem_s, rem_ts, rem_n),
               "hbm", M2 * (1 / 32 + 1 / 16), "0.09375 B/elem (scale bytes in and out)",
               "scale_max_kernel + remap_kernel<false> + remap_kernel<true>"),
@@ -416,6 +419,13 @@ def main():
               "kv_append_prefill16384", "indexer_scores_64x32768"):
         if n in rooflines:
             comps[n + "_GBps"] = rooflines[n]["achieved"]
+    # the two passes of the NV quantize with a computed s_t: pass 2 alone is the
+    # supplied-s_t stage; pass 1 (the tensor amax, 2 B read per element) is the rest
+    for t, n_el in (("W", M2), ("A", M2a)):
+        full, cal = rooflines.get(f"quantize_nv_{t}"), rooflines.get(f"quantize_nv_{t}_calibrated")
+        if full and cal and full["avg_us"] > cal["avg_us"]:
+            comps[f"quantize_nv_{t}_pass1_amax_GBps"] = round(n_el * 2.0 / ((full["avg_us"] - cal["avg_us"]) * 1e-6) / 1e9, 1)
+            comps[f"quantize_nv_{t}_pass2_GBps"] = cal["achieved"]
     if "moe_h4096" in rooflines:
         m = rooflines["moe_h4096"]
         comps["moe_h4096_tokens_per_s"] = round(8192 / (m["avg_us"] * 1e-6), 1)

@@ -1,4 +1,4 @@
-// LDS-staged MXFP4 block tile for gfx950: 256 x 256 outputs per 256-thread
+// LDS-staged MXFP4 block tile for gfx950: 256 x 256 outputs per 512-thread
 // workgroup, K advancing 256 values (8 MX blocks, one 128-byte line per row)
 // per step.
 //

@@ -3,7 +3,9 @@
 # the whole benchmark, HBM traffic (FETCH_SIZE, then WRITE_SIZE, one counter
 # per pass) of the main stages and of a plain 256 MiB device copy that
 # calibrates the counters, and the matrix-core busy cycles, MFMA operation
-# counts and LDS bank conflicts of the MFMA-bound stages.  Raw output goes to $PROFILE_OUT (default
+# counts and LDS bank conflicts of the MFMA-bound stages.  The summaries go to
+# $PROFILE_SUMMARY_DIR (default profiles/), merged with a traffic.json there
+# that was taken on the same kernel sources.  Raw output goes to $PROFILE_OUT (default
 # gpurun_out/profile); profile_summary.py writes the text summaries and
 # profiles/traffic.json that bench.py reads.
 set -euo pipefail
@@ -46,4 +48,4 @@ if [[ " $PARTS " == *" mfma "* ]]; then
     done
 fi
 
-python3 "$R/profile_summary.py" "$OUT" "$R/profiles"
+python3 "$R/profile_summary.py" "$OUT" "${PROFILE_SUMMARY_DIR:-$R/profiles}"
