@@ -48,6 +48,7 @@ plain copy of known size; it is null when the kernel sources changed since.
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import glob
 import json
@@ -66,7 +67,7 @@ MALL_BYTES = 256 << 20
 HERE = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_FILE = os.path.join(HERE, "profiles", "traffic.json")
 MOE_KERNELS = ("quantize_x", "routing", "gate_up", "down", "combine")
-SPACER_CYCLES = 4_000_000
+SPACER_CYCLES = 16_000_000
 TIMING_BLOCKS = 5              # per-stage timing blocks of `steps` launches each
 
 
@@ -304,6 +305,10 @@ def main():
         stages = [s for s in stages if s.name in want]
 
     progress(f"{len(stages)} stages built")
+    # No Python garbage collection while launches are queued: a collection pause
+    # longer than the spacer's cushion lets the device idle inside a timed block
+    # (seen as one block of a stage running ~40x slower).
+    gc.disable()
     for _ in range(args.warmup):
         for s in stages:
             s.launch()
@@ -363,13 +368,15 @@ def main():
             s.moe["set_events"]([None] * 6)
             moe_marks[s.name] = evs
 
+    gc.enable()
     progress("per-stage timing done")
     traffic = load_traffic()
     rooflines = {}
     kernel_rows = []                        # (ms, name, entry) for the dominant-kernel choice
     for s in stages:
         ms = float(np.mean(s.times))
-        e = roofline_entry(s.bound, s.work, ms, s.per_unit, s.kernel, {"best_us": round(s.best * 1e3, 2)})
+        e = roofline_entry(s.bound, s.work, ms, s.per_unit, s.kernel,
+                           {"best_us": round(s.best * 1e3, 2), "block_us": [round(t * 1e3, 2) for t in s.times]})
         if s.moe:
             e["kernels"] = {}
             evs = moe_marks[s.name]
