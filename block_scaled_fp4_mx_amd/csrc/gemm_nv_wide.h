@@ -31,8 +31,7 @@
 // w*64 .. w*64 + 63), so a B slot is refilled as soon as the wave's own reads
 // of it have finished, and the weights get two steps of copy time.  The
 // expansion needs no barrier of its own: the next step's barrier orders it
-// before the fragment reads (it runs at the start of the step, where only the
-// accumulators hold registers).
+// before the fragment reads.
 //
 // Stage layout per K step (128 values):
 //   fp16 A  128 rows x 256 B, 16-byte chunk c of row r at slot c ^ nv_a_swz(r);
@@ -130,31 +129,85 @@ __device__ __forceinline__ void nw_issue_a(NwAStage& st, const NwSrc& S, int ks)
 // Wait until at most one step of B copies (6 per wave) is in flight.
 __device__ __forceinline__ void nw_wait_b_in_flight() { asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); }
 
+
 // Half h (rows 64 h .. 64 h + 63) of one step's A expanded to fp16: each thread
-// expands one 16-group, in the swizzled layout the fragment reads use.
-__device__ __forceinline__ void nw_expand_a_half(const NwAStage& st, uint8_t* a16, int h) {
+// expands one 16-group, in the swizzled layout the fragment reads use.  The
+// load (codes and the group's E4M3 byte) and the store (expansion and write)
+// are separate calls so that the loop can issue them groups apart.
+__device__ __forceinline__ void nw_load_a_half(const NwAStage& st, int h, uint2& code, uint32_t& scale) {
     const int row = h * 64 + (int)(threadIdx.x >> 3), g = (int)(threadIdx.x & 7);
-    const uint2 c = *reinterpret_cast<const uint2*>(&st.c[row * kNwBRow + g * 8]);
-    const _Float16 sg = nv_scale_pair(st.s[row * kNwSRow + g])[0];
-    *reinterpret_cast<h8_t*>(&a16[row * kNwARow + (((2 * g) ^ nv_a_swz(row)) << 4)]) = nv_expand8(c.x, sg);
-    *reinterpret_cast<h8_t*>(&a16[row * kNwARow + (((2 * g + 1) ^ nv_a_swz(row)) << 4)]) = nv_expand8(c.y, sg);
+    code = *reinterpret_cast<const uint2*>(&st.c[row * kNwBRow + g * 8]);
+    scale = st.s[row * kNwSRow + g];
+}
+__device__ __forceinline__ void nw_store_a_half(uint8_t* a16, int h, uint2 code, uint32_t scale) {
+    const int row = h * 64 + (int)(threadIdx.x >> 3), g = (int)(threadIdx.x & 7);
+    const _Float16 sg = nv_scale_pair(scale)[0];
+    *reinterpret_cast<h8_t*>(&a16[row * kNwARow + (((2 * g) ^ nv_a_swz(row)) << 4)]) = nv_expand8(code.x, sg);
+    *reinterpret_cast<h8_t*>(&a16[row * kNwARow + (((2 * g + 1) ^ nv_a_swz(row)) << 4)]) = nv_expand8(code.y, sg);
+}
+__device__ __forceinline__ void nw_expand_a_half(const NwAStage& st, uint8_t* a16, int h) {
+    uint2 code;
+    uint32_t scale;
+    nw_load_a_half(st, h, code, scale);
+    nw_store_a_half(a16, h, code, scale);
 }
 
 __device__ __forceinline__ uint32_t nw_word(const uint4& c, int i) {
     return i == 0 ? c.x : (i == 1 ? c.y : (i == 2 ? c.z : c.w));
 }
 
+// A fragments 2g and 2g + 1 (those below MF) of sub-step i, from the step's
+// fp16 A slot.
+template <int MF>
+__device__ __forceinline__ void nw_read_pair(h8_t (&a)[2], const uint8_t* ab, int i, int g, int lr, int lq) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int mf = 2 * g + u;
+        if (mf < MF) {
+            const int row = mf * 16 + lr;
+            a[u] = *reinterpret_cast<const h8_t*>(&ab[row * kNwARow + (((4 * lq + i) ^ nv_a_swz(row)) << 4)]);
+        }
+    }
+}
+
+// The lane's 32 codes of its row in each of the wave's B fragments of one
+// step, and the row's two E4M3 group scales as fp16.
+__device__ __forceinline__ void nw_read_b(const NwBStage& st, uint4 (&c)[4], h2_t (&sp)[4], int wave, int lr, int lq) {
+#pragma unroll
+    for (int nf = 0; nf < 4; ++nf) {
+        const int row = wave * 64 + nf * 16 + lr;
+        c[nf] = *reinterpret_cast<const uint4*>(&st.b[(row & ~15) * kNwBRow + lq * 256 + lr * 16]);
+        sp[nf] = nv_scale_pair(*reinterpret_cast<const uint16_t*>(&st.s[row * kNwSRow + lq * 2]));
+    }
+}
+
+constexpr int kNwAhead = 2;   // groups by which A fragment reads run ahead of their MFMAs
+
 // Full K loop of one tile for the MF A fragments (16 rows each) that hold rows
 // of the problem.  acc[mf][nf]: A rows mf*16 .., B rows wave*64 + nf*16 ..;
 // D row = A row, D column = B row.  Every wave takes part in the copies, the A
 // expansion and the barriers; A rows of fragments past MF are not expanded.
 // MF is the same for the whole workgroup (a tile without rows does nothing).
+//
+// Inside a step the wave works through T = 4 * NG groups (sub-step i, pair g
+// of A fragments: 8 MFMAs each for a full pair).  A group's A fragments are
+// read from LDS two groups ahead (a ring of three register pairs), so the read
+// latency hides behind the MFMAs of the two groups before it; each sub-step's
+// B fragments are expanded during the groups of the sub-step before it (two
+// register sets).  Group boundaries are scheduling barriers, which keeps the
+// compiler from pulling the reads back next to their MFMAs.  The step's extra
+// work rides in its first groups: group 0 also reads the codes of the next
+// step's A, group 1 expands them into the other fp16 slot and, once every LDS
+// read issued so far has returned (the wave's reads of its B slot among them),
+// issues the copies of B(ks + 2) into that slot.
 template <int MF>
 __device__ __forceinline__ void nw_mainloop(NwSmem& sm, const NwSrc& S, int nsteps, v4f acc[kNwMf][4]) {
     const int lane = threadIdx.x & 63, wave = nw_wave();
     const int lr = lane & 15, lq = lane >> 4;
     static_assert(MF >= 1 && MF <= kNwMf, "fragment count");
     constexpr int kHalves = MF > 4 ? 2 : 1;   // expanded 64-row halves of A
+    constexpr int NG = (MF + 1) / 2;          // A fragment pairs per sub-step
+    constexpr int T = 4 * NG;                 // groups per step
     // copy order A(0), B(0), A(1), B(1), then per step A(ks + 2), B(ks + 2): the
     // wait at the top of step ks (for B(ks) and A(ks + 1)) leaves B(ks + 1) in flight
     nw_issue_a(sm.a[0], S, 0);
@@ -174,45 +227,55 @@ __device__ __forceinline__ void nw_mainloop(NwSmem& sm, const NwSrc& S, int nste
             wait_vm_zero();
         __syncthreads();
         const int cur = ks & 1, nxt = cur ^ 1;
+        const bool more = ks + 1 < nsteps;
         if (ks + 2 < nsteps) nw_issue_a(sm.a[cur], S, ks + 2);
-        const NwBStage& st = sm.b[cur];
         const uint8_t* ab = sm.a16[cur];
-        // B: the lane's 32 codes of its row in each of the wave's fragments
         uint4 c[4];
         h2_t sp[4];
+        nw_read_b(sm.b[cur], c, sp, wave, lr, lq);
+        h8_t af[kNwAhead + 1][2];
 #pragma unroll
-        for (int nf = 0; nf < 4; ++nf) {
-            const int row = wave * 64 + nf * 16 + lr;
-            c[nf] = *reinterpret_cast<const uint4*>(&st.b[(row & ~15) * kNwBRow + lq * 256 + lr * 16]);
-            sp[nf] = nv_scale_pair(*reinterpret_cast<const uint16_t*>(&st.s[row * kNwSRow + lq * 2]));
-        }
-        // the next step's A (its codes landed with this step's wait)
-        if (ks + 1 < nsteps)
+        for (int t = 0; t < kNwAhead; ++t) nw_read_pair<MF>(af[t], ab, t / NG, t % NG, lr, lq);
+        h8_t bx[2][4];
 #pragma unroll
-            for (int h = 0; h < kHalves; ++h) nw_expand_a_half(sm.a[nxt], sm.a16[nxt], h);
-        // B(ks + 2) into the slot just read: the wave's own rows, so its own
-        // reads are all that must finish first
-        if (ks + 2 < nsteps) {
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            nw_issue_b(sm.b[cur], S, ks + 2);
-        }
+        for (int nf = 0; nf < 4; ++nf) bx[0][nf] = nv_expand8(c[nf].x, sp[nf][0]);
+        __builtin_amdgcn_sched_barrier(0);
+        uint2 acode[kHalves];
+        uint32_t ascale[kHalves];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            // the sub-step's A fragment reads go out first and land while B is expanded
-            h8_t a[MF];
-#pragma unroll
-            for (int mf = 0; mf < MF; ++mf) {
-                const int row = mf * 16 + lr;
-                a[mf] = *reinterpret_cast<const h8_t*>(&ab[row * kNwARow + (((4 * lq + i) ^ nv_a_swz(row)) << 4)]);
+        for (int t = 0; t < T; ++t) {
+            const int i = t / NG, g = t % NG;
+            if (t == 1 && ks + 2 < nsteps) {
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                nw_issue_b(sm.b[cur], S, ks + 2);
             }
-            h8_t bx[4];
+            if (t + kNwAhead < T)
+                nw_read_pair<MF>(af[(t + kNwAhead) % (kNwAhead + 1)], ab, (t + kNwAhead) / NG, (t + kNwAhead) % NG,
+                                 lr, lq);
+            if (t == 0 && more) {
 #pragma unroll
-            for (int nf = 0; nf < 4; ++nf) bx[nf] = nv_expand8(nw_word(c[nf], i), sp[nf][i >> 1]);
+                for (int h = 0; h < kHalves; ++h) nw_load_a_half(sm.a[nxt], h, acode[h], ascale[h]);
+            }
+            if (t == 1 && more) {
 #pragma unroll
-            for (int mf = 0; mf < MF; ++mf)
+                for (int h = 0; h < kHalves; ++h) nw_store_a_half(sm.a16[nxt], h, acode[h], ascale[h]);
+            }
+            if (i + 1 < 4) {
 #pragma unroll
                 for (int nf = 0; nf < 4; ++nf)
-                    acc[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mf], bx[nf], acc[mf][nf], 0, 0, 0);
+                    if (nf % NG == g)
+                        bx[(i + 1) & 1][nf] = nv_expand8(nw_word(c[nf], i + 1), sp[nf][(i + 1) >> 1]);
+            }
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int mf = 2 * g + u;
+                if (mf < MF)
+#pragma unroll
+                    for (int nf = 0; nf < 4; ++nf)
+                        acc[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[t % (kNwAhead + 1)][u], bx[i & 1][nf],
+                                                                             acc[mf][nf], 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 }
