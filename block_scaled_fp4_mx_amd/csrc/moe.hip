@@ -294,6 +294,25 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
     return (g / (1.0f + expf(-g))) * u;
 }
 
+// Routing of the rows a down tile stores: a lane loads the slot and routing
+// weight of one routed position (nothing past the segment), ahead of the K
+// loop, so that the epilogue takes them from a register (v_readlane) instead
+// of two dependent loads per stored row.
+struct RowRoute {
+    int32_t slot = 0;
+    float wgt = 0.f;
+    __device__ __forceinline__ void load(const GemmParams& p, int64_t pos, int64_t rend, bool active) {
+        if (active && pos < rend) {
+            slot = p.perm[pos];
+            wgt = p.weights[slot];
+        }
+    }
+    __device__ __forceinline__ int64_t slot_of(int src) const { return __builtin_amdgcn_readlane(slot, src); }
+    __device__ __forceinline__ float wgt_of(int src) const {
+        return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), src));
+    }
+};
+
 template <int FMT>
 __global__ __launch_bounds__(kThreads) void moe_gate_up_kernel(GemmParams p) {
     const int tile = blockIdx.y;
@@ -634,6 +653,9 @@ __global__ __launch_bounds__(kTileThreads, 1) void moe_down_mx256_kernel(GemmPar
     A.soff = (uint32_t)(inj ? p.perm[spos] : spos) * kblocks;
     mx_slab_src(B, p.w2c + (int64_t)e * H * (I / 2), p.w2s + (int64_t)e * H * (I / 32), n0, H, I / 2, I / 32);
 
+    // lane L < 32 routes row wave + 8 (L % 16) of band L / 16 (the rows the wave stores)
+    RowRoute route;
+    route.load(p, r0 + (lane >> 4 & 1) * 128 + wave + 8 * (lane & 15), rend, lane < 32);
     v4f acc[kWaveFragsN][8];
 #pragma unroll
     for (int j = 0; j < kWaveFragsN; ++j)
@@ -668,11 +690,12 @@ __global__ __launch_bounds__(kTileThreads, 1) void moe_down_mx256_kernel(GemmPar
                         make_float4(acc[j][i][0], acc[j][i][1], acc[j][i][2], acc[j][i][3]);
         }
         __syncthreads();
-        for (int rr = wave; rr < 128; rr += kTileThreads / 64) {
+        for (int k = 0; k < 128 / (kTileThreads / 64); ++k) {
+            const int rr = wave + k * (kTileThreads / 64);
             const int64_t pos = r0 + band * 128 + rr;
             if (pos >= rend) break;     // rows are in order: the rest of this wave's rows are past the end too
-            const int64_t slot = p.perm[pos];
-            const float wgt = p.weights[slot];
+            const int64_t slot = route.slot_of(band * 16 + k);
+            const float wgt = route.wgt_of(band * 16 + k);
             const float4 v = *reinterpret_cast<const float4*>(&ysm[rr * kYRow + lane * 4]);
             *reinterpret_cast<float4*>(p.ybuf + slot * H + n0 + lane * 4) =
                 make_float4(__fmul_rn(wgt, v.x), __fmul_rn(wgt, v.y), __fmul_rn(wgt, v.z), __fmul_rn(wgt, v.w));
@@ -854,6 +877,9 @@ __global__ __launch_bounds__(kNvThreads, 1) void moe_down_nv_kernel(GemmParams p
     for (int mf = 0; mf < 4; ++mf)
 #pragma unroll
         for (int nf = 0; nf < 2; ++nf) acc[mf][nf] = v4f{0.f, 0.f, 0.f, 0.f};
+    // lane L < TM / 8 routes row wave + 8 L (the rows the wave stores)
+    RowRoute route;
+    route.load(p, r0 + wave + 8 * lane, rend, lane < TM / 8);
     nv_tile_mainloop_rows(sm, S, (int)(I / 256), acc, rend - r0);
     __syncthreads();   // the staging tile reuses the stages
 
@@ -873,11 +899,12 @@ __global__ __launch_bounds__(kNvThreads, 1) void moe_down_nv_kernel(GemmParams p
                 if (p.dbg.y && pos < rend) p.dbg.y[(int64_t)p.perm[pos] * H + n0 + cl] = y;
             }
     __syncthreads();
-    for (int rr = wave; rr < TM; rr += kNvThreads / 64) {
+    for (int k = 0; k < TM / (kNvThreads / 64); ++k) {
+        const int rr = wave + k * (kNvThreads / 64);
         const int64_t pos = r0 + rr;
         if (pos >= rend) break;     // rows are in order: the rest of this wave's rows are past the end too
-        const int64_t slot = p.perm[pos];
-        const float wgt = p.weights[slot];
+        const int64_t slot = route.slot_of(k);
+        const float wgt = route.wgt_of(k);
         const float4 v = *reinterpret_cast<const float4*>(&ysm[rr * kNvYRow + lane * 4]);
         *reinterpret_cast<float4*>(p.ybuf + slot * H + n0 + lane * 4) =
             make_float4(__fmul_rn(wgt, v.x), __fmul_rn(wgt, v.y), __fmul_rn(wgt, v.z), __fmul_rn(wgt, v.w));
@@ -1012,6 +1039,8 @@ __global__ __launch_bounds__(kNvThreads, 1) void moe_gate_up_nvw_kernel(GemmPara
 // fp32 result leaves through LDS in two passes of 64 rows.
 constexpr int kNwYRow = kNwN + 4;   // fp32 row pitch of the combine staging tile
 constexpr int kNwYRows = 64;        // rows per staging pass
+static_assert(kNwM == 2 * kNwYRows && kNwYRows / (kNvThreads / 64) == 8,
+              "the wide down tile's row routing covers two passes of eight rows per wave");
 
 __global__ __launch_bounds__(kNvThreads, 1) void moe_down_nvw_kernel(GemmParams p) {
     __shared__ __align__(16) NwSmem sm;
@@ -1052,6 +1081,9 @@ __global__ __launch_bounds__(kNvThreads, 1) void moe_down_nvw_kernel(GemmParams 
     for (int mf = 0; mf < kNwMf; ++mf)
 #pragma unroll
         for (int nf = 0; nf < 4; ++nf) acc[mf][nf] = v4f{0.f, 0.f, 0.f, 0.f};
+    // lane L < 16 routes row wave + 8 (L % 8) of staging pass L / 8 (the rows the wave stores)
+    RowRoute route;
+    route.load(p, r0 + (lane >> 3 & 1) * kNwYRows + wave + 8 * (lane & 7), rend, lane < 16);
     nw_mainloop_rows(sm, S, (int)(I / kNwK), acc, rend - r0);
 
     const float yscale = __fmul_rn(p.act_ts[1], p.w2ts[e]);
@@ -1074,11 +1106,12 @@ __global__ __launch_bounds__(kNvThreads, 1) void moe_down_nvw_kernel(GemmParams 
                     if (p.dbg.y && pos < rend && n0 + cl < H) p.dbg.y[(int64_t)p.perm[pos] * H + n0 + cl] = y;
                 }
         __syncthreads();
-        for (int rr = wave; rr < kNwYRows; rr += kNvThreads / 64) {
+        for (int k = 0; k < kNwYRows / (kNvThreads / 64); ++k) {
+            const int rr = wave + k * (kNvThreads / 64);
             const int64_t pos = r0 + pass * kNwYRows + rr;
             if (pos >= rend) break;     // rows are in order: the rest of this wave's rows are past the end too
-            const int64_t slot = p.perm[pos];
-            const float wgt = p.weights[slot];
+            const int64_t slot = route.slot_of(pass * 8 + k);
+            const float wgt = route.wgt_of(pass * 8 + k);
 #pragma unroll
             for (int hh = 0; hh < kNwN / 256; ++hh) {
                 const int col = hh * 256 + lane * 4;
@@ -1092,7 +1125,11 @@ __global__ __launch_bounds__(kNvThreads, 1) void moe_down_nvw_kernel(GemmParams 
 }
 
 // out[t] = bf16(sum over j of w * y of slot t*topk + j), summed in fp32 in
-// order j = 0 .. topk-1 over the slots whose expert id is in range.
+// order j = 0 .. topk-1 over the slots whose expert id is in range.  A thread
+// issues the loads of up to kCombineBatch slots at once (rows of unrouted
+// slots are read but never added: a skipped slot leaves the sum as it is, a
+// -0 included).
+constexpr int kCombineBatch = 8;
 __global__ __launch_bounds__(kThreads) void combine_kernel(const float4* __restrict__ ybuf,
                                                            const int32_t* __restrict__ ids, int topk, int E,
                                                            int64_t T, int64_t H4, uint2* __restrict__ out) {
@@ -1101,14 +1138,25 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const float4* __restr
     for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride) {
         const int64_t t = i / H4, c = i - t * H4;
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int j = 0; j < topk; ++j) {
-            const int64_t slot = t * topk + j;
-            if ((unsigned)ids[slot] >= (unsigned)E) continue;
-            const float4 v = ybuf[slot * H4 + c];
-            acc.x = __fadd_rn(acc.x, v.x);
-            acc.y = __fadd_rn(acc.y, v.y);
-            acc.z = __fadd_rn(acc.z, v.z);
-            acc.w = __fadd_rn(acc.w, v.w);
+        for (int j0 = 0; j0 < topk; j0 += kCombineBatch) {
+            float4 v[kCombineBatch];
+            bool ok[kCombineBatch];
+#pragma unroll
+            for (int u = 0; u < kCombineBatch; ++u) {
+                const int j = j0 + u;
+                const int64_t slot = t * topk + min(j, topk - 1);
+                ok[u] = j < topk && (unsigned)ids[slot] < (unsigned)E;
+                v[u] = ybuf[slot * H4 + c];
+            }
+#pragma unroll
+            for (int u = 0; u < kCombineBatch; ++u) {
+                if (ok[u]) {
+                    acc.x = __fadd_rn(acc.x, v[u].x);
+                    acc.y = __fadd_rn(acc.y, v[u].y);
+                    acc.z = __fadd_rn(acc.z, v[u].z);
+                    acc.w = __fadd_rn(acc.w, v[u].w);
+                }
+            }
         }
         out[i] = make_uint2(f32_to_bf16_rne(acc.x) | (f32_to_bf16_rne(acc.y) << 16),
                             f32_to_bf16_rne(acc.z) | (f32_to_bf16_rne(acc.w) << 16));
