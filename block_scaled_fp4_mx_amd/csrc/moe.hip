@@ -575,6 +575,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void moe_gate_up_mx256_kernel(Gemm
     uint16_t* hsm = reinterpret_cast<uint16_t*>(&sm.codes[0]);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
+        if (r0 + wm * 128 + i * 16 >= rend) break;    // fragments past the segment (uniform): no h rows
         const int rl = wm * 128 + i * 16 + lr;
         const int64_t pos = r0 + rl;
         const bool dbg_row = pos < rend && (p.dbg.gate_up || p.dbg.h_bf16);
@@ -604,12 +605,13 @@ __global__ __launch_bounds__(kTileThreads, 1) void moe_gate_up_mx256_kernel(Gemm
     for (int q = 0; q < (kTileM * kGu2Cols / 8) / kTileThreads; ++q) {
         const int unit = threadIdx.x + q * kTileThreads;
         const int rl = unit >> 4, cu = unit & 15;
+        const int64_t pos = r0 + rl;
+        if (pos >= rend) break;      // the rows of later units are further down
         const uint4 v = *reinterpret_cast<const uint4*>(&hsm[h_unit_off(rl, cu)]);
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
         uint32_t sb;
         const uint32_t packed = mx_quant8(w, sb);
-        const int64_t pos = r0 + rl;
-        if (pos < rend) {
+        {
             const int64_t col = c0 + cu * 8;
             reinterpret_cast<uint32_t*>(p.hc + pos * (I / 2) + col / 2)[0] = packed;
             const bool lead = (cu & 3) == 0;
@@ -986,7 +988,8 @@ __global__ __launch_bounds__(kNvThreads, 1) void moe_gate_up_nvw_kernel(GemmPara
     const float gscale = injected ? 1.0f : __fmul_rn(p.act_ts[0], p.w13ts[e]);
     uint16_t* hsm = reinterpret_cast<uint16_t*>(&sm);      // 128 rows x 256 bf16
 #pragma unroll
-    for (int mf = 0; mf < kNwMf; ++mf)
+    for (int mf = 0; mf < kNwMf; ++mf) {
+        if (r0 + mf * 16 >= rend) break;    // fragments past the segment (uniform): no h rows
 #pragma unroll
         for (int nf = 0; nf < 2; ++nf)
 #pragma unroll
@@ -1007,6 +1010,7 @@ __global__ __launch_bounds__(kNvThreads, 1) void moe_gate_up_nvw_kernel(GemmPara
                     if (p.dbg.h_bf16) static_cast<uint16_t*>(p.dbg.h_bf16)[slot * I + c0 + cl] = (uint16_t)hb;
                 }
             }
+    }
     __syncthreads();
     // quantize the 128 x 256 h tile: unit = 8 consecutive columns of one row; a
     // 16-group spans 2 consecutive lanes
