@@ -110,7 +110,7 @@ class _Args:
             raise TypeError(f"{fn}: {name} must be a torch tensor, got {type(t).__name__}")
         if t.dtype not in dtypes:
             raise TypeError(f"{fn}: {name} must be {' or '.join(str(d) for d in dtypes)}, got {t.dtype}")
-        if t.numel() and t.dim() and t.stride(-1) != 1:
+        if t.numel() and t.dim() and t.size(-1) > 1 and t.stride(-1) != 1:
             raise ValueError(f"{fn}: {name} must be contiguous along its last axis")
         if dense and t.numel() and not t.is_contiguous():
             raise ValueError(f"{fn}: {name} must be contiguous")

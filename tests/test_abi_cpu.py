@@ -208,6 +208,15 @@ def test_binding_rejects_what_the_c_side_would_misread(F):
     with pytest.raises(TypeError, match="uint8"):
         F.fp4_gemm(F.FMT_MX, u8(8, 32), u8(8, 2), torch.zeros((8, 32), dtype=torch.int8), u8(8, 2),
                    torch.zeros((8, 8)))
+    # top-1 routing: a [T, 1] id tensor is dense whatever the stride of its size-1
+    # axis (numpy may hand over 0 there); only the device check remains to fail
+    import numpy as np
+    ids1 = torch.from_numpy(np.ascontiguousarray((np.arange(8, dtype=np.int32) % 4)[:, None]))
+    w1 = torch.from_numpy(np.ascontiguousarray(np.ones(8, np.float32)[:, None]))
+    assert ids1.stride(-1) == 0 and w1.stride(-1) == 0
+    with pytest.raises(ValueError, match="GPU"):
+        F.fp4_moe_grouped_gemm(F.FMT_MX, x, ids1, w1, 4, 128, u8(4, 256, 32), u8(4, 256, 2), u8(4, 64, 64),
+                               u8(4, 64, 4), x.clone(), u8(64))
 
 
 def test_binding_checks_operand_shapes():

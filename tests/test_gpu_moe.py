@@ -85,6 +85,31 @@ def test_moe_decode_nv_segments():
     _all_checks(case, oracle_expect(case, np.arange(case.T), eq, calibrate_h=True))
 
 
+def _segment_case(fmt, seed, counts, H, I):
+    """topk 1, expert e routed exactly counts[e] tokens (in shuffled order)."""
+    counts = np.asarray(counts)
+    ids = np.repeat(np.arange(len(counts), dtype=np.int32), counts)
+    np.random.default_rng(seed).shuffle(ids)
+    case, eq = _small_case(fmt, seed, len(ids), H, I, len(counts), 1, ids=np.ascontiguousarray(ids[:, None]))
+    assert (np.bincount(case.ids.ravel(), minlength=len(counts)) == counts).all()
+    return case, eq
+
+
+@pytest.mark.parametrize("fmt,counts,H", [
+    # 256-row MX tiles: 16-row fragments, 128-row bands, a second tile of one row
+    ("mx", [1, 15, 16, 17, 127, 128, 129, 255, 257], 512),
+    # 128-row wide NV tiles: 16-row fragments, 64-row staging passes, a second tile of one row
+    ("nv", [1, 15, 16, 17, 63, 64, 65, 127, 129], 256),
+])
+def test_moe_segments_at_fragment_boundaries(fmt, counts, H):
+    """Expert segments that end exactly on, just past and just before a 16-row
+    fragment, a row band or staging pass, and a whole tile: the epilogues work
+    only on the fragments and rows inside the segment, and the down tiles take
+    each stored row's slot from a per-lane load."""
+    case, eq = _segment_case(fmt, 107, counts, H, H)
+    _all_checks(case, oracle_expect(case, np.arange(case.T), eq, calibrate_h=True))
+
+
 def test_moe_single_expert_topk1():
     T, H, I, E = 33, 128, 256, 5
     ids = np.full((T, 1), 3, np.int32)
