@@ -157,6 +157,15 @@ def test_gemm_nv_tiled_short_k(m, n, k):
     _nv_case(W.random_linear(m + n + k, m, n, k, outlier_p=0.01), torch.float32)
 
 
+@pytest.mark.parametrize("r", [16, 29, 48, 61, 80, 93, 112])
+def test_gemm_nv_tiled_last_tile_fragments(r):
+    """The tiled NV path whose last row tile holds 1 to 7 row fragments of 16
+    (its K loop is instantiated per fragment count, odd counts with half a
+    fragment pair), some with a ragged last fragment; 16 tiles, three K steps."""
+    m, n, k = 128 + r, 4096, 384
+    _nv_case(W.random_linear(7000 + r, m, n, k, outlier_p=0.01), torch.float32)
+
+
 def test_gemm_nv_4096_sampled():
     """NVFP4 GEMM at 4096^3 (the tiled path): every output of 32 sampled rows
     and 32 sampled columns within the bound."""
