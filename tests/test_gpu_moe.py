@@ -110,6 +110,14 @@ def test_moe_segments_at_fragment_boundaries(fmt, counts, H):
     _all_checks(case, oracle_expect(case, np.arange(case.T), eq, calibrate_h=True))
 
 
+@pytest.mark.parametrize("fmt", ["mx", "nv"])
+def test_moe_topk_above_eight(fmt):
+    """Top-12 routing over 16 experts: the combine sums a token's slots in two
+    batches of loads (slots 0-7, then 8-11), in slot order."""
+    case, eq = _small_case(fmt, 108, 40, 256, 256, 16, 12)
+    _all_checks(case, oracle_expect(case, np.arange(case.T), eq, calibrate_h=True))
+
+
 def test_moe_single_expert_topk1():
     T, H, I, E = 33, 128, 256, 5
     ids = np.full((T, 1), 3, np.int32)
