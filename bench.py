@@ -176,6 +176,7 @@ def main():
     rem_s = torch.empty((4096, 4096 // 16), dtype=torch.uint8, device=dev)
     rem_ts = torch.zeros(1, dtype=torch.float32, device=dev)
     rem_n = torch.zeros(1, dtype=torch.int32, device=dev)
+    smax_ws = torch.empty(F.fp4_scale_max_workspace_bytes(4096, 4096), dtype=torch.uint8, device=dev)
     deq = torch.empty((4096, 4096), dtype=torch.bfloat16, device=dev)
     fp8_v = torch.empty((4096, 4096), dtype=torch.uint8, device=dev)
     fp8_s = torch.empty((4096, 4096 // 32), dtype=torch.uint8, device=dev)
@@ -250,13 +251,14 @@ def main():
               M2a * NVB, "2.5625 B/elem (calibrated s_t: one pass)", "nv_quantize_kernel"),
         Stage("quantize_nv_W_calibrated", lambda: F.fp4_quantize_nv(cur(W2s), *W2nv, tsW_cal, True, nvws), "hbm",
               M2 * NVB, "2.5625 B/elem (supplied s_t: the second pass alone)", "nv_quantize_kernel"),
-        Stage("remap_W", lambda: F.fp4_remap_mx_to_nv(cur(W2mx_rot)[0], cur(W2mx_rot)[1], rem_s, rem_ts, rem_n),
+        Stage("remap_W", lambda: F.fp4_remap_mx_to_nv(cur(W2mx_rot)[0], cur(W2mx_rot)[1], rem_s, rem_ts, rem_n,
+                                                      workspace=smax_ws),
               "hbm", M2 * (1 / 32 + 1 / 16), "0.09375 B/elem (scale bytes in and out)",
-              "scale_max_kernel + remap_kernel<false> + remap_kernel<true>"),
+              "scale_max_kernel + remap_kernel"),
         Stage("dequant_fp8_W", lambda: F.fp4_mx_dequant_fp8(cur(W2mx_rot)[0], cur(W2mx_rot)[1], fp8_v, fp8_ts, fp8_n,
-                                                            fp8_s), "hbm", M2 * (0.5 + 1 / 32 + 1 + 1 / 32),
+                                                            fp8_s, workspace=smax_ws), "hbm", M2 * (0.5 + 1 / 32 + 1 + 1 / 32),
               "1.5625 B/elem (codes + UE8M0 scale in, E4M3 value + E4M3 block scale out)",
-              "scale_max_kernel + fp8_dequant_kernel<false> + fp8_dequant_kernel<true>"),
+              "scale_max_kernel + fp8_dequant_kernel"),
         Stage("dequant_mx_W", lambda: F.fp4_dequant(F.FMT_MX, cur(W2mx_rot)[0], cur(W2mx_rot)[1], None, deq), "hbm",
               M2 * (0.5 + 1 / 32 + 2), "2.53125 B/elem (codes + scale in, bf16 out)", "dequant_kernel"),
         Stage("fake_quant_mx_W", lambda: F.fp4_fake_quant(F.FMT_MX, cur(W2s), fq_out), "hbm", M2 * 4.0,

@@ -16,6 +16,7 @@ import torch
 __all__ = [
     "lib", "Fp4Error", "FMT_MX", "FMT_NV", "DT_BF16", "DT_F32",
     "fp4_quantize_mx", "fp4_quantize_nv", "fp4_quantize_nv_workspace_bytes", "fp4_quantize_nv_noalloc", "fp4_remap_mx_to_nv",
+    "fp4_scale_max_workspace_bytes",
     "fp4_dequant", "fp4_gemm", "fp4_quantize_mxfp8", "fp4_mx_to_mxfp8", "fp4_mx_dequant_fp8", "fp4_gemm_w4a8", "fp4_fake_quant",
     "fp4_ste_backward", "fp4_kv_append_mx", "fp4_moe_grouped_gemm", "fp4_moe_workspace_bytes", "MoeDebug",
     "fp4_abi_version", "LIB_PATH",
@@ -44,7 +45,8 @@ _SIGS = {
     "fp4_quantize_nv": (_i32, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _i32, _vp, _sz, _vp]),
     "fp4_quantize_nv_workspace_bytes": (_sz, [_i64, _i64]),
     "fp4_quantize_nv_noalloc": (_i32, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _i32, _vp]),
-    "fp4_remap_mx_to_nv": (_i32, [_vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp]),
+    "fp4_remap_mx_to_nv": (_i32, [_vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "fp4_scale_max_workspace_bytes": (_sz, [_i64, _i64]),
     "fp4_dequant": (_i32, [_i32, _vp, _vp, _vp, _i64, _i64, _vp, _i32, _i64, _vp]),
     "fp4_gemm": (_i32, [_i32, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _i32, _i64, _vp]),
     "fp4_kv_append_mx": (_i32, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _i64, _vp]),
@@ -52,7 +54,7 @@ _SIGS = {
     "fp4_ste_backward": (_i32, [_vp, _i32, _i64, _i64, _i64, _vp, _i64, _i32, _vp]),
     "fp4_quantize_mxfp8": (_i32, [_vp, _i64, _i64, _i64, _vp, _vp, _vp]),
     "fp4_mx_to_mxfp8": (_i32, [_vp, _i64, _i64, _vp, _vp]),
-    "fp4_mx_dequant_fp8": (_i32, [_vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp]),
+    "fp4_mx_dequant_fp8": (_i32, [_vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "fp4_gemm_w4a8": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _i32, _i64, _vp]),
     "fp4_moe_grouped_gemm": (_i32, [_i32, _vp, _i64, _i64, _vp, _vp, _i32, _i32, _i64, _vp, _vp, _vp,
                                      _vp, _vp, _vp, _vp, _vp, _vp, _sz, _c.POINTER(MoeDebug), _vp]),
@@ -60,10 +62,17 @@ _SIGS = {
 }
 
 
+ABI_VERSION = 2          # the signatures below
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'`")
     h = _c.CDLL(LIB_PATH)
+    h.fp4_abi_version.restype = _i32
+    if h.fp4_abi_version() != ABI_VERSION:
+        raise ImportError(f"{LIB_PATH} has ABI version {h.fp4_abi_version()}, this binding needs {ABI_VERSION}: "
+                          "rebuild it")
     for name, (res, args) in _SIGS.items():
         f = getattr(h, name)
         f.restype, f.argtypes = res, args
@@ -201,7 +210,12 @@ def fp4_quantize_nv_noalloc(x, codes, scales, tensor_scale, tensor_scale_is_inpu
                                            int(bool(tensor_scale_is_input)), _stream(stream)))
 
 
-def fp4_remap_mx_to_nv(codes, scales_e8m0, scales_e4m3, tensor_scale, n_inexact, rows=None, k=None, stream=None):
+def fp4_scale_max_workspace_bytes(rows: int, k: int) -> int:
+    return lib.fp4_scale_max_workspace_bytes(rows, k)
+
+
+def fp4_remap_mx_to_nv(codes, scales_e8m0, scales_e4m3, tensor_scale, n_inexact, workspace=None, rows=None, k=None,
+                       stream=None):
     rows = codes.shape[0] if rows is None else rows
     k = codes.shape[1] * 2 if k is None else k
     fn = "fp4_remap_mx_to_nv"
@@ -210,9 +224,12 @@ def fp4_remap_mx_to_nv(codes, scales_e8m0, scales_e4m3, tensor_scale, n_inexact,
         a(nm, t, _U8)
     a("tensor_scale", tensor_scale, _F32)
     a("n_inexact", n_inexact, _I32)
+    a("workspace", workspace, _U8, optional=True)
+    wsb = 0 if workspace is None else workspace.numel()
     a.on_device()
     _check("fp4_remap_mx_to_nv", lib.fp4_remap_mx_to_nv(_ptr(codes), _ptr(scales_e8m0), rows, k, _ptr(scales_e4m3),
-                                                        _ptr(tensor_scale), _ptr(n_inexact), _stream(stream)))
+                                                        _ptr(tensor_scale), _ptr(n_inexact), _ptr(workspace), wsb,
+                                                        _stream(stream)))
 
 
 def fp4_dequant(fmt, codes, scales, tensor_scale, out, rows=None, k=None, ld_out=None, stream=None):
@@ -329,7 +346,7 @@ def fp4_mx_to_mxfp8(codes, codes8, rows=None, k=None, stream=None):
 
 
 def fp4_mx_dequant_fp8(codes, scales_e8m0, values_e4m3, tensor_scale, n_inexact, block_scales_e4m3=None,
-                       rows=None, k=None, stream=None):
+                       workspace=None, rows=None, k=None, stream=None):
     rows = codes.shape[0] if rows is None else rows
     k = codes.shape[1] * 2 if k is None else k
     fn = "fp4_mx_dequant_fp8"
@@ -339,12 +356,14 @@ def fp4_mx_dequant_fp8(codes, scales_e8m0, values_e4m3, tensor_scale, n_inexact,
     a("block_scales_e4m3", block_scales_e4m3, _U8, optional=True)
     a("tensor_scale", tensor_scale, _F32)
     a("n_inexact", n_inexact, _I32)
+    a("workspace", workspace, _U8, optional=True)
+    wsb = 0 if workspace is None else workspace.numel()
     _shape(fn, "scales_e8m0", scales_e8m0, (rows, k // 32), rows_at_least=True)
     _shape(fn, "values_e4m3", values_e4m3, (rows, k), rows_at_least=True)
     a.on_device()
     _check("fp4_mx_dequant_fp8", lib.fp4_mx_dequant_fp8(_ptr(codes), _ptr(scales_e8m0), rows, k, _ptr(values_e4m3),
                                                         _ptr(block_scales_e4m3), _ptr(tensor_scale), _ptr(n_inexact),
-                                                        _stream(stream)))
+                                                        _ptr(workspace), wsb, _stream(stream)))
 
 
 def fp4_gemm_w4a8(a_codes8, a_scales, b_codes, b_scales, c, m=None, n=None, k=None, ldc=None, stream=None):

@@ -54,11 +54,23 @@ int check_ld(int64_t ld, int64_t width, const char* name) {
 
 size_t nv_ws_bytes() { return 4096; }   // pass-1 partial maxima of the tensor amax (1024 words)
 
+// The remap's and FP8 dequant's optional workspace: NULL (with 0 bytes) or at
+// least fp4_scale_max_workspace_bytes(rows, k) bytes.
+int check_scale_max_ws(const void* ws, size_t bytes, int64_t rows, int64_t k) {
+    if (ws == nullptr) {
+        FP4_REQUIRE(bytes == 0, FP4_ERR_WORKSPACE, "workspace is NULL but workspace_bytes=%zu", bytes);
+        return FP4_OK;
+    }
+    const size_t need = fp4::scale_max_workspace_bytes(rows, k);
+    FP4_REQUIRE(bytes >= need, FP4_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, bytes);
+    return FP4_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
-int fp4_abi_version(void) { return 1; }
+int fp4_abi_version(void) { return 2; }
 
 const char* fp4_status_string(int status) {
     switch (status) {
@@ -138,8 +150,13 @@ int fp4_quantize_nv_noalloc(const void* x_bf16, int64_t rows, int64_t k, int64_t
                       "fp4_quantize_nv_noalloc launch");
 }
 
+size_t fp4_scale_max_workspace_bytes(int64_t rows, int64_t k) {
+    return rows > 0 && k >= 32 ? fp4::scale_max_workspace_bytes(rows, k) : 0;
+}
+
 int fp4_remap_mx_to_nv(const uint8_t* codes, const uint8_t* scales_e8m0, int64_t rows, int64_t k,
-                       uint8_t* scales_e4m3, float* tensor_scale, int32_t* n_inexact_blocks, void* stream) {
+                       uint8_t* scales_e4m3, float* tensor_scale, int32_t* n_inexact_blocks, void* workspace,
+                       size_t workspace_bytes, void* stream) {
     FP4_REQUIRE(rows >= 0 && k >= 0, FP4_ERR_INVALID, "negative size rows=%lld k=%lld", (long long)rows, (long long)k);
     FP4_REQUIRE(k % 32 == 0, FP4_ERR_SHAPE, "k=%lld is not a multiple of 32", (long long)k);
     if (rows == 0 || k == 0) return ok();
@@ -148,8 +165,9 @@ int fp4_remap_mx_to_nv(const uint8_t* codes, const uint8_t* scales_e8m0, int64_t
     FP4_PTR(scales_e4m3);
     FP4_SCALAR_PTR(tensor_scale);
     FP4_SCALAR_PTR(n_inexact_blocks);
+    if (const int e = check_scale_max_ws(workspace, workspace_bytes, rows, k)) return e;
     return hip_status(fp4::launch_remap(codes, scales_e8m0, rows, k, scales_e4m3, tensor_scale, n_inexact_blocks,
-                                        static_cast<hipStream_t>(stream)),
+                                        static_cast<uint8_t*>(workspace), static_cast<hipStream_t>(stream)),
                       "fp4_remap_mx_to_nv launch");
 }
 
@@ -284,7 +302,7 @@ int fp4_quantize_mxfp8(const void* x_bf16, int64_t rows, int64_t k, int64_t ld_x
 
 int fp4_mx_dequant_fp8(const uint8_t* codes, const uint8_t* scales_e8m0, int64_t rows, int64_t k,
                        uint8_t* values_e4m3, uint8_t* block_scales_e4m3, float* tensor_scale,
-                       int32_t* n_inexact_blocks, void* stream) {
+                       int32_t* n_inexact_blocks, void* workspace, size_t workspace_bytes, void* stream) {
     FP4_REQUIRE(rows >= 0 && k >= 0, FP4_ERR_INVALID, "negative size rows=%lld k=%lld", (long long)rows, (long long)k);
     FP4_REQUIRE(k % 32 == 0, FP4_ERR_SHAPE, "k=%lld is not a multiple of 32", (long long)k);
     if (rows == 0 || k == 0) return ok();
@@ -293,8 +311,10 @@ int fp4_mx_dequant_fp8(const uint8_t* codes, const uint8_t* scales_e8m0, int64_t
     FP4_PTR(values_e4m3);
     FP4_SCALAR_PTR(tensor_scale);
     FP4_SCALAR_PTR(n_inexact_blocks);
+    if (const int e = check_scale_max_ws(workspace, workspace_bytes, rows, k)) return e;
     return hip_status(fp4::launch_dequant_fp8(codes, scales_e8m0, rows, k, values_e4m3, block_scales_e4m3,
-                                              tensor_scale, n_inexact_blocks, static_cast<hipStream_t>(stream)),
+                                              tensor_scale, n_inexact_blocks, static_cast<uint8_t*>(workspace),
+                                              static_cast<hipStream_t>(stream)),
                       "fp4_mx_dequant_fp8 launch");
 }
 

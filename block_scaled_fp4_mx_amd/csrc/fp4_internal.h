@@ -92,10 +92,13 @@ hipError_t launch_fake_quant(int fmt, const uint16_t* x, int64_t rows, int64_t k
                              hipStream_t s);
 hipError_t launch_ste_backward(const void* g, int g_f32, int64_t rows, int64_t k, int64_t ldg, float* gm, int64_t ldm,
                                int accumulate, hipStream_t s);
+// Bytes of the optional workspace of launch_remap / launch_dequant_fp8 (one per
+// partial-maximum workgroup, at most 256); ws == nullptr takes a third launch.
+size_t scale_max_workspace_bytes(int64_t rows, int64_t k);
 hipError_t launch_remap(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t k,
-                        uint8_t* scales_nv, float* tensor_scale, int32_t* n_inexact, hipStream_t s);
+                        uint8_t* scales_nv, float* tensor_scale, int32_t* n_inexact, uint8_t* ws, hipStream_t s);
 hipError_t launch_dequant_fp8(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t k, uint8_t* v8,
-                              uint8_t* s8, float* tensor_scale, int32_t* n_inexact, hipStream_t s);
+                              uint8_t* s8, float* tensor_scale, int32_t* n_inexact, uint8_t* ws, hipStream_t s);
 hipError_t launch_dequant(int fmt, const uint8_t* codes, const uint8_t* scales, const float* ts,
                           int64_t rows, int64_t k, void* out, int out_f32, int64_t ld_out,
                           hipStream_t s);

@@ -401,15 +401,17 @@ __global__ __launch_bounds__(kThreads) void ste_backward_kernel(const void* __re
 // ------------------------------------------------------------------ tensor-wide scale passes
 // The MX -> NV remap and the MX -> FP8 dequantization both need E_max, the
 // largest block exponent of the whole tensor, before any output is final.
-// Three launches, without workspace:
+// With a caller workspace of one byte per pass-1 workgroup, two launches:
 //   pass 1 (scale_max_kernel, many workgroups): workgroup g writes the largest
-//     scale byte of its share to byte g of the output array (a scratch use of
-//     bytes that pass 3 rewrites) and workgroup 0 clears the inexact counter;
+//     scale byte of its share to workspace byte g and workgroup 0 clears the
+//     inexact counter;
 //   pass 2 (many workgroups): each workgroup reduces the pass-1 bytes to E_max
-//     and converts its blocks, except the first `reserved` ones, whose output
-//     bytes hold the pass-1 maxima; inexact blocks are added to the counter
-//     (one atomic per workgroup that found any);
-//   pass 3 (one workgroup): the reserved blocks and the tensor scale.
+//     and converts its blocks; inexact blocks are added to the counter (one
+//     atomic per workgroup that found any); workgroup 0 writes the tensor scale.
+// Without workspace, three: pass 1 writes its bytes to the start of the output
+// array instead, pass 2 skips the first `reserved` blocks, whose output bytes
+// hold them, and pass 3 (one workgroup) converts those blocks last and writes
+// the tensor scale.
 // (A grid-wide "last workgroup finishes" ticket in pass 2 would save a launch,
 // but thousands of same-address atomics serialize: measured 44 us for 4096^2.)
 constexpr int kScaleMaxChunk = 4096;   // scale bytes per pass-1 workgroup
@@ -474,41 +476,69 @@ __device__ __forceinline__ void add_count(uint32_t mine, int32_t* cnt, uint32_t*
 // ------------------------------------------------------------------ MX -> NV remap
 // s_t = 2^(E_max - 8); both E4M3 group scales of block b are 2^(E_b - k),
 // exact for j = E_b - k in [-9, 8]; a block with a nonzero code below that
-// range is inexact (2^-10 ties to 0).  One lane per block.
-__device__ __forceinline__ uint32_t remap_block(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ s,
-                                                uint8_t* __restrict__ snv, int64_t i, int kexp) {
-    const int j = (int)s[i] - 127 - kexp;                 // <= 8
-    uint32_t sg, bad = 0;
-    if (j >= -6) {
-        sg = (uint32_t)(j + 7) << 3;                      // normal 2^j
-    } else if (j >= -9) {
-        sg = 1u << (j + 9);                               // subnormal 2^j = 2^(j+9) * 2^-9
-    } else {
-        sg = 0u;                                          // 2^-10 ties to 0, below rounds to 0
-        const uint4 a = reinterpret_cast<const uint4*>(codes + i * 16)[0];
-        bad = ((a.x | a.y | a.z | a.w) & 0x77777777u) ? 1u : 0u;
-    }
-    reinterpret_cast<uint16_t*>(snv)[i] = (uint16_t)(sg | (sg << 8));
-    return bad;
+// range is inexact (2^-10 ties to 0).  A lane takes four consecutive blocks:
+// one 4-byte scale load, one 8-byte store.
+__device__ __forceinline__ uint32_t remap_scale(uint32_t sbyte, int kexp, bool& low) {
+    const int j = (int)sbyte - 127 - kexp;                // <= 8
+    low = j < -9;
+    if (j >= -6) return (uint32_t)(j + 7) << 3;           // normal 2^j
+    if (j >= -9) return 1u << (j + 9);                    // subnormal 2^j = 2^(j+9) * 2^-9
+    return 0u;                                            // 2^-10 ties to 0, below rounds to 0
 }
 
-// Pass 2 (kFinish false): blocks [reserved, nb); pass 3 (kFinish true, one
-// workgroup): blocks [0, reserved) and the tensor scale.
-template <bool kFinish>
+__device__ __forceinline__ uint32_t remap_nonzero(const uint8_t* __restrict__ codes, int64_t b) {
+    const uint4 a = reinterpret_cast<const uint4*>(codes + b * 16)[0];
+    return ((a.x | a.y | a.z | a.w) & 0x77777777u) ? 1u : 0u;
+}
+
+// Blocks [b0, b1) (b0 a multiple of 4), E_max from the npart bytes at `part`;
+// workgroup 0 writes the tensor scale when ts is not null.  The lane's first
+// scale word is loaded before the reduction of the partial maxima.
 __global__ __launch_bounds__(kThreads) void remap_kernel(const uint8_t* __restrict__ codes,
-                                                         const uint8_t* __restrict__ s, int64_t nb,
-                                                         uint8_t* __restrict__ snv, int npart, int64_t reserved,
+                                                         const uint8_t* __restrict__ s, uint8_t* snv,
+                                                         const uint8_t* part, int npart, int64_t b0, int64_t b1,
                                                          float* __restrict__ ts, int32_t* __restrict__ n_inexact) {
     __shared__ uint32_t red[kThreads / 64];
-    const int kexp = (int)reduce_part(snv, npart, red) - 127 - 8;
+    const int64_t nq = (b1 - b0 + 3) >> 2;
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    int64_t q = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    auto load = [&](int64_t qq) -> uint32_t {
+        const int64_t i = b0 + 4 * qq;
+        if (i + 4 <= b1) return *reinterpret_cast<const uint32_t*>(s + i);
+        uint32_t w = 0;
+        for (int t = 0; t < 4 && i + t < b1; ++t) w |= (uint32_t)s[i + t] << (8 * t);
+        return w;
+    };
+    uint32_t w = q < nq ? load(q) : 0u;
+    const int kexp = (int)reduce_part(part, npart, red) - 127 - 8;
     __syncthreads();                       // every thread has read the pass-1 bytes before any is rewritten
     uint32_t bad = 0;
-    const int64_t stride = (int64_t)gridDim.x * kThreads;
-    const int64_t i0 = kFinish ? 0 : reserved, i1 = kFinish ? reserved : nb;
-    for (int64_t i = i0 + (int64_t)blockIdx.x * kThreads + threadIdx.x; i < i1; i += stride)
-        bad += remap_block(codes, s, snv, i, kexp);
+    while (q < nq) {
+        const int64_t i = b0 + 4 * q;
+        uint32_t o[4];
+        bool low[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            o[t] = remap_scale((w >> (8 * t)) & 0xFFu, kexp, low[t]);
+            o[t] |= o[t] << 8;
+        }
+        if (i + 4 <= b1) {
+            *reinterpret_cast<uint2*>(snv + 2 * i) = make_uint2(o[0] | o[1] << 16, o[2] | o[3] << 16);
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                if (low[t]) bad += remap_nonzero(codes, i + t);
+        } else {
+            for (int t = 0; t < 4 && i + t < b1; ++t) {
+                reinterpret_cast<uint16_t*>(snv)[i + t] = (uint16_t)o[t];
+                if (low[t]) bad += remap_nonzero(codes, i + t);
+            }
+        }
+        q += stride;
+        if (q < nq) w = load(q);
+    }
     add_count(bad, n_inexact, red);
-    if (kFinish && threadIdx.x == 0) *ts = ldexpf(1.0f, kexp);   // 2^-135 .. 2^119; below 2^-126 a subnormal
+    if (ts != nullptr && blockIdx.x == 0 && threadIdx.x == 0)
+        *ts = ldexpf(1.0f, kexp);          // 2^-135 .. 2^119; below 2^-126 a subnormal
 }
 
 // ------------------------------------------------------------------ MX -> FP8 dequant
@@ -581,7 +611,7 @@ __device__ __forceinline__ uint2 fp8_expand8(uint32_t c, uint32_t tlo, uint32_t 
 // 0x44, 0x48, 0x4C) with j added to each nonzero byte's exponent field (no
 // byte drops below 8, so no borrow crosses bytes).  Other blocks take the
 // general table.  Returns 1 for an inexact block.
-__device__ __forceinline__ uint32_t fp8_block(uint4 c, uint32_t sbyte, uint8_t* __restrict__ v8,
+__device__ __forceinline__ uint32_t fp8_block(uint4 c, uint32_t sbyte, uint8_t* v8,
                                               uint8_t* __restrict__ s8out, int64_t b, int kexp) {
     const int j = (int)sbyte - 127 - kexp;
     uint32_t tlo, thi, badm, s8;
@@ -607,40 +637,47 @@ __device__ __forceinline__ uint32_t fp8_block(uint4 c, uint32_t sbyte, uint8_t* 
 
 constexpr int kFp8Depth = 4;
 
-// Pass 2 (kFinish false): blocks [reserved, nb); pass 3 (kFinish true, one
-// workgroup): blocks [0, reserved) and the tensor scale.
-template <bool kFinish>
+// Blocks [b0, b1), E_max from the npart bytes at `part`; workgroup 0 writes
+// the tensor scale when ts is not null.
 __global__ __launch_bounds__(kThreads) void fp8_dequant_kernel(const uint8_t* __restrict__ codes,
-                                                               const uint8_t* __restrict__ s, int64_t nb,
-                                                               uint8_t* __restrict__ v8, uint8_t* __restrict__ s8out,
-                                                               int npart, int64_t reserved, float* __restrict__ ts,
+                                                               const uint8_t* __restrict__ s, uint8_t* v8,
+                                                               uint8_t* __restrict__ s8out, const uint8_t* part,
+                                                               int npart, int64_t b0, int64_t b1,
+                                                               float* __restrict__ ts,
                                                                int32_t* __restrict__ n_inexact) {
     __shared__ uint32_t red[kThreads / 64];
-    const int kexp = (int)reduce_part(v8, npart, red) - 127 - 6;
-    __syncthreads();                       // every thread has read the pass-1 bytes before any is rewritten
-    const int64_t b0 = kFinish ? 0 : reserved, b1 = kFinish ? reserved : nb;
     const int64_t stride = (int64_t)gridDim.x * kThreads;
-    uint32_t bad = 0;
-    // kFp8Depth blocks per lane: every load is issued before the first conversion
-    for (int64_t b = b0 + (int64_t)blockIdx.x * kThreads + threadIdx.x; b < b1; b += kFp8Depth * stride) {
-        uint4 c[kFp8Depth];
-        uint32_t sb[kFp8Depth];
+    // kFp8Depth blocks per lane: every load is issued before the first
+    // conversion, the first group's before the reduction of the partial maxima
+    uint4 c[kFp8Depth];
+    uint32_t sb[kFp8Depth];
+    auto load = [&](int64_t bb) {
 #pragma unroll
         for (int d = 0; d < kFp8Depth; ++d) {
-            const int64_t bd = b + d * stride;
+            const int64_t bd = bb + d * stride;
             if (bd < b1) {
                 c[d] = reinterpret_cast<const uint4*>(codes)[bd];
                 sb[d] = s[bd];
             }
         }
+    };
+    int64_t b = b0 + (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (b < b1) load(b);
+    const int kexp = (int)reduce_part(part, npart, red) - 127 - 6;
+    __syncthreads();                       // every thread has read the pass-1 bytes before any is rewritten
+    uint32_t bad = 0;
+    while (b < b1) {
 #pragma unroll
         for (int d = 0; d < kFp8Depth; ++d) {
             const int64_t bd = b + d * stride;
             if (bd < b1) bad += fp8_block(c[d], sb[d], v8, s8out, bd, kexp);
         }
+        b += kFp8Depth * stride;
+        if (b < b1) load(b);
     }
     add_count(bad, n_inexact, red);
-    if (kFinish && threadIdx.x == 0) *ts = ldexpf(1.0f, kexp);   // 2^-133 .. 2^121; below 2^-126 a subnormal
+    if (ts != nullptr && blockIdx.x == 0 && threadIdx.x == 0)
+        *ts = ldexpf(1.0f, kexp);          // 2^-133 .. 2^121; below 2^-126 a subnormal
 }
 
 }  // namespace
@@ -802,29 +839,41 @@ hipError_t launch_ste_backward(const void* g, int g_f32, int64_t rows, int64_t k
     return hipGetLastError();
 }
 
+size_t scale_max_workspace_bytes(int64_t rows, int64_t k) {
+    return scale_max_groups(rows * (k / 32));
+}
+
 hipError_t launch_remap(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t k,
-                        uint8_t* scales_nv, float* ts, int32_t* n_inexact, hipStream_t s) {
+                        uint8_t* scales_nv, float* ts, int32_t* n_inexact, uint8_t* ws, hipStream_t s) {
     const int64_t nb = rows * (k / 32);
     const unsigned g1 = scale_max_groups(nb);
-    scale_max_kernel<<<g1, kThreads, 0, s>>>(scales, nb, scales_nv, n_inexact);
-    const int64_t reserved = min((int64_t)(g1 + 1) / 2, nb);   // blocks whose 2 output bytes hold pass-1 maxima
-    unsigned g2 = grid_for(nb - reserved, 4);
+    // without workspace the maxima go to the first output bytes, 2 per block
+    // (a multiple of 4: remap_kernel's lanes take aligned groups of 4 blocks)
+    const int64_t reserved = ws ? 0 : min((int64_t)((g1 + 1) / 2 + 3) & ~(int64_t)3, nb);
+    uint8_t* part = ws ? ws : scales_nv;
+    scale_max_kernel<<<g1, kThreads, 0, s>>>(scales, nb, part, n_inexact);
+    unsigned g2 = grid_for((nb - reserved + 3) / 4, 1);
     if (g2 > kMxMaxBlocks) g2 = kMxMaxBlocks;
-    remap_kernel<false><<<g2, kThreads, 0, s>>>(codes, scales, nb, scales_nv, (int)g1, reserved, ts, n_inexact);
-    remap_kernel<true><<<1, kThreads, 0, s>>>(codes, scales, nb, scales_nv, (int)g1, reserved, ts, n_inexact);
+    remap_kernel<<<g2, kThreads, 0, s>>>(codes, scales, scales_nv, part, (int)g1, reserved, nb, ws ? ts : nullptr,
+                                         n_inexact);
+    if (!ws) remap_kernel<<<1, kThreads, 0, s>>>(codes, scales, scales_nv, part, (int)g1, 0, reserved, ts, n_inexact);
     return hipGetLastError();
 }
 
 hipError_t launch_dequant_fp8(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t k, uint8_t* v8,
-                              uint8_t* s8, float* ts, int32_t* n_inexact, hipStream_t s) {
+                              uint8_t* s8, float* ts, int32_t* n_inexact, uint8_t* ws, hipStream_t s) {
     const int64_t nb = rows * (k / 32);
     const unsigned g1 = scale_max_groups(nb);
-    scale_max_kernel<<<g1, kThreads, 0, s>>>(scales, nb, v8, n_inexact);
-    const int64_t reserved = min((int64_t)(g1 + 31) / 32, nb);  // blocks whose 32 output bytes hold pass-1 maxima
+    // without workspace the maxima go to the first value bytes, 32 per block
+    const int64_t reserved = ws ? 0 : min((int64_t)(g1 + 31) / 32, nb);
+    uint8_t* part = ws ? ws : v8;
+    scale_max_kernel<<<g1, kThreads, 0, s>>>(scales, nb, part, n_inexact);
     unsigned g2 = grid_for(nb - reserved, kFp8Depth);
     if (g2 > kMxMaxBlocks) g2 = kMxMaxBlocks;
-    fp8_dequant_kernel<false><<<g2, kThreads, 0, s>>>(codes, scales, nb, v8, s8, (int)g1, reserved, ts, n_inexact);
-    fp8_dequant_kernel<true><<<1, kThreads, 0, s>>>(codes, scales, nb, v8, s8, (int)g1, reserved, ts, n_inexact);
+    fp8_dequant_kernel<<<g2, kThreads, 0, s>>>(codes, scales, v8, s8, part, (int)g1, reserved, nb, ws ? ts : nullptr,
+                                               n_inexact);
+    if (!ws)
+        fp8_dequant_kernel<<<1, kThreads, 0, s>>>(codes, scales, v8, s8, part, (int)g1, 0, reserved, ts, n_inexact);
     return hipGetLastError();
 }
 

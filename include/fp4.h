@@ -129,11 +129,26 @@ int fp4_quantize_nv_noalloc(const void* x_bf16, int64_t rows, int64_t k, int64_t
  *   is below 2^-9 (those lose precision); 0 means the remap is lossless.
  * codes: [rows, k/2]; scales_e8m0: [rows, k/32]; scales_e4m3: [rows, k/16];
  * tensor_scale: 1 device float; n_inexact_blocks: 1 device int32.
- * Errors: k % 32 != 0 -> FP4_ERR_SHAPE.
+ * workspace: optional device memory of at least
+ * fp4_scale_max_workspace_bytes(rows, k) bytes (any alignment, not overlapping
+ * the other arguments) for the partial maxima of E_max; the call then takes two
+ * kernel launches instead of three.  NULL (with workspace_bytes 0) keeps the
+ * maxima in the output array's first bytes until a third launch rewrites them.
+ * Results are the same either way.  Calls sharing one workspace must be ordered
+ * (one stream).
+ * Errors: k % 32 != 0 -> FP4_ERR_SHAPE; workspace too small, or NULL with
+ * workspace_bytes != 0 -> FP4_ERR_WORKSPACE.
  */
 int fp4_remap_mx_to_nv(const uint8_t* codes, const uint8_t* scales_e8m0,
                        int64_t rows, int64_t k, uint8_t* scales_e4m3,
-                       float* tensor_scale, int32_t* n_inexact_blocks, void* stream);
+                       float* tensor_scale, int32_t* n_inexact_blocks,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Bytes of the optional workspace of fp4_remap_mx_to_nv and fp4_mx_dequant_fp8
+ * for an MX tensor of rows x k (at most 256; 0 for an empty tensor).
+ */
+size_t fp4_scale_max_workspace_bytes(int64_t rows, int64_t k);
 
 /*
  * Dequantization (explainer, section 2: the block scales multiply back in;
@@ -268,12 +283,14 @@ int fp4_mx_to_mxfp8(const uint8_t* codes, int64_t rows, int64_t k, uint8_t* code
  * codes: [rows, k/2]; scales_e8m0: [rows, k/32]; values_e4m3: [rows, k] bytes;
  * block_scales_e4m3: [rows, k/32] or NULL (not written); tensor_scale: 1 device
  * float; n_inexact_blocks: 1 device int32 (cleared, then accumulated, while the
- * call runs).
- * Errors: k % 32 != 0 -> FP4_ERR_SHAPE.
+ * call runs).  workspace / workspace_bytes: optional, as for fp4_remap_mx_to_nv
+ * (two launches with it, three without; the same results).
+ * Errors: k % 32 != 0 -> FP4_ERR_SHAPE; workspace too small, or NULL with
+ * workspace_bytes != 0 -> FP4_ERR_WORKSPACE.
  */
 int fp4_mx_dequant_fp8(const uint8_t* codes, const uint8_t* scales_e8m0, int64_t rows, int64_t k,
                        uint8_t* values_e4m3, uint8_t* block_scales_e4m3, float* tensor_scale,
-                       int32_t* n_inexact_blocks, void* stream);
+                       int32_t* n_inexact_blocks, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * W4A8 GEMM: C[m, n] = sum_k A_hat[m, k] * B_hat[n, k] with fp32 accumulation,

@@ -59,8 +59,7 @@ ROWS = {
     "gemm_mx_4096": ("gemm_mx_4096", [("gemm_mx_256_kernel", None)]),
     "quantize_mx_W": ("quantize_mx_W", [("mx_quantize_kernel", None)]),
     "quantize_nv_W": ("quantize_nv_W", [("nv_amax_kernel", None), ("nv_quantize_kernel", None)]),
-    "dequant_fp8_W": ("dequant_fp8_W", [("scale_max_kernel", None), ("fp8_dequant_kernel<false>", None),
-                                        ("fp8_dequant_kernel<true>", None)]),
+    "dequant_fp8_W": ("dequant_fp8_W", [("scale_max_kernel", None), ("fp8_dequant_kernel", None)]),
     "moe_h4096.gate_up": ("moe_h4096", [("moe_gate_up_mx256_kernel", None)]),
     "moe_h4096.down": ("moe_h4096", [("moe_down_mx256_kernel", None)]),
     "moe_h4096.combine": ("moe_h4096", [("combine_kernel", None)]),

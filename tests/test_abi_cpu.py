@@ -48,7 +48,7 @@ def test_library_exports_every_declared_symbol(F):
 
 
 def test_version_and_status_strings(F):
-    assert F.lib.fp4_abi_version() >= 1
+    assert F.lib.fp4_abi_version() == 2
     for st in (OK, INVALID, SHAPE, ALIGN, UNSUPPORTED, WORKSPACE, HIPERR):
         assert F.lib.fp4_status_string(st)
     assert F.lib.fp4_status_string(12345) == b"unknown status"
@@ -85,8 +85,14 @@ def test_quantize_nv_rejections(F):
 
 def test_remap_and_dequant_rejections(F):
     r = F.lib.fp4_remap_mx_to_nv
-    assert r(FAKE, FAKE, 4, 48, FAKE, FAKE, FAKE, None) == SHAPE
-    assert r(FAKE, FAKE, 4, 64, FAKE, FAKE, None, None) == INVALID
+    assert r(FAKE, FAKE, 4, 48, FAKE, FAKE, FAKE, None, 0, None) == SHAPE
+    assert r(FAKE, FAKE, 4, 64, FAKE, FAKE, None, None, 0, None) == INVALID
+    # the optional workspace: one byte per partial-maximum workgroup
+    need = F.lib.fp4_scale_max_workspace_bytes(4096, 4096)
+    assert need == 128 and F.lib.fp4_scale_max_workspace_bytes(1 << 20, 4096) == 256
+    assert F.lib.fp4_scale_max_workspace_bytes(4, 64) == 1 and F.lib.fp4_scale_max_workspace_bytes(0, 64) == 0
+    assert r(FAKE, FAKE, 4096, 4096, FAKE, FAKE, FAKE, FAKE, need - 1, None) == WORKSPACE
+    assert r(FAKE, FAKE, 4096, 4096, FAKE, FAKE, FAKE, None, need, None) == WORKSPACE   # NULL with a size
     d = F.lib.fp4_dequant
     assert d(7, FAKE, FAKE, FAKE, 4, 32, FAKE, 0, 32, None) == INVALID         # format
     assert d(0, FAKE, FAKE, FAKE, 4, 32, FAKE, 9, 32, None) == INVALID         # dtype
@@ -177,11 +183,13 @@ def test_fake_quant_ste_and_kv_rejections(F):
 
 def test_fp8_dequant_rejections(F):
     d = F.lib.fp4_mx_dequant_fp8
-    assert d(FAKE, FAKE, 4, 48, FAKE, None, FAKE, FAKE, None) == SHAPE            # k % 32
-    assert d(FAKE, FAKE, 4, 64, FAKE, None, None, FAKE, None) == INVALID          # tensor scale
-    assert d(FAKE, FAKE, 4, 64, FAKE, None, FAKE, None, None) == INVALID          # count
-    assert d(FAKE, FAKE, 4, 64, MISALIGNED, None, FAKE, FAKE, None) == ALIGN
-    assert d(None, None, 0, 64, None, None, None, None, None) == OK
+    assert d(FAKE, FAKE, 4, 48, FAKE, None, FAKE, FAKE, None, 0, None) == SHAPE            # k % 32
+    assert d(FAKE, FAKE, 4, 64, FAKE, None, None, FAKE, None, 0, None) == INVALID          # tensor scale
+    assert d(FAKE, FAKE, 4, 64, FAKE, None, FAKE, None, None, 0, None) == INVALID          # count
+    assert d(FAKE, FAKE, 4, 64, MISALIGNED, None, FAKE, FAKE, None, 0, None) == ALIGN
+    assert d(FAKE, FAKE, 8192, 4096, FAKE, None, FAKE, FAKE, FAKE, 255, None) == WORKSPACE   # needs 256
+    assert d(FAKE, FAKE, 4, 64, FAKE, None, FAKE, FAKE, None, 1, None) == WORKSPACE
+    assert d(None, None, 0, 64, None, None, None, None, None, 0, None) == OK
 
 
 def test_binding_rejects_what_the_c_side_would_misread(F):

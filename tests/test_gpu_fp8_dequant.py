@@ -2,7 +2,8 @@
 and a power-of-two tensor scale) and of the remap's tensor-wide passes against
 the CPU oracle: value bytes, block scale bytes, tensor scale and inexact-block
 count bit-exact, from one block to many workgroups, with inexact blocks inside
-and outside the blocks the last workgroup finishes."""
+and outside the blocks the last workgroup finishes, with and without the
+optional workspace that holds the partial maxima."""
 from __future__ import annotations
 
 import numpy as np
@@ -18,7 +19,13 @@ from oracle import quant as Q
 pytestmark = pytest.mark.gpu
 
 
-def _run(codes, scales, with_s8=True):
+def _workspace(R, K, fill=0xFF):
+    """A workspace of the required size, filled with bytes that would raise
+    E_max if a stale one were read."""
+    return torch.full((F.fp4_scale_max_workspace_bytes(R, K),), fill, dtype=torch.uint8, device=DEV)
+
+
+def _run(codes, scales, with_s8=True, ws=None):
     R, nb = scales.shape
     c = torch.from_numpy(np.ascontiguousarray(codes)).to(DEV)
     s = torch.from_numpy(np.ascontiguousarray(scales)).to(DEV)
@@ -26,14 +33,14 @@ def _run(codes, scales, with_s8=True):
     s8 = empty_u8(R, nb) if with_s8 else None
     ts = torch.full((1,), float("nan"), dtype=torch.float32, device=DEV)
     n = torch.full((1,), -7, dtype=torch.int32, device=DEV)
-    F.fp4_mx_dequant_fp8(c, s, v8, ts, n, s8)
+    F.fp4_mx_dequant_fp8(c, s, v8, ts, n, s8, workspace=ws)
     torch.cuda.synchronize()
     return host_u8(v8), None if s8 is None else host_u8(s8), ts.item(), n.item()
 
 
-def _check(codes, scales, with_s8=True):
+def _check(codes, scales, with_s8=True, ws=None):
     ev, es, est, en = Q.mx_dequant_fp8(codes, scales)
-    gv, gs, gts, gn = _run(codes, scales, with_s8)
+    gv, gs, gts, gn = _run(codes, scales, with_s8, ws)
     assert gts == float(est), (gts, float(est))
     assert gn == en, (gn, en)
     if with_s8:
@@ -84,12 +91,14 @@ def _spread(seed, R, K, spread, every=None):
     return Q.pack_nibbles(c4), sc
 
 
+@pytest.mark.parametrize("with_ws", [False, True], ids=["three_launch", "workspace"])
 @pytest.mark.parametrize("R,K", [(1, 32), (1, 64), (3, 96), (5, 1024), (777, 4096), (2048, 16384)])
-def test_fp8_dequant_shapes(R, K):
-    """One block up to 1M blocks (256 pass-1 workgroups): the blocks whose output
-    bytes hold the pass-1 maxima (finished by the last workgroup) include block 0."""
+def test_fp8_dequant_shapes(R, K, with_ws):
+    """One block up to 1M blocks (256 pass-1 workgroups): without workspace the
+    blocks whose output bytes hold the pass-1 maxima (finished by the last
+    workgroup) include block 0; with it the maxima sit in the workspace."""
     codes, scales = _spread(R * 31 + K, R, K, 15, every=97)
-    n = _check(codes, scales)
+    n = _check(codes, scales, ws=_workspace(R, K) if with_ws else None)
     if R * K // 32 > 97:
         assert n > 0
 
@@ -120,10 +129,26 @@ def test_fp8_dequant_back_to_back_calls():
         _check(codes, scales)
 
 
-@pytest.mark.parametrize("R,K", [(1, 32), (2, 64), (4096, 8192)])
-def test_remap_inexact_blocks_in_every_region(R, K):
-    """Remap over one block to 1M blocks with inexact blocks at block 0 (output
-    bytes that held the pass-1 maxima) and spread through the tensor."""
+def test_fp8_dequant_workspace_reused():
+    """One workspace through three calls, the second on a smaller tensor (fewer
+    pass-1 workgroups, so bytes of the first call stay behind) and a call with
+    the workspace and one without agreeing on the same tensor."""
+    a = _spread(3, 2048, 16384, 16, every=13)
+    b = _spread(4, 33, 512, 20, every=3)
+    ws = _workspace(2048, 16384, fill=0)
+    assert ws.numel() == 256
+    for codes, scales in (a, b, a):
+        _check(codes, scales, ws=ws)
+    assert all(x == y if isinstance(x, float) else np.array_equal(x, y)
+               for x, y in zip(_run(*b, ws=ws), _run(*b)))
+
+
+@pytest.mark.parametrize("with_ws", [False, True], ids=["three_launch", "workspace"])
+@pytest.mark.parametrize("R,K", [(1, 32), (2, 64), (777, 4096), (4096, 8192)])
+def test_remap_inexact_blocks_in_every_region(R, K, with_ws):
+    """Remap over one block to 1M blocks with inexact blocks at block 0 (without
+    workspace, output bytes that held the pass-1 maxima) and spread through the
+    tensor."""
     rng = np.random.default_rng(R + K)
     c4 = rng.integers(1, 16, (R, K), dtype=np.uint8)
     sc = (150 - rng.integers(0, 10, (R, K // 32))).astype(np.uint8)
@@ -135,7 +160,8 @@ def test_remap_inexact_blocks_in_every_region(R, K):
     snv = empty_u8(R, K // 16)
     ts = torch.full((1,), float("nan"), dtype=torch.float32, device=DEV)
     n = torch.full((1,), -7, dtype=torch.int32, device=DEV)
-    F.fp4_remap_mx_to_nv(torch.from_numpy(codes).to(DEV), torch.from_numpy(sc).to(DEV), snv, ts, n)
+    F.fp4_remap_mx_to_nv(torch.from_numpy(codes).to(DEV), torch.from_numpy(sc).to(DEV), snv, ts, n,
+                         workspace=_workspace(R, K) if with_ws else None)
     torch.cuda.synchronize()
     esnv, est, en = Q.remap_mx_to_nv(codes, sc)
     assert n.item() == en and ts.item() == float(est)

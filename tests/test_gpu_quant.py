@@ -224,8 +224,9 @@ def test_dequant_mx_extreme_scales():
     assert np.array_equal(out.cpu().numpy().view(np.uint32), exp.view(np.uint32))
 
 
+@pytest.mark.parametrize("with_ws", [False, True], ids=["three_launch", "workspace"])
 @pytest.mark.parametrize("which", ["A", "W"])
-def test_remap_workload2_lossless(which):
+def test_remap_workload2_lossless(which, with_ws):
     wl = W.workload2()
     bits = W.bf16_bits(getattr(wl, which))
     x = dev_bf16(bits)
@@ -233,7 +234,10 @@ def test_remap_workload2_lossless(which):
     snv = empty_u8(bits.shape[0], bits.shape[1] // 16)
     ts = torch.zeros(1, dtype=torch.float32, device=DEV)
     n = torch.full((1,), -7, dtype=torch.int32, device=DEV)
-    F.fp4_remap_mx_to_nv(c, s, snv, ts, n)
+    ws = None
+    if with_ws:
+        ws = torch.full((F.fp4_scale_max_workspace_bytes(*bits.shape),), 0xFF, dtype=torch.uint8, device=DEV)
+    F.fp4_remap_mx_to_nv(c, s, snv, ts, n, workspace=ws)
     torch.cuda.synchronize()
     ec, es = chunked(Q.mx_quantize, bits)
     esnv, est, en = Q.remap_mx_to_nv(ec, es)
