@@ -85,6 +85,14 @@ def test_moe_decode_nv_segments():
     _all_checks(case, oracle_expect(case, np.arange(case.T), eq, calibrate_h=True))
 
 
+def test_moe_decode_nv_two_step_k():
+    """Hidden and intermediate 512 on the 32-row decode tiles: K loops of
+    exactly two steps, so the prologue's two copies are the whole loop and the
+    first step's wait leaves the last step's copies in flight."""
+    case, eq = _small_case("nv", 109, 100, 512, 512, 8, 6)
+    _all_checks(case, oracle_expect(case, np.arange(case.T), eq, calibrate_h=True))
+
+
 def _segment_case(fmt, seed, counts, H, I):
     """topk 1, expert e routed exactly counts[e] tokens (in shuffled order)."""
     counts = np.asarray(counts)
