@@ -168,3 +168,42 @@ def test_remap_inexact_blocks_in_every_region(R, K, with_ws):
     if flat.size > 1:
         assert en > 0
     assert np.array_equal(host_u8(snv), esnv), describe_mismatch("remap scales", host_u8(snv), esnv)
+
+
+@pytest.mark.parametrize("with_ws", [False, True], ids=["three_launch", "workspace"])
+@pytest.mark.parametrize("R,K", [(3, 96), (777, 4096)])
+def test_scale_passes_write_only_their_outputs(R, K, with_ws):
+    """Guard bands around every output of the remap and the FP8 dequant (and
+    past the workspace bytes the query asks for) keep their sentinel bytes:
+    the pass-1 maxima land in the workspace or in the output's own first
+    bytes, and nothing is written past an output's end."""
+    codes, sc = _spread(R + K, R, K, 12, every=37)
+    c = torch.from_numpy(codes).to(DEV)
+    s = torch.from_numpy(sc).to(DEV)
+    G = 4096
+    need = F.fp4_scale_max_workspace_bytes(R, K)
+
+    def guarded(n):
+        buf = torch.full((n + 2 * G,), 0xA5, dtype=torch.uint8, device=DEV)
+        return buf, buf[G:G + n]
+
+    ws_buf, ws = guarded(need + 64) if with_ws else (None, None)
+    snv_buf, snv = guarded(R * K // 16)
+    v8_buf, v8 = guarded(R * K)
+    s8_buf, s8 = guarded(R * K // 32)
+    ts = torch.zeros(2, dtype=torch.float32, device=DEV)
+    n = torch.zeros(2, dtype=torch.int32, device=DEV)
+    F.fp4_remap_mx_to_nv(c, s, snv.view(R, K // 16), ts[:1], n[:1], workspace=ws)
+    F.fp4_mx_dequant_fp8(c, s, v8.view(R, K), ts[1:], n[1:], s8.view(R, K // 32), workspace=ws)
+    torch.cuda.synchronize()
+    for name, buf, m in (("remap scales", snv_buf, R * K // 16), ("fp8 values", v8_buf, R * K),
+                         ("fp8 block scales", s8_buf, R * K // 32)):
+        h = host_u8(buf)
+        assert (h[:G] == 0xA5).all() and (h[G + m:] == 0xA5).all(), name
+    if with_ws:
+        assert (host_u8(ws_buf)[:G] == 0xA5).all() and (host_u8(ws_buf)[G + need:] == 0xA5).all(), "workspace"
+    esnv, est, en = Q.remap_mx_to_nv(codes, sc)
+    assert np.array_equal(host_u8(snv).reshape(R, K // 16), esnv) and ts[0].item() == float(est) and n[0].item() == en
+    ev, es, est8, en8 = Q.mx_dequant_fp8(codes, sc)
+    assert np.array_equal(host_u8(v8).reshape(R, K), ev) and np.array_equal(host_u8(s8).reshape(R, K // 32), es)
+    assert ts[1].item() == float(est8) and n[1].item() == en8
