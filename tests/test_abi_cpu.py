@@ -237,3 +237,11 @@ def test_binding_checks_operand_shapes():
     F._shape("fp4_gemm", "b_codes", torch.zeros((12, 32)), (8, 32), rows_at_least=True)
     with pytest.raises(ValueError, match="w13_codes"):
         F._shape("fp4_moe_grouped_gemm", "w13_codes", torch.zeros((4, 256, 16)), (4, 256, 32))
+
+
+def test_peak_probe_library_exports():
+    """The peak-rate microbenchmark library (not part of the ABI) is built
+    beside libfp4.so and exports its four entry points."""
+    lib = ctypes.CDLL(os.path.join(ROOT, "block_scaled_fp4_mx_amd", "probes", "libfp4_peak.so"))
+    for n in ("peak_mfma", "peak_copy", "peak_lds_dma", "peak_lds_read"):
+        assert hasattr(lib, n), n
