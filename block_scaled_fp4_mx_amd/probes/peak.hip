@@ -158,20 +158,24 @@ __global__ __launch_bounds__(kThreads, 1) void lds_read_kernel(float* __restrict
 
 template <typename F>
 hipError_t timed(F launch, int reps, float* ms) {
-    hipEvent_t e0, e1;
-    hipError_t e;
-    if ((e = hipEventCreate(&e0)) != hipSuccess) return e;
-    if ((e = hipEventCreate(&e1)) != hipSuccess) return e;
-    launch();   // warm-up
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipEventRecord(e0, 0);
-    for (int r = 0; r < reps; ++r) launch();
-    hipEventRecord(e1, 0);
-    if ((e = hipEventSynchronize(e1)) != hipSuccess) return e;
-    hipEventElapsedTime(ms, e0, e1);
-    hipEventDestroy(e0);
-    hipEventDestroy(e1);
-    return hipGetLastError();
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    hipError_t e = hipEventCreate(&e0);
+    if (e == hipSuccess) e = hipEventCreate(&e1);
+    if (e == hipSuccess) {
+        launch();   // warm-up
+        e = hipGetLastError();
+    }
+    if (e == hipSuccess) {
+        hipEventRecord(e0, 0);
+        for (int r = 0; r < reps; ++r) launch();
+        hipEventRecord(e1, 0);
+        e = hipEventSynchronize(e1);
+    }
+    if (e == hipSuccess) e = hipEventElapsedTime(ms, e0, e1);
+    if (e == hipSuccess) e = hipGetLastError();
+    if (e0) hipEventDestroy(e0);
+    if (e1) hipEventDestroy(e1);
+    return e;
 }
 
 }  // namespace
@@ -191,6 +195,11 @@ int peak_mfma(int kind, int groups, int iters, int reps, double* tflops) {
         return (int)e;
     }
     int* h = static_cast<int*>(malloc(kInWords * sizeof(int)));
+    if (!h) {
+        hipFree(in);
+        hipFree(out);
+        return -1;
+    }
     uint32_t x = 12345u;
     for (int i = 0; i < kInWords; ++i) {   // xorshift32 random operand bits
         x ^= x << 13;
