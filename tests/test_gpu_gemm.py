@@ -191,9 +191,10 @@ def test_gemm_nv_4096_sampled():
                                              (64, 8200, 512, torch.bfloat16, 0), (100, 5000, 256, torch.bfloat16, 5),
                                              (128, 4160, 1024, torch.float32, 0), (33, 6000, 7168, torch.float32, 0)])
 def test_gemm_mx_skinny_streaming(m, n, k, dtype, pad):
-    """At most 128 A rows and at least 4096 B rows (k % 128 == 0): the
-    streaming kernel (one pass over B), ragged m and n, both output types and
-    an output pitch that forces the element-wise stores."""
+    """Few A rows against at least 4096 B rows: up to 64 A rows (k % 128 == 0)
+    take the streaming kernel (one pass over B), 100 and 128 rows the fallback
+    kernel (fewer than 64 tiles of 256 x 256); ragged m and n, both output
+    types and an output pitch that forces the element-wise stores."""
     wl = W.random_linear(m * 7 + n + k, m, n, k, outlier_p=0.01)
     ab, wb = W.bf16_bits(wl.A), W.bf16_bits(wl.W)
     a = quantize_mx(dev_bf16(ab))
