@@ -216,10 +216,23 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, i
     tn = r / rows_in_group;
 }
 
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// A whole 16-byte piece of C; kStream: a non-temporal store (measured faster
+// for the W4A8 and NV GEMMs' outputs, 1% slower for the MX GEMM's).
+template <bool kStream>
+__device__ __forceinline__ void store_piece(uint8_t* dst, uint4 v) {
+    if (kStream)
+        __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_t*>(dst));
+    else
+        *reinterpret_cast<uint4*>(dst) = v;
+}
+
 // Stores rows_pass rows of a tile staged in LDS (row r's 16-byte chunk c at
 // chunk c ^ (r & 15), rowb bytes per row) to C rows grow0 .. and columns n0 ..,
 // one 16-byte piece per thread and iteration; pieces past m or n are dropped
 // or written element by element.
+template <bool kStream>
 __device__ __forceinline__ void store_rows_from_lds(const uint8_t* csm, int rows_pass, int chunks_row, int rowb,
                                                     int64_t grow0, int64_t n0, int64_t m, int64_t n, void* c,
                                                     int c_f32, int64_t ldc, bool vec) {
@@ -232,7 +245,7 @@ __device__ __forceinline__ void store_rows_from_lds(const uint8_t* csm, int rows
         const uint4 v = *reinterpret_cast<const uint4*>(csm + row * rowb + ((ch ^ (row & 15)) << 4));
         uint8_t* dst = static_cast<uint8_t*>(c) + (grow * ldc + gcol) * esz;
         if (vec && gcol + 16 / esz <= n) {
-            *reinterpret_cast<uint4*>(dst) = v;
+            store_piece<kStream>(dst, v);
         } else {
             const uint32_t w[4] = {v.x, v.y, v.z, v.w};
             for (int e = 0; e < 16 / esz && gcol + e < n; ++e) {
@@ -299,7 +312,8 @@ __global__ __launch_bounds__(kTileThreads, 1) void gemm_mx_256_kernel(
                 }
         }
         __syncthreads();
-        store_rows_from_lds(csm, rows_pass, chunks_row, rowb, m0 + pass * rows_pass, n0, m, n, c, c_f32, ldc, vec);
+        store_rows_from_lds<false>(csm, rows_pass, chunks_row, rowb, m0 + pass * rows_pass, n0, m, n, c, c_f32, ldc,
+                                   vec);
     }
 }
 
@@ -354,7 +368,8 @@ __global__ __launch_bounds__(kW8Threads, 1) void gemm_w4a8_256_kernel(
                 }
         }
         __syncthreads();
-        store_rows_from_lds(csm, rows_pass, chunks_row, rowb, m0 + pass * rows_pass, n0, m, n, c, c_f32, ldc, vec);
+        store_rows_from_lds<true>(csm, rows_pass, chunks_row, rowb, m0 + pass * rows_pass, n0, m, n, c, c_f32, ldc,
+                                  vec);
     }
 }
 
@@ -429,7 +444,7 @@ __global__ __launch_bounds__(kNvThreads, 1) void gemm_nv_tile_kernel(
             const uint4 v = *reinterpret_cast<const uint4*>(csm + row * rowb + ch * 16);
             uint8_t* dst = static_cast<uint8_t*>(c) + (grow * ldc + gcol) * esz;
             if (vec && gcol + 16 / esz <= n) {
-                *reinterpret_cast<uint4*>(dst) = v;
+                store_piece<true>(dst, v);
             } else {
                 const uint32_t w[4] = {v.x, v.y, v.z, v.w};
                 for (int e = 0; e < 16 / esz && gcol + e < n; ++e) {
