@@ -290,6 +290,16 @@ struct GemmParams {
     fp4_moe_debug dbg;
 };
 
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// w * y of one routed row's 4 columns into the fp32 y buffer.  Non-temporal:
+// the rows are read once, by the combine, after the whole down stage.
+__device__ __forceinline__ void store_y(float* dst, float wgt, float4 v) {
+    __builtin_nontemporal_store(f32x4_t{__fmul_rn(wgt, v.x), __fmul_rn(wgt, v.y), __fmul_rn(wgt, v.z),
+                                        __fmul_rn(wgt, v.w)},
+                                reinterpret_cast<f32x4_t*>(dst));
+}
+
 __device__ __forceinline__ float silu_mul(float g, float u) {
     return (g / (1.0f + expf(-g))) * u;
 }
@@ -699,8 +709,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void moe_down_mx256_kernel(GemmPar
             const int64_t slot = route.slot_of(band * 16 + k);
             const float wgt = route.wgt_of(band * 16 + k);
             const float4 v = *reinterpret_cast<const float4*>(&ysm[rr * kYRow + lane * 4]);
-            *reinterpret_cast<float4*>(p.ybuf + slot * H + n0 + lane * 4) =
-                make_float4(__fmul_rn(wgt, v.x), __fmul_rn(wgt, v.y), __fmul_rn(wgt, v.z), __fmul_rn(wgt, v.w));
+            store_y(p.ybuf + slot * H + n0 + lane * 4, wgt, v);
         }
     }
 }
@@ -908,8 +917,7 @@ __global__ __launch_bounds__(kNvThreads, 1) void moe_down_nv_kernel(GemmParams p
         const int64_t slot = route.slot_of(k);
         const float wgt = route.wgt_of(k);
         const float4 v = *reinterpret_cast<const float4*>(&ysm[rr * kNvYRow + lane * 4]);
-        *reinterpret_cast<float4*>(p.ybuf + slot * H + n0 + lane * 4) =
-            make_float4(__fmul_rn(wgt, v.x), __fmul_rn(wgt, v.y), __fmul_rn(wgt, v.z), __fmul_rn(wgt, v.w));
+        store_y(p.ybuf + slot * H + n0 + lane * 4, wgt, v);
     }
 }
 
@@ -1121,8 +1129,7 @@ __global__ __launch_bounds__(kNvThreads, 1) void moe_down_nvw_kernel(GemmParams 
                 const int col = hh * 256 + lane * 4;
                 if (n0 + col >= H) break;     // H is a multiple of 4: a float4 is wholly in or out
                 const float4 v = *reinterpret_cast<const float4*>(&ysm[rr * kNwYRow + col]);
-                *reinterpret_cast<float4*>(p.ybuf + slot * H + n0 + col) =
-                    make_float4(__fmul_rn(wgt, v.x), __fmul_rn(wgt, v.y), __fmul_rn(wgt, v.z), __fmul_rn(wgt, v.w));
+                store_y(p.ybuf + slot * H + n0 + col, wgt, v);
             }
         }
     }
