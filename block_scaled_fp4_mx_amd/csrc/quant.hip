@@ -35,6 +35,8 @@ __device__ __forceinline__ int64_t x_offset(int64_t u, int64_t upr, int64_t ldx)
 // kernels: kOutCodes writes codes and scales; kOutBf16 / kOutF32 write the
 // dequantized values instead (row pitch ld_out elements).
 constexpr int kOutCodes = 0, kOutBf16 = 1, kOutF32 = 2;
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kOutSlots = 3;   // codes and scales of row r go to row slots[r] (skipped if outside [0, capacity))
 
 // Element offset of unit u (n consecutive elements; upr units per row).
@@ -49,19 +51,19 @@ __device__ __forceinline__ int64_t unit_offset(int64_t u, int64_t upr, int64_t n
 template <int kOut, int n>
 __device__ __forceinline__ void store_values(void* out, int64_t o, const float* f) {
     if (kOut == kOutF32) {
-        float4* p = reinterpret_cast<float4*>(static_cast<float*>(out) + o);
+        f32x4_t* p = reinterpret_cast<f32x4_t*>(static_cast<float*>(out) + o);
 #pragma unroll
-        for (int i = 0; i < n / 4; ++i) p[i] = make_float4(f[4 * i], f[4 * i + 1], f[4 * i + 2], f[4 * i + 3]);
+        for (int i = 0; i < n / 4; ++i)
+            __builtin_nontemporal_store(f32x4_t{f[4 * i], f[4 * i + 1], f[4 * i + 2], f[4 * i + 3]}, p + i);
     } else {
-        uint4* p = reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + o);
+        u32x4_t* p = reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(out) + o);
 #pragma unroll
         for (int i = 0; i < n / 8; ++i) {
-            uint4 q;
-            q.x = f32_to_bf16_rne(f[8 * i + 0]) | (f32_to_bf16_rne(f[8 * i + 1]) << 16);
-            q.y = f32_to_bf16_rne(f[8 * i + 2]) | (f32_to_bf16_rne(f[8 * i + 3]) << 16);
-            q.z = f32_to_bf16_rne(f[8 * i + 4]) | (f32_to_bf16_rne(f[8 * i + 5]) << 16);
-            q.w = f32_to_bf16_rne(f[8 * i + 6]) | (f32_to_bf16_rne(f[8 * i + 7]) << 16);
-            p[i] = q;
+            const u32x4_t q = {f32_to_bf16_rne(f[8 * i + 0]) | (f32_to_bf16_rne(f[8 * i + 1]) << 16),
+                               f32_to_bf16_rne(f[8 * i + 2]) | (f32_to_bf16_rne(f[8 * i + 3]) << 16),
+                               f32_to_bf16_rne(f[8 * i + 4]) | (f32_to_bf16_rne(f[8 * i + 5]) << 16),
+                               f32_to_bf16_rne(f[8 * i + 6]) | (f32_to_bf16_rne(f[8 * i + 7]) << 16)};
+            __builtin_nontemporal_store(q, p + i);
         }
     }
 }
@@ -629,8 +631,8 @@ __device__ __forceinline__ uint32_t fp8_block(uint4 c, uint32_t sbyte, uint8_t* 
     const uint2 o2 = fp8_expand8(c.z, tlo, thi, hit);
     const uint2 o3 = fp8_expand8(c.w, tlo, thi, hit);
     uint4* o = reinterpret_cast<uint4*>(v8 + b * 32);
-    o[0] = make_uint4(o0.x, o0.y, o1.x, o1.y);
-    o[1] = make_uint4(o2.x, o2.y, o3.x, o3.y);
+    __builtin_nontemporal_store(u32x4_t{o0.x, o0.y, o1.x, o1.y}, reinterpret_cast<u32x4_t*>(o));
+    __builtin_nontemporal_store(u32x4_t{o2.x, o2.y, o3.x, o3.y}, reinterpret_cast<u32x4_t*>(o) + 1);
     if (s8out != nullptr) s8out[b] = (uint8_t)s8;
     return (hit & badm) ? 1u : 0u;
 }
