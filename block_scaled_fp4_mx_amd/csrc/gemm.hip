@@ -84,6 +84,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     store_tile(acc, c, c_f32, ldc, m, n, m0, n0, lane, scale);
 }
 
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
 // MX GEMM for few A rows (m <= 64) and many B rows, e.g. indexer scores of a
 // handful of queries against a long key cache: the work is streaming B once.
 // A workgroup owns 64 B rows (4 waves x one 16-row fragment) and all A rows
@@ -182,7 +184,9 @@ __global__ __launch_bounds__(256) void gemm_mx_skinny_kernel(
             if (c_f32) {
                 float* dst = static_cast<float*>(c) + row * ldc + col;
                 if (vec) {
-                    *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+                    __builtin_nontemporal_store(u32x4_t{__float_as_uint(v[0]), __float_as_uint(v[1]),
+                                                        __float_as_uint(v[2]), __float_as_uint(v[3])},
+                                                reinterpret_cast<u32x4_t*>(dst));
                 } else {
                     for (int e = 0; e < 4 && col + e < n; ++e) dst[e] = v[e];
                 }
@@ -215,8 +219,6 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, i
     tm = group * G + r % rows_in_group;
     tn = r / rows_in_group;
 }
-
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 // A whole 16-byte piece of C; kStream: a non-temporal store (measured faster
 // for the W4A8 and NV GEMMs' outputs, 1% slower for the MX GEMM's).

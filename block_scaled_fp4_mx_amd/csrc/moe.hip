@@ -291,6 +291,7 @@ struct GemmParams {
 };
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
 // w * y of one routed row's 4 columns into the fp32 y buffer.  Non-temporal:
 // the rows are read once, by the combine, after the whole down stage.
@@ -1169,8 +1170,9 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const float4* __restr
                 }
             }
         }
-        out[i] = make_uint2(f32_to_bf16_rne(acc.x) | (f32_to_bf16_rne(acc.y) << 16),
-                            f32_to_bf16_rne(acc.z) | (f32_to_bf16_rne(acc.w) << 16));
+        __builtin_nontemporal_store(u32x2_t{f32_to_bf16_rne(acc.x) | (f32_to_bf16_rne(acc.y) << 16),
+                                            f32_to_bf16_rne(acc.z) | (f32_to_bf16_rne(acc.w) << 16)},
+                                    reinterpret_cast<u32x2_t*>(out + i));
     }
 }
 
