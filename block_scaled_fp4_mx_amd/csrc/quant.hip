@@ -197,6 +197,7 @@ __global__ __launch_bounds__(kThreads) void mx_to_mxfp8_kernel(const uint32_t* _
 constexpr int kNvAmaxBlocks = 1024;   // partial maxima written by pass 1
 constexpr int kNvDepth = 1;           // 16-groups per lane whose loads are in flight (32 B each)
 constexpr unsigned kNvMaxBlocks = 1024;
+static_assert(kNvAmaxBlocks % kThreads == 0, "pass 2 loads kNvAmaxBlocks / kThreads partial maxima per lane");
 
 template <bool kContig>
 __global__ __launch_bounds__(kThreads) void nv_amax_kernel(
@@ -270,8 +271,16 @@ __global__ __launch_bounds__(kThreads) void nv_quantize_kernel(
         if (uj < total) nv_load16<kContig>(x, uj, gpr, ldx, va[j], vb[j]);
     }
     if (npart > 0) {
-        uint32_t am = 0;
-        for (int i = threadIdx.x; i < npart; i += kThreads) am = max(am, part[i]);
+        // a lane's partial maxima (npart <= kNvAmaxBlocks) are loaded together
+        uint32_t pv[kNvAmaxBlocks / kThreads];
+#pragma unroll
+        for (int j = 0; j < kNvAmaxBlocks / kThreads; ++j) {
+            const int i = threadIdx.x + j * kThreads;
+            pv[j] = i < npart ? part[i] : 0u;
+        }
+        uint32_t am = pv[0];
+#pragma unroll
+        for (int j = 1; j < kNvAmaxBlocks / kThreads; ++j) am = max(am, pv[j]);
         for (int off = 32; off > 0; off >>= 1) am = max(am, (uint32_t)__shfl_xor((int)am, off));
         if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = am;
         __syncthreads();
