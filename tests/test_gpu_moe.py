@@ -118,6 +118,14 @@ def test_moe_segments_at_fragment_boundaries(fmt, counts, H):
     _all_checks(case, oracle_expect(case, np.arange(case.T), eq, calibrate_h=True))
 
 
+def test_moe_tiled_mx_hidden_1024():
+    """Hidden and intermediate 1024 on the 256-row MX tiles: K loops of four
+    steps (two scale loads each), eight gate/up column blocks, and segments at
+    fragment, band and tile boundaries."""
+    case, eq = _segment_case("mx", 110, [1, 16, 17, 128, 129, 255, 257, 300], 1024, 1024)
+    _all_checks(case, oracle_expect(case, np.arange(case.T), eq, calibrate_h=True))
+
+
 @pytest.mark.parametrize("fmt", ["mx", "nv"])
 def test_moe_topk_above_eight(fmt):
     """Top-12 routing over 16 experts: the combine sums a token's slots in two
